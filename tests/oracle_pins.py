@@ -1,0 +1,463 @@
+"""Pins of the CPU oracle against facts it does not compute itself.
+
+Each pin is a plain function that raises AssertionError when the oracle
+disagrees with: a format's value table or an independent library decoder, a
+hand-derived closed form (fixtures under tests/golden/), an invariant the
+method fixes, a textbook routine that a special case reduces to, or a
+brute-force property on tiny inputs. ``test_oracle_pins.py`` runs each one,
+and ``test_oracle_mutations.py`` re-runs them against oracle builds with a
+planted mistake to show that each plausible mistake is caught.
+"""
+
+from __future__ import annotations
+
+import itertools
+import math
+
+import numpy as np
+import torch
+
+import oracle
+from helpers import golden, hand_cache, hand_window, pack_nibbles, reorder_pages
+from synth import encode_e4m3, encode_fp4_blocks, make_small_decode
+
+TAU = 1.0 / math.sqrt(512.0)
+
+
+# ---------------------------------------------------------------- formats
+
+def pin_e2m1_table():
+    """All 16 E2M1 codes equal the OCP MX E2M1 value table (golden)."""
+    g = golden("e2m1_values.json")["values"]
+    got = [oracle.e2m1(c) for c in range(16)]
+    assert got == g, got
+    assert all(math.copysign(1, a) == math.copysign(1, b) for a, b in zip(got, g))
+
+
+def pin_e4m3_vs_library():
+    """All 256 E4M3 bytes decode as torch's float8_e4m3fn does (an independent decoder)."""
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = np.array([oracle.e4m3(b) for b in range(256)])
+    nan_r, nan_g = np.isnan(ref), np.isnan(got)
+    assert (nan_r == nan_g).all()
+    assert (ref[~nan_r] == got[~nan_g]).all()
+
+
+def pin_e4m3_landmarks():
+    g = golden("e4m3_landmarks.json")
+    for b, v in zip(g["bytes"], g["values"]):
+        got = oracle.e4m3(b)
+        assert got == v and math.copysign(1, got) == math.copysign(1, v), (b, got, v)
+    for b in g["nan_bytes"]:
+        assert math.isnan(oracle.e4m3(b))
+
+
+def pin_dequant_fp4_exhaustive():
+    """Every (code, scale) pair: value = E2M1 table x library E4M3 value; low nibble = even channel."""
+    e2 = golden("e2m1_values.json")["values"]
+    e4 = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    codes = np.arange(16, dtype=np.uint8)
+    # one row per scale byte: 16 channels hold codes 0..15 in order
+    nib = np.tile(codes, (256, 1))
+    packed = pack_nibbles(nib)
+    scales = np.arange(256, dtype=np.uint8)[:, None]
+    got = oracle.dequant_fp4(packed, scales)
+    want = np.array(e2)[None, :] * e4[:, None]
+    fin = ~np.isnan(want)
+    assert (np.isnan(got) == ~fin).all()
+    assert (got[fin] == want[fin]).all()
+    # the byte 0x21 holds channel 0 = code 1 (0.5) and channel 1 = code 2 (1.0)
+    row = np.zeros(8, np.uint8)
+    row[0] = 0x21
+    d = oracle.dequant_fp4(row[None, :], np.array([[0x38]], np.uint8))[0]
+    assert d[0] == 0.5 and d[1] == 1.0 and (d[2:] == 0).all()
+
+
+def pin_dequant_scale_groups():
+    """Channel c takes scale c // 16 (distinct power-of-two scales per group)."""
+    nib = np.full((1, 512), 2, np.uint8)  # 1.0 everywhere
+    scale_bytes = (0x20 + 8 * (np.arange(32) % 4)).astype(np.uint8)  # 2^-3..2^0 repeating
+    got = oracle.dequant_fp4(pack_nibbles(nib), scale_bytes[None, :])[0]
+    e4 = torch.tensor(scale_bytes).view(torch.float8_e4m3fn).double().numpy()
+    assert (got == np.repeat(e4, 16)).all()
+
+
+def pin_dequant_e4m3_rows():
+    b = np.arange(256, dtype=np.uint8).reshape(2, 128)
+    rs = np.array([1.0, 0.5], np.float32)
+    got = oracle.dequant_e4m3(b, rs)
+    ref = torch.tensor(b).view(torch.float8_e4m3fn).double().numpy() * rs[:, None]
+    fin = ~np.isnan(ref)
+    assert (got[fin] == ref[fin]).all() and np.isnan(got[~fin]).all()
+
+
+def pin_encoder_roundtrip():
+    """Values on the E2M1 grid with amax 6 (scale 1.0) survive encode -> oracle decode exactly."""
+    grid = np.array(golden("e2m1_values.json")["values"])
+    x = np.array([grid[(5 * c + 3) % 16] for c in range(64)], np.float32)
+    x[0] = 6.0  # amax 6 in every block -> scale 1
+    x[16], x[32], x[48] = -6.0, 6.0, -6.0
+    codes, scales = encode_fp4_blocks(x[None, :])
+    assert (scales == 0x38).all()
+    assert (oracle.dequant_fp4(codes, scales)[0] == x).all()
+    # E4M3 window round trip on its own grid
+    v = torch.arange(0, 127, dtype=torch.uint8).view(torch.float8_e4m3fn).float().numpy()
+    assert (oracle.dequant_e4m3(encode_e4m3(v)[None, :])[0] == v).all()
+
+
+# ---------------------------------------------------------------- index score
+
+def _ix_query(q_nib, q_scales, w):
+    return (pack_nibbles(np.asarray(q_nib))[None, None], np.asarray(q_scales, np.uint8)[None, None],
+            np.asarray(w, np.float32)[None, None])
+
+
+def pin_score_all_ones():
+    case = golden("index_score_cases.json")["cases"][0]
+    k_nib = np.full((1, 1, 64), case["k_fill_code"])
+    cache = hand_cache([1], page_size=4, ix_nib=k_nib, ix_scales=np.full((1, 1, 4), case["k_scale_byte"]))
+    qc, qs, w = _ix_query(np.full((4, 64), case["q_fill_code"]), np.full((4, 4), case["q_scale_byte"]), case["w"])
+    s = oracle.index_score(cache, qc, qs, w)
+    assert s[0, 0, 0] == case["expected"], s[0, 0, 0]
+    assert np.isneginf(s[0, 0, 1:]).all()
+
+
+def pin_score_one_hot_signs():
+    case = golden("index_score_cases.json")["cases"][1]
+    q_nib = np.zeros((4, 64), np.uint8)
+    q_sc = np.full((4, 4), 0x38, np.uint8)
+    for h, ch, code, sbyte in case["q"]:
+        q_nib[h, ch] = code
+        q_sc[h, ch // 16] = sbyte
+    k_nib = np.zeros((1, 1, 64), np.uint8)
+    for ch, code in case["k"]:
+        k_nib[0, 0, ch] = code
+    cache = hand_cache([1], page_size=4, ix_nib=k_nib, ix_scales=np.array(case["k_scales"])[None, None])
+    qc, qs, w = _ix_query(q_nib, q_sc, case["w"])
+    s = oracle.index_score(cache, qc, qs, w)
+    assert s[0, 0, 0] == case["expected"], s[0, 0, 0]
+
+
+def pin_score_all_heads_negative():
+    """q = -k on every head: each dot is negative, ReLU gives exactly 0."""
+    k_nib = np.full((1, 1, 64), 3)  # 1.5
+    q_nib = np.full((4, 64), 3 | 8)  # -1.5
+    cache = hand_cache([1], ix_nib=k_nib, ix_scales=np.full((1, 1, 4), 0x38))
+    qc, qs, w = _ix_query(q_nib, np.full((4, 4), 0x38), [1, 1, 1, 1])
+    assert oracle.index_score(cache, qc, qs, w)[0, 0, 0] == 0.0
+
+
+def _ramp_cache(N, page_size=4, B=1, block_table=None, num_pages=None):
+    """Indexer key of entry s = (s+1)/2 on channel 0 only (codes grow with s up to 12 entries)."""
+    vals = [0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    k_nib = np.zeros((B, N, 64), np.uint8)
+    k_sc = np.full((B, N, 4), 0x38, np.uint8)
+    for b in range(B):
+        for s in range(N):
+            k_nib[b, s, 0] = 1 + (s % 7)          # value vals[s % 7]
+            k_sc[b, s, 0] = 0x38 + 8 * (s // 7)   # x 2^(s // 7)
+    want = np.array([vals[s % 7] * 2.0 ** (s // 7) for s in range(N)])
+    return hand_cache([N] * B, page_size=page_size, ix_nib=k_nib, ix_scales=k_sc,
+                      block_table=block_table, num_pages=num_pages), want
+
+
+def pin_score_entry_placement():
+    """Entry s's score comes from page block_table[s // page], slot s % page (shuffled table)."""
+    N, P = 13, 4
+    bt = np.array([[3, 0, 2, 1]], np.int32)
+    cache, want = _ramp_cache(N, page_size=P, block_table=bt, num_pages=4)
+    q_nib = np.zeros((4, 64), np.uint8)
+    q_nib[0, 0] = 2  # head 0: q[0] = 1
+    qc, qs, w = _ix_query(q_nib, np.full((4, 4), 0x38), [1, 1, 1, 1])
+    s = oracle.index_score(cache, qc, qs, w)[0, 0]
+    assert (s[:N] == want).all(), (s[:N], want)
+    assert np.isneginf(s[N:]).all()
+
+
+def pin_score_block_causal():
+    """Entry s (tokens 4s..4s+3) is visible to position p iff 4(s+1) <= p+1."""
+    cache, want = _ramp_cache(8)
+    q_nib = np.zeros((4, 64), np.uint8)
+    q_nib[0, 0] = 2
+    qc, qs, w = _ix_query(q_nib, np.full((4, 4), 0x38), [1, 1, 1, 1])
+    for p in range(0, 33):
+        s = oracle.index_score(cache, qc, qs, w, q_pos=np.array([[p]], np.int32))[0, 0]
+        vis = [i for i in range(8) if 4 * (i + 1) <= p + 1]
+        assert [i for i in range(8) if np.isfinite(s[i])] == vis, (p, s)
+
+
+def pin_score_candidates():
+    """Reindex scoring of a candidate list equals the Full score of each listed entry; pads -> -inf."""
+    wl = make_small_decode([800], layers="F", k=8)  # 200 entries
+    L = wl.layers[0]
+    full = oracle.index_score(wl.caches[0], L.qix_codes, L.qix_scales, L.w)[0, 0]
+    cand = np.array([[[7, 150, -1, 0, 49, 300, 199]]], np.int32)
+    sc = oracle.index_score(wl.caches[0], L.qix_codes, L.qix_scales, L.w, cand=cand)[0, 0]
+    for j, e in enumerate(cand[0, 0]):
+        if 0 <= e < 200:
+            assert sc[j] == full[e]
+        else:
+            assert np.isneginf(sc[j])
+
+
+def pin_score_exact_product_bound():
+    """Per-head dots are exact in fp64: integer-valued inputs give integer scores."""
+    rng = np.random.default_rng(3)
+    N = 16
+    k_nib = rng.integers(0, 16, size=(1, N, 64)).astype(np.uint8)
+    m = k_nib & 7
+    k_nib[(m == 1) | (m == 3)] = 2  # drop the 0.5 and 1.5 magnitudes: integer values only
+    cache = hand_cache([N], ix_nib=k_nib, ix_scales=np.full((1, N, 4), 0x38))
+    q_nib = rng.integers(0, 16, size=(4, 64)).astype(np.uint8)
+    m = q_nib & 7
+    q_nib[(m == 1) | (m == 3)] = 2
+    qc, qs, w = _ix_query(q_nib, np.full((4, 4), 0x38), [1, 2, 3, 4])
+    s = oracle.index_score(cache, qc, qs, w)[0, 0, :N]
+    assert (s == np.round(s)).all()
+    # ... and equal to an integer computation of the same definition
+    e2 = np.array(golden("e2m1_values.json")["values"])
+    kv = e2[k_nib[0]]
+    qv = e2[q_nib]
+    ref = (np.maximum(qv @ kv.T, 0) * np.array([1, 2, 3, 4])[:, None]).sum(0)
+    assert (s == ref).all()
+
+
+# ---------------------------------------------------------------- selection
+
+def _brute_topk_ok(scores, ids, sel, k):
+    """Defining property of the selection, checked pairwise on tiny rows."""
+    valid = [(s, i) for s, i in zip(scores, ids) if s > -math.inf]
+    chosen = [i for i in sel if i >= 0]
+    assert len(chosen) == min(k, len(valid))
+    assert chosen == sorted(chosen)
+    assert all(i == -1 for i in sel[len(chosen):])
+    sc = {i: s for s, i in valid}
+    out = [i for _, i in valid if i not in chosen]
+    for a in chosen:
+        for b in out:
+            assert sc[a] > sc[b] or (sc[a] == sc[b] and a < b), (a, b, sc[a], sc[b])
+
+
+def pin_topk_ties_and_padding():
+    s = np.array([1.0, 3.0, 3.0, 2.0, 3.0, -np.inf, 0.0])
+    assert oracle.topk(s, 2).tolist() == [1, 2]
+    assert oracle.topk(s, 4).tolist() == [1, 2, 3, 4]
+    assert oracle.topk(s, 10).tolist() == [0, 1, 2, 3, 4, 6, -1, -1, -1, -1]
+    cand = np.array([9, 4, 7], np.int32)
+    assert oracle.topk(np.array([1.0, 5.0, 5.0]), 1, cand=cand).tolist() == [4]
+    assert oracle.topk(np.array([-np.inf, -np.inf]), 3).tolist() == [-1, -1, -1]
+
+
+def pin_topk_bruteforce():
+    rng = np.random.default_rng(11)
+    for n in range(1, 9):
+        for trial in range(6):
+            s = rng.integers(-2, 3, size=n).astype(np.float64)  # many exact ties
+            s[rng.random(n) < 0.2] = -np.inf
+            ids = rng.permutation(50)[:n].astype(np.int32)
+            for k in range(1, n + 2):
+                sel = oracle.topk(s, k, cand=ids).tolist()
+                _brute_topk_ok(s, ids, sel, k)
+                # exhaustive cross-check: the chosen set maximises the sorted score vector
+                valid = [j for j in range(n) if s[j] > -np.inf]
+                kk = min(k, len(valid))
+                best = max(itertools.combinations(valid, kk),
+                           key=lambda c: (sorted((s[j] for j in c), reverse=True),
+                                          [-x for x in sorted(ids[j] for j in c)]))
+                assert sorted(int(ids[j]) for j in best) == [i for i in sel if i >= 0]
+
+
+def pin_layer_full_pool_nesting():
+    """Full layer: top-K is a subset of the pool; Reindex over an all-entries pool with the
+    Full layer's own indexer query reproduces the Full selection."""
+    wl = make_small_decode([600, 257], layers="F", k=24, pool=64, page_size=16, shuffle=True)
+    L, c = wl.layers[0], wl.caches[0]
+    r = oracle.layer_step("F", c, L.win, L.q, L.qix_codes, L.qix_scales, L.w, k=24, pool=64)
+    for b in range(2):
+        assert set(r["idx"][b, 0][r["idx"][b, 0] >= 0]) <= set(r["pool"][b, 0][r["pool"][b, 0] >= 0])
+    allpool = np.full((2, 1, 600), -1, np.int32)
+    for b, n in enumerate(c.n_entries):
+        allpool[b, 0, :n] = np.arange(n)
+    rr = oracle.layer_step("R", c, L.win, L.q, L.qix_codes, L.qix_scales, L.w, k=24, pool=600,
+                           idx_in=allpool)
+    assert (rr["idx"] == r["idx"]).all()
+    assert np.allclose(rr["out"], r["out"], rtol=0, atol=0)
+
+
+def pin_short_rows_pad():
+    """N < K: every entry is selected, the rest is -1."""
+    wl = make_small_decode([40], layers="F", k=16)
+    L = wl.layers[0]
+    r = oracle.layer_step("F", wl.caches[0], L.win, L.q, L.qix_codes, L.qix_scales, L.w, k=16)
+    assert r["idx"][0, 0].tolist() == list(range(10)) + [-1] * 6
+
+
+# ---------------------------------------------------------------- attention
+
+def _rows_of(cache, b, ids):
+    out = []
+    for s in ids:
+        p, sl = cache.block_table[b, s // cache.page_size], s % cache.page_size
+        out.append(oracle.dequant_fp4(cache.kv_codes[p, sl][None], cache.kv_scales[p, sl][None])[0])
+    return np.array(out).reshape(-1, 512)
+
+
+def pin_attend_golden():
+    case = golden("attend_cases.json")["cases"][0]
+    kv = np.zeros((1, 1, 512), np.uint8)
+    kv[0, 0, 0] = 2
+    cache = hand_cache([1], kv_nib=kv, kv_scales=np.full((1, 1, 32), 0x38))
+    wrow = np.zeros((1, 1, 512), np.uint8)
+    wrow[0, 0, 0] = 0x40
+    win = hand_window(wrow)
+    q = np.zeros((1, 1, 16, 512), np.float32)
+    a = np.float32(math.log(2.0))
+    q[0, 0, 0::2, 0] = a
+    out, lse, psum = oracle.sparse_attend(cache, np.array([[[0, -1]]], np.int32), q, win,
+                                          sm_scale=case["tau"])
+    # q carries ln2 rounded to fp32; propagate that rounding exactly into the closed form
+    e1, e2 = math.exp(float(a)), math.exp(2 * float(a))
+    assert abs(out[0, 0, 0, 0] - (e1 + 2 * e2) / (e1 + e2)) < 1e-15
+    assert abs(out[0, 0, 0, 0] - case["even_out0"]) < 1e-7
+    assert abs(lse[0, 0, 0] - math.log(e1 + e2)) < 1e-15
+    assert abs(lse[0, 0, 0] - case["even_lse"]) < 1e-7
+    assert out[0, 0, 1, 0] == case["odd_out0"] and abs(lse[0, 0, 1] - case["odd_lse"]) < 1e-15
+    assert (out[0, 0, :, 1:] == 0).all()
+    assert np.allclose(psum, 1.0, atol=1e-14)
+
+
+def pin_attend_dense_equals_sdpa():
+    """K >= N: sparse attention equals dense attention (torch SDPA, fp64) over all entries + window."""
+    wl = make_small_decode([97 * 4, 33 * 4], layers="F", k=128, page_size=8, shuffle=True,
+                           row_scale=True)
+    L, c = wl.layers[0], wl.caches[0]
+    idx = np.full((2, 1, 128), -1, np.int32)
+    for b in range(2):
+        n = int(c.n_entries[b])
+        idx[b, 0, :n] = np.random.default_rng(b).permutation(n)
+    out, lse, psum = oracle.sparse_attend(c, idx, L.q, L.win, sm_scale=TAU)
+    for b in range(2):
+        n = int(c.n_entries[b])
+        rows = _rows_of(c, b, range(n))
+        ln = int(L.win.length[b])
+        w = oracle.dequant_e4m3(L.win.codes[b, :ln], L.win.row_scale[b, :ln])
+        kv = torch.from_numpy(np.concatenate([rows, w], 0))[None, None]
+        qq = torch.from_numpy(L.q[b, 0].astype(np.float64))[None, :, None, :]
+        ref = torch.nn.functional.scaled_dot_product_attention(qq, kv, kv, scale=TAU)[0, :, 0]
+        ref_lse = torch.logsumexp(TAU * (qq[0, :, 0] @ kv[0, 0].T), dim=-1)
+        assert np.abs(out[b, 0] - ref.numpy()).max() < 1e-12
+        assert np.abs(lse[b, 0] - ref_lse.numpy()).max() < 1e-12
+    assert np.abs(psum - 1).max() < 1e-12
+
+
+def pin_attend_special_cases():
+    """Single row -> that row; identical rows -> that row, lse + ln R; q = 0 -> mean of rows."""
+    wl = make_small_decode([64], layers="F", k=8)
+    c = wl.caches[0]
+    empty_win = hand_window(np.zeros((1, 1, 512), np.uint8), length=[0])
+    q = wl.layers[0].q
+    out, lse, _ = oracle.sparse_attend(c, np.array([[[5] + [-1] * 7]], np.int32), q, empty_win, sm_scale=TAU)
+    r5 = _rows_of(c, 0, [5])[0]
+    assert np.abs(out[0, 0] - r5[None, :]).max() < 1e-13
+    z = TAU * (q[0, 0].astype(np.float64) @ r5)
+    assert np.abs(lse[0, 0] - z).max() < 1e-12
+    out3, lse3, _ = oracle.sparse_attend(c, np.array([[[5, 5, 5, -1, -1, -1, -1, -1]]], np.int32), q,
+                                         empty_win, sm_scale=TAU)
+    assert np.abs(out3[0, 0] - r5[None, :]).max() < 1e-13
+    assert np.abs(lse3[0, 0] - (z + math.log(3))).max() < 1e-12
+    ids = [0, 3, 9, 10]
+    outz, lsez, _ = oracle.sparse_attend(c, np.array([[ids + [-1] * 4]], np.int32),
+                                         np.zeros_like(q), empty_win, sm_scale=TAU)
+    assert np.abs(outz[0, 0] - _rows_of(c, 0, ids).mean(0)[None, :]).max() < 1e-13
+    assert np.abs(lsez - math.log(4)).max() < 1e-14
+    oute, lsee, _ = oracle.sparse_attend(c, np.full((1, 1, 8), -1, np.int32), q, empty_win, sm_scale=TAU)
+    assert (oute == 0).all() and np.isneginf(lsee).all()
+
+
+def pin_attend_large_logits():
+    """Huge logits (scale 448 rows, large q) stay finite: the max is subtracted."""
+    kv = np.full((1, 2, 512), 7, np.uint8)  # 6.0
+    cache = hand_cache([2], kv_nib=kv, kv_scales=np.full((1, 2, 32), 0x7E))
+    q = np.full((1, 1, 16, 512), 50.0, np.float32)
+    win = hand_window(np.zeros((1, 1, 512), np.uint8), length=[0])
+    out, lse, _ = oracle.sparse_attend(cache, np.array([[[0, 1]]], np.int32), q, win, sm_scale=TAU)
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+    assert np.abs(out - 6.0 * 448.0).max() == 0
+
+
+def pin_attend_permutation_and_window_rows():
+    wl = make_small_decode([400], layers="F", k=32, row_scale=True)
+    L, c = wl.layers[0], wl.caches[0]
+    ids = np.random.default_rng(1).choice(100, 20, replace=False).astype(np.int32)
+    a = np.full((1, 1, 32), -1, np.int32)
+    a[0, 0, :20] = ids
+    b = np.full((1, 1, 32), -1, np.int32)
+    b[0, 0, 5:25] = ids[::-1]
+    oa, la, _ = oracle.sparse_attend(c, a, L.q, L.win, sm_scale=TAU)
+    ob, lb, _ = oracle.sparse_attend(c, b, L.q, L.win, sm_scale=TAU)
+    assert np.abs(oa - ob).max() < 1e-12 and np.abs(la - lb).max() < 1e-12
+    # window rows: scaling the row scales by 2 equals doubling those rows
+    w2 = hand_window(L.win.codes, L.win.length, L.win.row_scale * 2)
+    o2, _, _ = oracle.sparse_attend(c, np.full((1, 1, 32), -1, np.int32), L.q, w2, sm_scale=TAU)
+    ow = oracle.dequant_e4m3(L.win.codes[0, :L.win.length[0]], L.win.row_scale[0, :L.win.length[0]] * 2)
+    kv = torch.from_numpy(ow)[None, None]
+    qq = torch.from_numpy(L.q[0, 0].astype(np.float64))[None, :, None, :]
+    ref = torch.nn.functional.scaled_dot_product_attention(qq, kv, kv, scale=TAU)[0, :, 0].numpy()
+    assert np.abs(o2[0, 0] - ref).max() < 1e-12
+
+
+def pin_prefill_window_bounds():
+    """A query at position p sees window tokens in (p - W, p]."""
+    W = 4
+    rows = 10
+    codes = np.zeros((1, rows, 512), np.uint8)
+    for j in range(rows):
+        codes[0, j, 0] = encode_e4m3(np.array([float(j + 1)]))[0]  # row j: channel 0 = j+1
+    win = hand_window(codes, length=[rows], pos0=[100], window=W)
+    cache = hand_cache([0], page_size=4)
+    cache.n_entries[:] = 0
+    q = np.zeros((1, 3, 16, 512), np.float32)  # q = 0: out = mean of visible rows
+    qpos = np.array([[100, 103, 109]], np.int32)
+    out, lse, _ = oracle.sparse_attend(cache, np.full((1, 3, 2), -1, np.int32), q, win,
+                                       q_pos=qpos, sm_scale=TAU)
+    # visible token positions: p=100 -> {100}; 103 -> {100..103}; 109 -> {106..109}
+    assert out[0, 0, 0, 0] == 1.0
+    assert out[0, 1, 0, 0] == np.mean([1, 2, 3, 4])
+    assert out[0, 2, 0, 0] == np.mean([7, 8, 9, 10])
+    assert abs(lse[0, 1, 0] - math.log(4)) < 1e-14
+
+
+def pin_reuse_equals_full_given_indices():
+    wl = make_small_decode([800, 300], layers="FU", k=40, page_size=16, shuffle=True)
+    F, U = wl.layers
+    c = wl.caches[0]
+    rf = oracle.layer_step("F", c, F.win, F.q, F.qix_codes, F.qix_scales, F.w, k=40)
+    ru = oracle.layer_step("U", c, F.win, F.q, k=40, idx_in=rf["idx"])
+    assert (ru["out"] == rf["out"]).all() and (ru["lse"] == rf["lse"]).all()
+    # a Reuse layer with its own q and window equals sparse_attend on the inherited indices
+    ru2 = oracle.layer_step("U", c, U.win, U.q, k=40, idx_in=rf["idx"])
+    o, l, _ = oracle.sparse_attend(c, rf["idx"], U.q, U.win, sm_scale=TAU)
+    assert (ru2["out"] == o).all() and (ru2["lse"] == l).all()
+
+
+def pin_paged_equals_contiguous():
+    wl = make_small_decode([300, 130], layers="F", k=20, page_size=8)
+    L, c = wl.layers[0], wl.caches[0]
+    c2 = reorder_pages(c)
+    r1 = oracle.layer_step("F", c, L.win, L.q, L.qix_codes, L.qix_scales, L.w, k=20, want_scores=True)
+    r2 = oracle.layer_step("F", c2, L.win, L.q, L.qix_codes, L.qix_scales, L.w, k=20, want_scores=True)
+    assert (r1["idx"] == r2["idx"]).all()
+    assert (r1["out"] == r2["out"]).all()
+
+
+ALL_PINS = [
+    pin_e2m1_table, pin_e4m3_vs_library, pin_e4m3_landmarks, pin_dequant_fp4_exhaustive,
+    pin_dequant_scale_groups, pin_dequant_e4m3_rows, pin_encoder_roundtrip,
+    pin_score_all_ones, pin_score_one_hot_signs, pin_score_all_heads_negative,
+    pin_score_entry_placement, pin_score_block_causal, pin_score_candidates,
+    pin_score_exact_product_bound, pin_topk_ties_and_padding, pin_topk_bruteforce,
+    pin_layer_full_pool_nesting, pin_short_rows_pad, pin_attend_golden,
+    pin_attend_dense_equals_sdpa, pin_attend_special_cases, pin_attend_large_logits,
+    pin_attend_permutation_and_window_rows, pin_prefill_window_bounds,
+    pin_reuse_equals_full_given_indices, pin_paged_equals_contiguous,
+]

@@ -1,0 +1,55 @@
+"""Plant plausible mistakes in copies of the oracle and check that the pins catch each one.
+
+Every mutation is a textual edit of the oracle's C source compiled into a
+separate library under a temporary directory; the real oracle is untouched.
+A mutation survives only if every pin still passes, which fails the test.
+"""
+
+import pytest
+
+import oracle
+from oracle_pins import ALL_PINS
+
+MUTATIONS = [
+    ("nibble order swapped", "((c & 1) * 4)", "((1 - (c & 1)) * 4)"),
+    ("neighbouring scale group", "T_E4M3[scales[c / ORC_G]]", "T_E4M3[scales[(c / ORC_G) ^ 1]]"),
+    ("E2M1 exponent bias", "ldexp(1.0 + 0.5 * m, e - 1)", "ldexp(1.0 + 0.5 * m, e)"),
+    ("E2M1 sign dropped", "double v = (e == 0) ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);\n  return s ? -v : v;",
+     "double v = (e == 0) ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);\n  return v;"),
+    ("E4M3 exponent bias", "ldexp(1.0 + m / 8.0, e - 7)", "ldexp(1.0 + m / 8.0, e - 8)"),
+    ("E4M3 subnormal scale", "ldexp(m / 8.0, -6)", "ldexp(m / 8.0, -7)"),
+    ("ReLU dropped", "(dot > 0.0 ? dot : 0.0)", "dot"),
+    ("head weight dropped", "I += wq[h] * (dot > 0.0 ? dot : 0.0);", "I += (dot > 0.0 ? dot : 0.0);"),
+    ("visibility off by one", "q_pos[(int64_t)b * nq + t] + 1) / ORC_TPE", "q_pos[(int64_t)b * nq + t]) / ORC_TPE"),
+    ("page slot reversed", "return (int64_t)page * c->page_size + s % c->page_size;",
+     "return (int64_t)page * c->page_size + (c->page_size - 1 - s % c->page_size);"),
+    ("tie order reversed", "return (a->id > b->id) - (a->id < b->id);", "return (a->id < b->id) - (a->id > b->id);"),
+    ("selection ascending", "if (a->score > b->score) return -1;\n  if (a->score < b->score) return 1;",
+     "if (a->score < b->score) return -1;\n  if (a->score > b->score) return 1;"),
+    ("window dropped", "    if (win) {\n      int64_t len", "    if (0) {\n      int64_t len"),
+    ("window row scale ignored", "double rs = win->row_scale ? (double)win->row_scale[(int64_t)b * win->rows + j] : 1.0;",
+     "double rs = 1.0;"),
+    ("window lower bound inclusive", "tok > p - win->window", "tok >= p - win->window"),
+    ("softmax scale dropped", "z[r] = sm_scale * dot;", "z[r] = dot;"),
+    ("max not subtracted", "L += exp(z[r] - M);", "L += exp(z[r]) * exp(-M) * exp(M) / exp(M);"),
+    ("lse without log", "lse[bt * ORC_H + h] = M + log(L);", "lse[bt * ORC_H + h] = M + L;"),
+    ("query head stride", "const float *qh = q + (bt * ORC_H + h) * ORC_D;", "const float *qh = q + (bt * ORC_H + (h ^ 1)) * ORC_D;"),
+    ("selected entry rows skipped", "if (s < 0 || s >= c->n_entries[b]) continue;", "if (s <= 0 || s >= c->n_entries[b]) continue;"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_pins_catch_mutation(tmp_path, name, old, new):
+    src = oracle.source()
+    assert src.count(old) == 1, f"mutation anchor not found once: {name}"
+    path = oracle.build_variant(src.replace(old, new), str(tmp_path / "liboracle_mut.so"))
+    failed = []
+    with oracle.using(path):
+        for pin in ALL_PINS:
+            try:
+                pin()
+            except AssertionError:
+                failed.append(pin.__name__)
+            except Exception as e:  # a crash or NaN-driven error also counts as caught
+                failed.append(f"{pin.__name__}:{type(e).__name__}")
+    assert failed, f"no pin catches: {name}"
