@@ -1,0 +1,58 @@
+"""Build the CSA2 HIP library (libcsa2.so) for gfx950 with hipcc, in-tree."""
+
+from __future__ import annotations
+
+import glob
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+OBJ = os.path.join(ROOT, "_build", "csa2")
+LIB = os.path.join(HERE, "libcsa2.so")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
+    # packed fp32 VALU ops stay off: the compiler would otherwise form them by itself
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", os.path.join(ROOT, "include"),
+]
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
+    return r.returncode, err
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(OBJ, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    objs = [os.path.join(OBJ, os.path.basename(s) + ".o") for s in srcs]
+
+    def compile_one(so):
+        s, o = so
+        return s, _run([HIPCC, *FLAGS, "-c", s, "-o", o])
+
+    with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        results = list(ex.map(compile_one, zip(srcs, objs)))
+    failed = [(s, e) for s, (rc, e) in results if rc != 0]
+    if failed:
+        raise RuntimeError("hipcc failed:\n" + "\n".join(f"{s}:\n{e}" for s, e in failed))
+    if verbose:
+        for s, (rc, e) in results:
+            if e.strip():
+                print(e)
+    rc, err = _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", LIB, *objs,
+                    "-Wl,-rpath,/opt/rocm/lib"])
+    if rc != 0:
+        raise RuntimeError("link failed:\n" + err)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

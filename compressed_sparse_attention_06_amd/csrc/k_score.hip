@@ -1,0 +1,140 @@
+// Lightning-indexer scoring for decode, gfx950.
+//
+// Score of entry s for one query: I_s = sum_{h<4} w_h * max(0, q_h . k_s),
+// q_h and k_s 64-channel FP4 rows with one E4M3 scale per 16 channels
+// (DeepSeek V4.1 Flash summaries: "DeepSeek V4.1 Flash 如何靠压缩 KV 缓存实现小模型
+// 干翻大模型", sections "CSA2" and "FP4 量化 + Bounded Replay").
+//
+// Design. Decode scoring streams 36 bytes per entry (32 code bytes + 4 scale
+// bytes) and does 256 multiply-adds on them. At HBM rate that is ~177 VALU
+// lane-ops per entry on MI355X, about what a nibble-decode + FMA loop needs,
+// so a VALU version would be ALU-bound. The FP4 matrix core consumes the raw
+// E2M1 codes directly: one v_mfma_scale_f32_16x16x128_f8f6f4 (both operands
+// FP4, unit block scales) gives the 16 products D[h][g][s] = sum over the 16
+// channels of group g of E2M1(q_h) * E2M1(k_s), exact in fp32, for 16 entries.
+// The A operand is block-diagonal: row (h, g) holds q_h's codes in group g
+// and zeros elsewhere, so all 16 rows of the tile do useful work. The K
+// dimension is 128 codes, two entries' worth of 64: the same B registers feed
+// a second MFMA whose A operand sits in the upper half, so one 16-byte load
+// per lane covers 32 entries (1 KB, contiguous within a page). The epilogue
+// applies the two E4M3 scales per group in fp32, the ReLU, the head weight,
+// and sums the 4 heads across lanes.
+//
+// Lane layouts (checked on gfx950): for 16x16x128 FP4 lane l holds row/col
+// l%16 and K = 32*(l/16)+j in nibble j%8 of dword j/8; C lane l holds rows
+// 4*(l/16)+i of column l%16.
+#include "csa2_dev.h"
+#include "kernels.h"
+
+namespace csa2 {
+
+__global__ __launch_bounds__(256) void k_index_score(ScoreArgs a) {
+  __shared__ uint32_t lhist[HIST_BINS];
+  const int r = blockIdx.y;
+  const int b = r / a.nq, t = r % a.nq;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int32_t nent = a.c.n_entries[b];
+  const int32_t V = visible_entries(a.c, a.q_pos, b, a.nq, t);
+  const int64_t col0 = (int64_t)blockIdx.x * a.chunk;
+  const int64_t col_end = min(col0 + (int64_t)a.chunk, (int64_t)a.n_cols);
+  const int64_t work_end = (a.cand || a.write_masked) ? col_end : min(col_end, (int64_t)V);
+  if (col0 >= work_end) return;  // uniform across the block
+  const bool do_hist = a.hist != nullptr;
+  if (do_hist) {
+    for (int i = threadIdx.x; i < HIST_BINS; i += 256) lhist[i] = 0;
+    __syncthreads();
+  }
+
+  // A operands (block-diagonal indexer query), rows m = 4h + g.
+  const int m = lane & 15, h = m >> 2, g = m & 3, kg = lane >> 4;
+  const uint32_t *qc = (const uint32_t *)(a.qix_codes + ((int64_t)r * CSA2_HI + h) * 32);
+  v8i A1 = {0, 0, 0, 0, 0, 0, 0, 0}, A2 = {0, 0, 0, 0, 0, 0, 0, 0};
+  {
+    const uint32_t d0 = qc[2 * g], d1 = qc[2 * g + 1];
+    if (kg == (g >> 1)) { A1[2 * (g & 1)] = (int)d0; A1[2 * (g & 1) + 1] = (int)d1; }
+    if (kg == 2 + (g >> 1)) { A2[2 * (g & 1)] = (int)d0; A2[2 * (g & 1) + 1] = (int)d1; }
+  }
+  // Epilogue constants: C rows of this lane are (head hc, group i), i = 0..3.
+  const int hc = lane >> 4;
+  float sq[4];
+  {
+    const uint32_t sw = *(const uint32_t *)(a.qix_scales + ((int64_t)r * CSA2_HI + hc) * 4);
+    v2f lo = e4m3x2_lo_to_f32(sw), hi = e4m3x2_hi_to_f32(sw);
+    sq[0] = lo[0]; sq[1] = lo[1]; sq[2] = hi[0]; sq[3] = hi[1];
+  }
+  const float wh = a.w[(int64_t)r * CSA2_HI + hc];
+  const int64_t out_base = (int64_t)r * a.n_cols;
+  const int32_t *cand_row = a.cand ? a.cand + (int64_t)r * a.n_cand : nullptr;
+
+  for (int64_t e0 = col0 + wave * 32; e0 < work_end; e0 += 4 * 32) {
+    // load: lane l covers column e0 + 16*(l/32) + l%16, half (l/16)%2 of its 32 code bytes
+    const int64_t jl = e0 + ((lane >> 5) << 4) + (lane & 15);
+    const int half = (lane >> 4) & 1;
+    int32_t row_l = -1;
+    if (jl < col_end) {
+      const int32_t s = cand_row ? cand_row[jl] : (int32_t)jl;
+      if (s < V) row_l = (int32_t)cache_row(a.c, b, s, nent);
+    }
+    v8i B = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (row_l >= 0) {
+      const v4i x = *(const v4i *)(a.c.ix_codes + (int64_t)row_l * 32 + half * 16);
+      B[0] = x[0]; B[1] = x[1]; B[2] = x[2]; B[3] = x[3];
+    }
+    const v4f z = {0.f, 0.f, 0.f, 0.f};
+    const v4f C1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A1, B, z, 4, 4, 0, 127, 0, 127);
+    const v4f C2 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A2, B, z, 4, 4, 0, 127, 0, 127);
+    const int32_t row1 = __shfl(row_l, lane & 15);
+    const int32_t row2 = __shfl(row_l, 32 + (lane & 15));
+    float t1 = 0.f, t2 = 0.f;
+    if (row1 >= 0) {
+      const uint32_t sw = *(const uint32_t *)(a.c.ix_scales + (int64_t)row1 * 4);
+      v2f lo = e4m3x2_lo_to_f32(sw), hi = e4m3x2_hi_to_f32(sw);
+      float p = C1[0] * (sq[0] * lo[0]);
+      p = fmaf(C1[1], sq[1] * lo[1], p);
+      p = fmaf(C1[2], sq[2] * hi[0], p);
+      p = fmaf(C1[3], sq[3] * hi[1], p);
+      t1 = wh * fmaxf(p, 0.f);
+    }
+    if (row2 >= 0) {
+      const uint32_t sw = *(const uint32_t *)(a.c.ix_scales + (int64_t)row2 * 4);
+      v2f lo = e4m3x2_lo_to_f32(sw), hi = e4m3x2_hi_to_f32(sw);
+      float p = C2[0] * (sq[0] * lo[0]);
+      p = fmaf(C2[1], sq[1] * lo[1], p);
+      p = fmaf(C2[2], sq[2] * hi[0], p);
+      p = fmaf(C2[3], sq[3] * hi[1], p);
+      t2 = wh * fmaxf(p, 0.f);
+    }
+    // sum the four heads (lanes n, n+16, n+32, n+48 hold heads 0..3 of column n)
+    t1 += __shfl_xor(t1, 16);
+    t1 += __shfl_xor(t1, 32);
+    t2 += __shfl_xor(t2, 16);
+    t2 += __shfl_xor(t2, 32);
+    if (lane < 32) {
+      const int64_t col = e0 + lane;  // lanes 0..15: first tile; 16..31: second tile
+      const float sc = (lane < 16) ? t1 : t2;
+      const int32_t rv = (lane < 16) ? row1 : row2;
+      if (col < col_end) {
+        const float o = (rv >= 0) ? sc : -INFINITY;
+        a.scores[out_base + col] = o;
+        if (do_hist && rv >= 0) atomicAdd(&lhist[score_key(o) >> HIST_SHIFT], 1u);
+      }
+    }
+  }
+  if (do_hist) {
+    __syncthreads();
+    uint32_t *gh = a.hist + (int64_t)r * HIST_BINS;
+    for (int i = threadIdx.x; i < HIST_BINS; i += 256) {
+      const uint32_t v = lhist[i];
+      if (v) atomicAdd(&gh[i], v);
+    }
+  }
+}
+
+hipError_t launch_index_score(const ScoreArgs &a, int rows, hipStream_t st) {
+  const int64_t chunks = (a.n_cols + a.chunk - 1) / a.chunk;
+  dim3 grid((unsigned)chunks, (unsigned)rows);
+  hipLaunchKernelGGL(k_index_score, grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace csa2

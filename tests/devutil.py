@@ -1,0 +1,178 @@
+"""Helpers for the GPU parity tests: move synthetic inputs to the device, run
+the HIP path layer by layer, slice workloads for the oracle, compare."""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import compressed_sparse_attention_06_amd as csa2
+from synth.workloads import Cache as HostCache
+from synth.workloads import DecodeWorkload, LayerInputs, Window as HostWindow
+
+
+def t(a, dtype=None, device="cuda"):
+    if a is None:
+        return None
+    x = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        x = x.to(dtype)
+    return x.to(device)
+
+
+def dev_cache(c: HostCache) -> csa2.Cache:
+    return csa2.Cache(kv_codes=t(c.kv_codes), kv_scales=t(c.kv_scales), ix_codes=t(c.ix_codes),
+                      ix_scales=t(c.ix_scales), block_table=t(c.block_table), n_entries=t(c.n_entries))
+
+
+def dev_window(w: HostWindow):
+    if w is None:
+        return None
+    return csa2.Window(codes=t(w.codes), length=t(w.length), row_scale=t(w.row_scale),
+                       pos0=t(w.pos0), window=w.window)
+
+
+class DevWorkload:
+    """Device copies of a workload's inputs (caches, per-layer q / window / indexer query)."""
+
+    def __init__(self, wl: DecodeWorkload):
+        self.wl = wl
+        self.caches = [dev_cache(c) for c in wl.caches]
+        self.layers = []
+        for L in wl.layers:
+            self.layers.append(dict(mode=L.mode, cache_id=L.cache_id, q=t(L.q), win=dev_window(L.win),
+                                    qix_codes=t(L.qix_codes), qix_scales=t(L.qix_scales), w=t(L.w)))
+        self.q_pos = t(wl.q_pos)
+
+    def calls(self, layers=None):
+        """LayerCall objects chained like the model: Reindex reads the latest Full pool,
+        Reuse the latest Full/Reindex top-K."""
+        wl = self.wl
+        out = []
+        last_idx = last_pool = None
+        sel = range(len(self.layers)) if layers is None else layers
+        for li in sel:
+            L = self.layers[li]
+            cache = self.caches[L["cache_id"]]
+            kw = dict(q_pos=self.q_pos)
+            if L["mode"] == "F":
+                kw.update(qix_codes=L["qix_codes"], qix_scales=L["qix_scales"], w=L["w"])
+                pool = wl.pool
+            elif L["mode"] == "R":
+                kw.update(qix_codes=L["qix_codes"], qix_scales=L["qix_scales"], w=L["w"], idx_in=last_pool)
+                pool = wl.pool
+            else:
+                kw.update(idx_in=last_idx)
+                pool = 0
+            call = csa2.LayerCall(L["mode"], cache, L["win"], L["q"], wl.k, pool=pool,
+                                  sm_scale=wl.sm_scale, **kw)
+            if L["mode"] in ("F", "R"):
+                last_idx = call.idx_out
+            if L["mode"] == "F" and wl.pool > 0:
+                last_pool = call.pool_out
+            out.append(call)
+        return out
+
+
+def run_gpu(wl: DecodeWorkload, layers=None):
+    dw = DevWorkload(wl)
+    calls = dw.calls(layers)
+    for c in calls:
+        c()
+    torch.cuda.synchronize()
+    res = []
+    for c in calls:
+        res.append(dict(out=c.out.cpu().numpy(), lse=c.lse.cpu().numpy(),
+                        idx=None if c.idx_out is None else c.idx_out.cpu().numpy(),
+                        pool=None if c.pool_out is None else c.pool_out.cpu().numpy()))
+    return res
+
+
+def slice_requests(wl: DecodeWorkload, reqs) -> DecodeWorkload:
+    """The same workload restricted to some requests (caches keep every page)."""
+    reqs = list(reqs)
+
+    def cs(c: HostCache):
+        return HostCache(kv_codes=c.kv_codes, kv_scales=c.kv_scales, ix_codes=c.ix_codes,
+                         ix_scales=c.ix_scales, block_table=c.block_table[reqs],
+                         n_entries=c.n_entries[reqs], page_size=c.page_size)
+
+    def ws(w: HostWindow):
+        return HostWindow(codes=w.codes[reqs], row_scale=None if w.row_scale is None else w.row_scale[reqs],
+                          length=w.length[reqs], pos0=None if w.pos0 is None else w.pos0[reqs],
+                          window=w.window)
+
+    layers = []
+    for L in wl.layers:
+        layers.append(LayerInputs(mode=L.mode, cache_id=L.cache_id, q=L.q[reqs], win=ws(L.win),
+                                  qix_codes=None if L.qix_codes is None else L.qix_codes[reqs],
+                                  qix_scales=None if L.qix_scales is None else L.qix_scales[reqs],
+                                  w=None if L.w is None else L.w[reqs]))
+    return DecodeWorkload(name=wl.name + "_slice", contexts=wl.contexts[reqs], nq=wl.nq, k=wl.k,
+                          pool=wl.pool, caches=[cs(c) for c in wl.caches], layers=layers,
+                          q_pos=None if wl.q_pos is None else wl.q_pos[reqs], sm_scale=wl.sm_scale,
+                          window=wl.window, meta=dict(wl.meta))
+
+
+def slice_queries(wl: DecodeWorkload, qs) -> DecodeWorkload:
+    """The same (single-request) workload restricted to some query rows."""
+    qs = list(qs)
+    layers = []
+    for L in wl.layers:
+        layers.append(LayerInputs(mode=L.mode, cache_id=L.cache_id, q=L.q[:, qs], win=L.win,
+                                  qix_codes=None if L.qix_codes is None else L.qix_codes[:, qs],
+                                  qix_scales=None if L.qix_scales is None else L.qix_scales[:, qs],
+                                  w=None if L.w is None else L.w[:, qs]))
+    return DecodeWorkload(name=wl.name + "_qslice", contexts=wl.contexts, nq=len(qs), k=wl.k,
+                          pool=wl.pool, caches=wl.caches, layers=layers,
+                          q_pos=None if wl.q_pos is None else wl.q_pos[:, qs], sm_scale=wl.sm_scale,
+                          window=wl.window, meta=dict(wl.meta))
+
+
+# ---- comparisons -------------------------------------------------------------------
+
+OUT_MAX_ABS = 2e-3
+OUT_MEAN_ABS = 1e-3
+LSE_ABS = 1e-4
+SCORE_RTOL = 1e-6
+BAND_REL = 1e-5
+
+
+def assert_attention_close(g_out, g_lse, o_out, o_lse, what=""):
+    o_out = np.asarray(o_out)
+    fin = np.isfinite(o_lse)
+    assert (np.isfinite(g_lse) == fin).all(), f"{what}: empty-set rows differ"
+    assert (g_out[~fin] == 0).all(), f"{what}: empty rows must give 0"
+    d = np.abs(g_out - o_out)
+    assert d.max() <= OUT_MAX_ABS, f"{what}: out max-abs {d.max():.3e}"
+    assert d.mean() <= OUT_MEAN_ABS, f"{what}: out mean-abs {d.mean():.3e}"
+    if fin.any():
+        dl = np.abs(g_lse[fin] - o_lse[fin])
+        assert dl.max() <= LSE_ABS, f"{what}: lse max-abs {dl.max():.3e}"
+    return float(d.max()), float(d.mean())
+
+
+def band_sets(score_of, o_ids, g_ids, rel=BAND_REL):
+    """Top-K sets outside the near-tie band around the oracle's K-th score."""
+    o = [int(i) for i in o_ids if i >= 0]
+    g = [int(i) for i in g_ids if i >= 0]
+    if not o:
+        return set(), set(g)
+    kth = min(score_of(i) for i in o)
+    band = rel * abs(kth)
+    keep = lambda i: abs(score_of(i) - kth) > band  # noqa: E731
+    return {i for i in o if keep(i)}, {i for i in g if keep(i)}
+
+
+def assert_selection_matches(o_scores_row, o_ids, g_ids, id_to_col=None, what=""):
+    """GPU and oracle top-K agree outside the near-tie band; both have the same size."""
+    col = (lambda i: id_to_col[i]) if id_to_col is not None else (lambda i: i)
+    score_of = lambda i: o_scores_row[col(i)]  # noqa: E731
+    o_n = int((np.asarray(o_ids) >= 0).sum())
+    g_n = int((np.asarray(g_ids) >= 0).sum())
+    assert o_n == g_n, f"{what}: selected {g_n}, oracle {o_n}"
+    go = [int(i) for i in g_ids if i >= 0]
+    assert len(set(go)) == len(go), f"{what}: duplicate ids"
+    a, b = band_sets(score_of, o_ids, g_ids)
+    assert a == b, f"{what}: {len(a ^ b)} ids differ outside the tie band"
+    return set(int(i) for i in o_ids if i >= 0) == set(go)

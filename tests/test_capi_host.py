@@ -1,0 +1,140 @@
+"""The C-ABI library on the host: it loads, exports every declared symbol, and
+rejects bad arguments before launching anything (no GPU needed)."""
+
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import compressed_sparse_attention_06_amd as csa2
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "csa2.h")
+
+EINVAL, EUNSUPPORTED, EWORKSPACE = 1, 2, 3
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(csa2_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = csa2.lib()
+    decl = declared_functions()
+    assert len(decl) >= 10
+    for name in decl:
+        assert hasattr(L, name), name
+    assert set(csa2.EXPORTS) <= set(decl)
+
+
+def test_version_and_status_strings():
+    assert "gfx950" in csa2.version()
+    L = csa2.lib()
+    assert L.csa2_status_string(0) == b"ok"
+    assert L.csa2_status_string(3) == b"workspace too small"
+
+
+def _cache_struct(page_size=64, max_pages=4, num_pages=8, null_bt=False):
+    s = csa2._Cache()
+    dummy = 0x1000  # never dereferenced: validation reads no device memory
+    s.kv_codes = s.kv_scales = s.ix_codes = s.ix_scales = dummy
+    s.block_table = None if null_bt else dummy
+    s.n_entries = dummy
+    s.page_size, s.max_pages, s.num_pages = page_size, max_pages, num_pages
+    return s
+
+
+def _layer(mode=csa2.FULL, **over):
+    cs = _cache_struct(**{k: over.pop(k) for k in list(over) if k in ("page_size", "max_pages", "num_pages", "null_bt")})
+    a = csa2._LayerArgs()
+    a.mode = mode
+    a.cache = C.addressof(cs)
+    a.q = a.qix_codes = a.qix_scales = a.w = a.out = a.lse = a.idx_out = a.idx_in = 0x2000
+    a.batch, a.nq, a.k, a.pool = 2, 1, 16, 0
+    a.sm_scale = 0.04
+    a.ws, a.ws_bytes = 0x10000, 0
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a, cs
+
+
+def _step(a):
+    return csa2.lib().csa2_layer_step(C.byref(a), None)
+
+
+def test_layer_step_validation():
+    L = csa2.lib()
+    assert L.csa2_layer_step(None, None) == EINVAL
+    a, keep = _layer(k=0)
+    assert _step(a) == EINVAL
+    a, keep = _layer(k=5000)
+    assert _step(a) == EINVAL
+    a, keep = _layer(batch=0)
+    assert _step(a) == EINVAL
+    a, keep = _layer(q=None)
+    assert _step(a) == EINVAL
+    a, keep = _layer(mode=7)
+    assert _step(a) == EINVAL
+    a, keep = _layer(null_bt=True)
+    assert _step(a) == EINVAL
+    a, keep = _layer(page_size=48)
+    assert _step(a) == EUNSUPPORTED
+    a, keep = _layer(pool=8)  # pool < k
+    assert _step(a) == EINVAL
+    a, keep = _layer(pool=32, pool_out=None)
+    assert _step(a) == EINVAL
+    a, keep = _layer(mode=csa2.REINDEX, pool=32, idx_in=None)
+    assert _step(a) == EINVAL
+    a, keep = _layer(mode=csa2.REUSE, idx_in=None)
+    assert _step(a) == EINVAL
+    a, keep = _layer(sm_scale=float("inf"))
+    assert _step(a) == EINVAL
+    a, keep = _layer(mode=csa2.FULL, qix_codes=None)
+    assert _step(a) == EINVAL
+    # everything valid but the workspace: missing, misaligned, short
+    a, keep = _layer(ws=None, ws_bytes=1 << 30)
+    assert _step(a) == EWORKSPACE
+    a, keep = _layer(ws=0x10010, ws_bytes=1 << 30)
+    assert _step(a) == EWORKSPACE
+    need = csa2.workspace_bytes(csa2.FULL, 2, 1, 4 * 64, 16)
+    a, keep = _layer(ws_bytes=need - 1)
+    assert _step(a) == EWORKSPACE
+    assert b"needed" in L.csa2_last_error()
+
+
+def test_other_entry_points_validation():
+    L = csa2.lib()
+    cs = _cache_struct()
+    p = C.c_void_p(0x2000)
+    assert L.csa2_index_score(None, p, p, p, None, None, 0, 1, 1, p, None) == EINVAL
+    assert L.csa2_index_score(C.byref(cs), None, p, p, None, None, 0, 1, 1, p, None) == EINVAL
+    assert L.csa2_index_score(C.byref(cs), p, p, p, None, p, 0, 1, 1, p, None) == EINVAL
+    assert L.csa2_topk(p, None, 1, 1, 100, 0, p, p, C.c_size_t(1 << 30), None) == EINVAL
+    assert L.csa2_topk(p, None, 1, 1, 100, 8, p, None, C.c_size_t(0), None) == EWORKSPACE
+    assert L.csa2_sparse_attend(C.byref(cs), p, 0, p, None, None, C.c_float(0.04), 1, 1, p, p, p,
+                                C.c_size_t(1 << 30), None) == EINVAL
+    w = csa2._Window()
+    w.rows, w.window = 16, 0
+    assert L.csa2_sparse_attend(C.byref(cs), p, 8, p, C.byref(w), None, C.c_float(0.04), 1, 1, p, p,
+                                p, C.c_size_t(1 << 30), None) == EINVAL
+    assert L.csa2_dequant_fp4(p, p, 4, 48, p, None) == EINVAL
+    assert L.csa2_dequant_e4m3(None, 4, p, None) == EINVAL
+
+
+@pytest.mark.parametrize("mode,n_cols,k,pool,win", [
+    (csa2.FULL, 262144, 2048, 16384, 128),
+    (csa2.FULL, 2048, 256, 0, 128),
+    (csa2.REINDEX, 16384, 2048, 16384, 128),
+    (csa2.REUSE, 0, 2048, 0, 128),
+])
+def test_workspace_sizes(mode, n_cols, k, pool, win):
+    nb = csa2.workspace_bytes(mode, 8, 1, n_cols, k, pool, win)
+    assert nb % 256 == 0
+    splits = -(-(k + win) // 256)
+    assert nb >= 8 * splits * 16 * 514 * 4
+    if mode != csa2.REUSE:
+        assert nb >= 8 * n_cols * 4
+    assert csa2.workspace_bytes(mode, 0, 1, n_cols, k, pool, win) == 0

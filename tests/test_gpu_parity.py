@@ -1,0 +1,298 @@
+"""HIP path vs the CPU oracle (GPU required).
+
+Tolerances (written here, derived in the design doc):
+ * dequantised values: bit-exact (fp16 of the FP4 path, fp32 of E4M3);
+ * index scores: |gpu - oracle| <= 1e-6 |oracle| + 1e-6 max|row|;
+ * top-K id sets: equal after dropping ids whose oracle score lies within
+   1e-5 (relative) of the oracle's K-th score; exact when scores are exact;
+ * attention, given the oracle's indices: out max-abs <= 2e-3, mean-abs <=
+   1e-3, lse abs <= 1e-4 against fp64.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+import compressed_sparse_attention_06_amd as csa2  # noqa: E402
+import oracle  # noqa: E402
+from devutil import (SCORE_RTOL, DevWorkload, assert_attention_close,  # noqa: E402
+                     assert_selection_matches, dev_cache, dev_window, run_gpu, t)
+from helpers import hand_window  # noqa: E402
+from synth import make_small_decode  # noqa: E402
+
+TAU = 1.0 / math.sqrt(512.0)
+
+
+def setup_module(module):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    csa2.lib()
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+# ------------------------------------------------------------------ dequantisation
+
+def test_dequant_fp4_bit_exact():
+    _log("dequant fp4: 16 codes x 256 scales")
+    nib = np.tile(np.arange(16, dtype=np.uint8), (256, 2))  # 32 channels per row
+    codes = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+    scales = np.repeat(np.arange(256, dtype=np.uint8)[:, None], 2, axis=1)
+    g = csa2.dequant_fp4(t(codes), t(scales)).cpu().numpy().astype(np.float64)
+    o = oracle.dequant_fp4(codes, scales)
+    nan = np.isnan(o)
+    assert (np.isnan(g) == nan).all()
+    assert (g[~nan] == o[~nan]).all()
+
+
+def test_dequant_e4m3_bit_exact():
+    b = np.arange(256, dtype=np.uint8)
+    g = csa2.dequant_e4m3(t(b)).cpu().numpy().astype(np.float64)
+    o = oracle.dequant_e4m3(b[None, :])[0]
+    nan = np.isnan(o)
+    assert (np.isnan(g) == nan).all()
+    assert (g[~nan] == o[~nan]).all()
+    assert (np.signbit(g[~nan]) == np.signbit(o[~nan])).all()
+
+
+# ------------------------------------------------------------------ index scores
+
+def _check_scores(g, o, what):
+    g = np.asarray(g, np.float64)
+    masked = np.isneginf(o)
+    assert (np.isneginf(g) == masked).all(), f"{what}: masked columns differ"
+    rowmax = np.where(masked, 0, np.abs(o)).max(axis=-1, keepdims=True)
+    tol = SCORE_RTOL * np.abs(np.where(masked, 0, o)) + SCORE_RTOL * rowmax
+    d = np.abs(np.where(masked, 0, g - o))
+    assert (d <= tol).all(), f"{what}: score error {d.max():.3e}"
+
+
+SCORE_CASES = [
+    dict(contexts=[8192], page_size=64, shuffle=False),                 # 2048 entries, 1 row
+    dict(contexts=[4 * 777 + 1, 1000, 64, 8], page_size=16, shuffle=True),  # ragged tails
+    dict(contexts=[4 * 5000], page_size=128, shuffle=True, nq=3),        # several query rows
+]
+
+
+@pytest.mark.parametrize("case", SCORE_CASES, ids=["tiny", "ragged_paged", "multi_query"])
+def test_index_score_full(case):
+    _log(f"index_score full {case}")
+    wl = make_small_decode(layers="F", k=16, **case)
+    L, c = wl.layers[0], wl.caches[0]
+    g = csa2.index_score(dev_cache(c), t(L.qix_codes), t(L.qix_scales), t(L.w)).cpu().numpy()
+    o = oracle.index_score(c, L.qix_codes, L.qix_scales, L.w)
+    _check_scores(g, o, "full")
+
+
+def test_index_score_causal_and_candidates():
+    _log("index_score q_pos + candidates")
+    wl = make_small_decode([4 * 3000], layers="F", k=16, nq=6, prefill=True, page_size=32, shuffle=True)
+    L, c = wl.layers[0], wl.caches[0]
+    qp = np.array([[3, 4, 7, 100, 8000, 11999]], np.int32)
+    g = csa2.index_score(dev_cache(c), t(L.qix_codes), t(L.qix_scales), t(L.w), q_pos=t(qp)).cpu().numpy()
+    o = oracle.index_score(c, L.qix_codes, L.qix_scales, L.w, q_pos=qp)
+    _check_scores(g, o, "causal")
+    rng = np.random.default_rng(5)
+    cand = rng.integers(-5, 3100, size=(1, 6, 777)).astype(np.int32)
+    g = csa2.index_score(dev_cache(c), t(L.qix_codes), t(L.qix_scales), t(L.w), q_pos=t(qp),
+                         cand=t(cand)).cpu().numpy()
+    o = oracle.index_score(c, L.qix_codes, L.qix_scales, L.w, q_pos=qp, cand=cand)
+    _check_scores(g, o, "candidates")
+
+
+# ------------------------------------------------------------------ top-K
+
+@pytest.mark.parametrize("n,k", [(100, 7), (2048 + 37, 256), (16384, 2048), (16385, 2048),
+                                 (70000, 4096), (300000, 2048), (50, 100)])
+def test_topk_exact_ties(n, k):
+    """Integer scores (exact in fp32, many ties): the lowest-id rule decides, exact match."""
+    _log(f"topk ties n={n} k={k}")
+    rng = np.random.default_rng(n + k)
+    s = rng.integers(0, 9, size=(2, 1, n)).astype(np.float64)
+    s[rng.random(s.shape) < 0.1] = -np.inf
+    s[1, 0, :] = 3.0  # one row where every score ties
+    g = csa2.topk(t(s.astype(np.float32)), k).cpu().numpy()
+    o = oracle.topk(s, k)
+    assert (g == o).all()
+
+
+@pytest.mark.parametrize("n,k", [(5000, 2048), (262144, 4096), (40000, 1)])
+def test_topk_random_scores(n, k):
+    _log(f"topk random n={n} k={k}")
+    rng = np.random.default_rng(7)
+    s = rng.standard_normal((3, 1, n)) * 10
+    s32 = s.astype(np.float32)
+    g = csa2.topk(t(s32), k).cpu().numpy()
+    o = oracle.topk(s32.astype(np.float64), k)  # same fp32 values: exact ties only
+    assert (g == o).all()
+
+
+def test_topk_candidate_map():
+    rng = np.random.default_rng(9)
+    n, k = 20000, 300
+    s = np.round(rng.standard_normal((2, 1, n)) * 4)
+    cand = np.stack([rng.permutation(10 ** 6)[:n] for _ in range(2)])[:, None, :].astype(np.int32)
+    g = csa2.topk(t(s.astype(np.float32)), k, cand=t(cand)).cpu().numpy()
+    o = oracle.topk(s, k, cand=cand)
+    assert (g == o).all()
+
+
+# ------------------------------------------------------------------ attention
+
+ATT_CASES = [
+    dict(contexts=[8192], k=256, page_size=64),
+    dict(contexts=[4 * 700, 4 * 33, 4 * 1500 + 3], k=512, page_size=16, shuffle=True, row_scale=True),
+    dict(contexts=[4 * 100, 40], k=300, page_size=8),   # N < K: pads
+]
+
+
+@pytest.mark.parametrize("case", ATT_CASES, ids=["tiny", "ragged_rowscale", "short"])
+def test_sparse_attend_given_oracle_indices(case):
+    _log(f"sparse_attend {case}")
+    wl = make_small_decode(layers="F", **case)
+    L, c = wl.layers[0], wl.caches[0]
+    r = oracle.layer_step("F", c, L.win, L.q, L.qix_codes, L.qix_scales, L.w, k=wl.k)
+    g_out, g_lse = csa2.sparse_attend(dev_cache(c), t(r["idx"]), t(L.q), dev_window(L.win))
+    torch.cuda.synchronize()
+    assert_attention_close(g_out.cpu().numpy(), g_lse.cpu().numpy(), r["out"], r["lse"], "attend")
+
+
+def test_sparse_attend_edge_cases():
+    _log("sparse_attend edges")
+    wl = make_small_decode([4 * 64, 4 * 64], layers="F", k=8)
+    c, L = wl.caches[0], wl.layers[0]
+    # request 0: nothing at all (no entries, empty window) -> out 0, lse -inf
+    # request 1: ids out of range / padding mixed with valid ones
+    idx = np.array([[[-1] * 8], [[3, 99999, -1, 5, 64, 63, -7, 0]]], np.int32)
+    win = hand_window(L.win.codes, length=[0, 17])
+    g_out, g_lse = csa2.sparse_attend(dev_cache(c), t(idx), t(L.q), dev_window(win))
+    o_out, o_lse, _ = oracle.sparse_attend(c, idx, L.q, win, sm_scale=TAU)
+    assert_attention_close(g_out.cpu().numpy(), g_lse.cpu().numpy(), o_out, o_lse, "edges")
+    # no window at all
+    g_out, g_lse = csa2.sparse_attend(dev_cache(c), t(idx), t(L.q), None)
+    o_out, o_lse, _ = oracle.sparse_attend(c, idx, L.q, None, sm_scale=TAU)
+    assert_attention_close(g_out.cpu().numpy(), g_lse.cpu().numpy(), o_out, o_lse, "no window")
+
+
+def test_sparse_attend_large_logits():
+    """Rows of 2688 and a large query: the running max keeps the softmax finite."""
+    wl = make_small_decode([4 * 64], layers="F", k=4)
+    c = wl.caches[0]
+    c.kv_codes[...] = 0x77  # every channel 6.0
+    c.kv_scales[...] = 0x7E  # x 448
+    q = np.full((1, 1, 16, 512), 3.0, np.float32)
+    idx = np.array([[[0, 1, 2, -1]]], np.int32)
+    win = hand_window(np.zeros((1, 1, 512), np.uint8), length=[0])
+    g_out, g_lse = csa2.sparse_attend(dev_cache(c), t(idx), t(q), dev_window(win))
+    o_out, o_lse, _ = oracle.sparse_attend(c, idx, q, win, sm_scale=TAU)
+    g_out, g_lse = g_out.cpu().numpy(), g_lse.cpu().numpy()
+    assert np.isfinite(g_out).all() and np.isfinite(g_lse).all()
+    assert np.abs(g_out - o_out).max() <= 2e-3 * 2688
+    assert np.abs(g_lse - o_lse).max() / abs(o_lse).max() < 1e-6
+
+
+def test_sparse_attend_prefill_windows():
+    _log("sparse_attend prefill windows")
+    wl = make_small_decode([4 * 900], layers="F", k=64, nq=7, prefill=True, page_size=32)
+    L, c = wl.layers[0], wl.caches[0]
+    r = oracle.layer_step("F", c, L.win, L.q, L.qix_codes, L.qix_scales, L.w, q_pos=wl.q_pos, k=64)
+    g_out, g_lse = csa2.sparse_attend(dev_cache(c), t(r["idx"]), t(L.q), dev_window(L.win), q_pos=t(wl.q_pos))
+    torch.cuda.synchronize()
+    assert_attention_close(g_out.cpu().numpy(), g_lse.cpu().numpy(), r["out"], r["lse"], "prefill")
+
+
+# ------------------------------------------------------------------ layer steps
+
+def _compare_workload(wl, res_g, res_o, what):
+    n_exact = n_rows = 0
+    for li, (g, o) in enumerate(zip(res_g, res_o)):
+        L = wl.layers[li]
+        B, nq = L.q.shape[0], L.q.shape[1]
+        if L.mode in ("F", "R"):
+            for b in range(B):
+                for q in range(nq):
+                    if L.mode == "F":
+                        same = assert_selection_matches(o["scores"][b, q], o["idx"][b, q], g["idx"][b, q],
+                                                        what=f"{what} L{li} b{b}")
+                    else:
+                        pool_ids = res_o[_last_full(wl, li)]["pool"][b, q]
+                        id_to_col = {int(e): j for j, e in enumerate(pool_ids) if e >= 0}
+                        same = assert_selection_matches(o["scores"][b, q], o["idx"][b, q], g["idx"][b, q],
+                                                        id_to_col=id_to_col, what=f"{what} L{li} b{b}")
+                    assert (np.diff(g["idx"][b, q][g["idx"][b, q] >= 0]) > 0).all(), "idx not ascending"
+                    n_rows += 1
+                    n_exact += same
+        if o.get("pool") is not None and g.get("pool") is not None:
+            for b in range(B):
+                for q in range(nq):
+                    assert_selection_matches(o["scores"][b, q], o["pool"][b, q], g["pool"][b, q],
+                                             what=f"{what} L{li} pool b{b}")
+    # attention: compare rows whose selection (and inherited selection) agrees exactly
+    _log(f"{what}: {n_exact}/{n_rows} selections identical")
+    for li, (g, o) in enumerate(zip(res_g, res_o)):
+        L = wl.layers[li]
+        idx_g = g["idx"] if g["idx"] is not None else None
+        src = li
+        while wl.layers[src].mode == "U":
+            src -= 1
+        same = (res_g[src]["idx"] == res_o[src]["idx"]).all(axis=-1)
+        if wl.layers[src].mode == "R":
+            same &= np.array([[set(res_g[_last_full(wl, src)]["pool"][b, q]) == set(res_o[_last_full(wl, src)]["pool"][b, q])
+                               for q in range(L.q.shape[1])] for b in range(L.q.shape[0])])
+        assert same.mean() >= 0.5, f"{what} L{li}: too few identical selections"
+        assert_attention_close(g["out"][same], g["lse"][same], o["out"][same], o["lse"][same], f"{what} L{li}")
+        del idx_g
+
+
+def _last_full(wl, li):
+    while wl.layers[li].mode != "F":
+        li -= 1
+    return li
+
+
+LAYER_CASES = [
+    dict(contexts=[8192], layers="F", k=256, pool=0),
+    dict(contexts=[4 * 3000, 4 * 1200], layers="FUU", k=128, pool=0, page_size=32, shuffle=True),
+    dict(contexts=[4 * 20000, 4 * 9000, 4 * 600], layers="FRUU", k=256, pool=2048, page_size=64, shuffle=True),
+    dict(contexts=[4 * 20000, 4 * 300], layers="FRU", k=512, pool=1024, page_size=64, row_scale=True),
+    dict(contexts=[4 * 40], layers="FRU", k=64, pool=128, page_size=8),  # N < K < pool
+]
+
+
+@pytest.mark.parametrize("case", LAYER_CASES, ids=["tiny_full", "full_reuse", "full_reindex_reuse",
+                                                   "rowscale", "short_ctx"])
+def test_layer_step_chain(case):
+    _log(f"layer chain {case}")
+    wl = make_small_decode(**case)
+    res_g = run_gpu(wl)
+    res_o = oracle.run_workload(wl, want_scores=True)
+    _compare_workload(wl, res_g, res_o, "chain")
+
+
+def test_reuse_equals_full_given_same_indices():
+    wl = make_small_decode([4 * 5000], layers="FU", k=256, page_size=64)
+    dw = DevWorkload(wl)
+    calls = dw.calls()
+    calls[0]()
+    F = dw.layers[0]
+    u = csa2.LayerCall("U", dw.caches[0], F["win"], F["q"], wl.k, idx_in=calls[0].idx_out)
+    u()
+    torch.cuda.synchronize()
+    assert torch.equal(u.out, calls[0].out) and torch.equal(u.lse, calls[0].lse)
+
+
+def test_layer_step_repeatable():
+    """Same inputs, same outputs (selection is deterministic; attention sums in a fixed order)."""
+    wl = make_small_decode([4 * 30000, 4 * 7000], layers="FRU", k=512, pool=2048, shuffle=True)
+    a = run_gpu(wl)
+    b = run_gpu(wl)
+    for x, y in zip(a, b):
+        if x["idx"] is not None:
+            assert (x["idx"] == y["idx"]).all()
+        assert (x["out"] == y["out"]).all() and (x["lse"] == y["lse"]).all()
