@@ -1,0 +1,304 @@
+"""Benchmark of the CSA2 decode hot path on one MI355X.
+
+One step = one decode step of the 1M-context workload: batch 8, 1,048,576
+tokens of context per request (262,144 compressed entries), layers
+[Full, Reindex, Reuse x4] with top-K 2048, a 16,384-entry candidate pool and a
+128-token FP8 window per layer. Inputs are seeded and synthetic and resident
+in HBM before timing; the step's inputs are rotated over several device
+copies so the 256 MB Infinity Cache cannot hold one step's data for the next.
+
+Printed: one JSON line (metric, value = queries/s, roofline of the dominant
+kernel measured live with HIP events, CPU-oracle baseline).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+WORKLOAD = "b8_1m_full_reindex_reuse4"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_index_score_b8_1m.json")
+SCORE_SRC = os.path.join(ROOT, "compressed_sparse_attention_06_amd", "csrc", "k_score.hip")
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--copies", type=int, default=5, help="device copies of the inputs, rotated per step")
+    p.add_argument("--kernel-iters", type=int, default=50)
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--skip-cpu", action="store_true")
+    p.add_argument("--no-graph", action="store_true")
+    p.add_argument("--copy-probe-mb", type=int, default=0,
+                   help="also run a plain device copy of this size (counter calibration)")
+    return p.parse_args()
+
+
+def step_bytes(wl) -> int:
+    """Algorithmic HBM bytes of one step (every byte the method must move once).
+
+    Per request with N entries, K = min(k, N), P = min(pool, N):
+      Full    = 36N + 160 + 4P + A(K)
+      Reindex = 40P + 160 + A(K)
+      Reuse   = A(K)
+      A(K)    = 292K + window + 32768 + 32832
+    (36 B indexer key per scored entry, 160 B indexer query + weights, 4 B per
+    pool id written, 40 B per pool entry rescored incl. its id, 288 B main-KV
+    row + 4 B id per selected entry, window rows, 32 KB fp32 query, 32 KB
+    output + 64 B lse.)
+    """
+    total = 0
+    for li, L in enumerate(wl.layers):
+        c = wl.caches[L.cache_id]
+        for b in range(wl.batch):
+            N = int(c.n_entries[b])
+            K, P = min(wl.k, N), min(wl.pool, N)
+            win = int(L.win.length[b]) * (512 + (4 if L.win.row_scale is not None else 0))
+            A = 292 * K + win + 32768 + 32832
+            if L.mode == "F":
+                total += 36 * N + 160 + 4 * P + A
+            elif L.mode == "R":
+                total += 40 * P + 160 + A
+            else:
+                total += A
+    return total * wl.nq
+
+
+def score_kernel_bytes(wl) -> int:
+    """Algorithmic bytes of one launch of the Full-layer scoring kernel:
+    36 B per scored entry + 160 B of indexer query and weights per query."""
+    c = wl.caches[0]
+    return int(sum(36 * int(n) + 160 for n in c.n_entries)) * wl.nq
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(decode requests shard by batch with no exchange, see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import compressed_sparse_attention_06_amd as csa2
+    from synth import make_decode_workload
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    csa2.lib()
+    t0 = time.time()
+    wl = make_decode_workload(WORKLOAD)
+    log(f"workload {WORKLOAD} generated in {time.time() - t0:.1f}s; modes {wl.modes}, "
+        f"N/request {int(wl.caches[0].n_entries[0])}")
+
+    def up(a, dtype=None):
+        if a is None:
+            return None
+        x = torch.from_numpy(np.ascontiguousarray(a))
+        return x.to(dev)
+
+    # ---- device inputs, `copies` independent copies ----
+    host = dict(caches=[], layers=[])
+    for c in wl.caches:
+        host["caches"].append(dict(kv_codes=up(c.kv_codes), kv_scales=up(c.kv_scales),
+                                   ix_codes=up(c.ix_codes), ix_scales=up(c.ix_scales),
+                                   block_table=up(c.block_table), n_entries=up(c.n_entries)))
+    for L in wl.layers:
+        host["layers"].append(dict(q=up(L.q), win_codes=up(L.win.codes), win_len=up(L.win.length),
+                                   qix_codes=up(L.qix_codes), qix_scales=up(L.qix_scales), w=up(L.w)))
+    copies = []
+    for ci in range(args.copies):
+        cl = (lambda x: x) if ci == 0 else (lambda x: None if x is None else x.clone())
+        caches = [csa2.Cache(**{k: cl(v) for k, v in c.items()}) for c in host["caches"]]
+        layers = [{k: cl(v) for k, v in L.items()} for L in host["layers"]]
+        copies.append((caches, layers))
+    torch.cuda.synchronize()
+    log(f"inputs on device: {args.copies} copies, "
+        f"{torch.cuda.memory_allocated() / 2**30:.2f} GiB allocated")
+
+    # shared outputs and per-layer workspaces (reused by every copy)
+    B, nq, k, pool = wl.batch, wl.nq, wl.k, wl.pool
+
+    def build_chain(caches, layers):
+        calls, last_idx, last_pool = [], None, None
+        for li, Lh in enumerate(wl.layers):
+            L = layers[li]
+            cache = caches[Lh.cache_id]
+            win = csa2.Window(codes=L["win_codes"], length=L["win_len"])
+            if Lh.mode == "F":
+                c = csa2.LayerCall("F", cache, win, L["q"], k, pool=pool, qix_codes=L["qix_codes"],
+                                   qix_scales=L["qix_scales"], w=L["w"], sm_scale=wl.sm_scale)
+                last_idx, last_pool = c.idx_out, c.pool_out
+            elif Lh.mode == "R":
+                c = csa2.LayerCall("R", cache, win, L["q"], k, pool=pool, qix_codes=L["qix_codes"],
+                                   qix_scales=L["qix_scales"], w=L["w"], idx_in=last_pool,
+                                   sm_scale=wl.sm_scale)
+                last_idx = c.idx_out
+            else:
+                c = csa2.LayerCall("U", cache, win, L["q"], k, idx_in=last_idx, sm_scale=wl.sm_scale)
+            calls.append(c)
+        return calls
+
+    chains = [build_chain(*cp) for cp in copies]
+
+    def run_step(i):
+        for c in chains[i % len(chains)]:
+            c()
+
+    # ---- eager timing ----
+    for i in range(args.warmup):
+        run_step(i)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    ev0.record()
+    for i in range(args.steps):
+        run_step(i)
+    ev1.record()
+    torch.cuda.synchronize()
+    eager_s = time.perf_counter() - w0
+    eager_ev_ms = ev0.elapsed_time(ev1) / args.steps
+    log(f"eager: {eager_s / args.steps * 1e3:.3f} ms/step wall, {eager_ev_ms:.3f} ms/step events")
+
+    # ---- HIP graph timing (one graph per input copy) ----
+    graph_s = None
+    if not args.no_graph:
+        try:
+            graphs = []
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                for ci in range(len(chains)):
+                    run_step(ci)
+            torch.cuda.current_stream().wait_stream(s)
+            torch.cuda.synchronize()
+            for ci in range(len(chains)):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    run_step(ci)
+                graphs.append(g)
+            torch.cuda.synchronize()
+            for i in range(args.warmup):
+                graphs[i % len(graphs)].replay()
+            torch.cuda.synchronize()
+            w0 = time.perf_counter()
+            for i in range(args.steps):
+                graphs[i % len(graphs)].replay()
+            torch.cuda.synchronize()
+            graph_s = time.perf_counter() - w0
+            log(f"graph: {graph_s / args.steps * 1e3:.3f} ms/step wall")
+        except Exception as e:  # capture unsupported: report eager only
+            log(f"graph capture failed: {e!r}")
+            graph_s = None
+
+    best_s = min(x for x in (eager_s, graph_s) if x is not None)
+    ms_per_step = best_s / args.steps * 1e3
+    qps = B * nq * args.steps / best_s
+    sbytes = step_bytes(wl)
+    gbps = sbytes / (best_s / args.steps) / 1e9
+
+    # ---- dominant kernel: Full-layer index scoring, timed live with HIP events ----
+    kb = score_kernel_bytes(wl)
+    scores = torch.empty(B, nq, copies[0][0][0].capacity, dtype=torch.float32, device=dev)
+    hist = torch.zeros(B, nq, 4096, dtype=torch.int32, device=dev)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.kernel_iters)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.kernel_iters)]
+    for i in range(5):
+        caches, layers = copies[i % len(copies)]
+        csa2.index_score(caches[0], layers[0]["qix_codes"], layers[0]["qix_scales"], layers[0]["w"],
+                         out=scores, hist=hist)
+    torch.cuda.synchronize()
+    for i in range(args.kernel_iters):
+        caches, layers = copies[i % len(copies)]
+        starts[i].record()
+        csa2.index_score(caches[0], layers[0]["qix_codes"], layers[0]["qix_scales"], layers[0]["w"],
+                         out=scores, hist=hist)
+        ends[i].record()
+    torch.cuda.synchronize()
+    k_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(starts, ends)]))
+    k_gbps = kb / (k_ms * 1e-3) / 1e9
+    log(f"index_score kernel: {k_ms * 1e3:.2f} us/launch, {k_gbps:.0f} GB/s algorithmic")
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        try:
+            rec = json.load(open(TRAFFIC_FILE))
+            src_hash = hashlib.sha256(open(SCORE_SRC, "rb").read()).hexdigest()
+            if rec.get("kernel_source_sha256") == src_hash and rec.get("workload") == WORKLOAD:
+                traffic = rec.get("bytes_per_launch")
+        except Exception:
+            traffic = None
+
+    if args.copy_probe_mb:
+        n = args.copy_probe_mb * 2**20
+        x = torch.empty(n, dtype=torch.uint8, device=dev)
+        y = torch.empty_like(x)
+        for _ in range(5):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        log(f"copy probe: 5 x {args.copy_probe_mb} MiB device copies")
+
+    # ---- CPU oracle baseline (bounded sample, host cores) ----
+    cpu = None
+    if not args.skip_cpu:
+        import oracle
+        reps, t_cpu = 0, 0.0
+        w0 = time.perf_counter()
+        while reps == 0 or (time.perf_counter() - w0) < args.cpu_seconds:
+            oracle.run_workload(wl)
+            reps += 1
+        t_cpu = time.perf_counter() - w0
+        cores = min(oracle.num_threads(), len(os.sched_getaffinity(0)), B * nq)
+        cpu = dict(value=round(B * nq * reps / t_cpu, 3), unit="queries/s", cores=cores, kind="oracle",
+                   sample=f"the whole 6-layer step of all {B} requests, repeated {reps}x "
+                          f"({t_cpu:.1f}s); fp64 C oracle, OpenMP over requests")
+        log(f"cpu oracle: {cpu['value']} queries/s on {cores} threads")
+
+    line = {
+        "metric": "CSA2 decode queries/s + achieved HBM GB/s (% of peak) at 1M ctx",
+        "value": round(qps, 1),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp4/fp8 inputs; fp4 and f16 MFMA, f32 accumulate",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD, "batch": B, "context_tokens": int(wl.contexts[0]),
+                   "entries_per_request": int(wl.caches[0].n_entries[0]), "layers": wl.modes,
+                   "top_k": k, "pool": pool, "window": 128, "input_copies": args.copies,
+                   "timing": "graph" if (graph_s is not None and graph_s <= eager_s) else "eager"},
+        "step_gbps": round(gbps, 1),
+        "step_pct_of_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
+        "step_algorithmic_bytes": sbytes,
+        "eager_ms_per_step": round(eager_s / args.steps * 1e3, 4),
+        "graph_ms_per_step": None if graph_s is None else round(graph_s / args.steps * 1e3, 4),
+        "roofline": {"kernel": "k_index_score (Full-layer lightning-indexer scoring)", "bound": "hbm",
+                     "achieved": round(k_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(k_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "bytes_per_launch": kb, "us_per_launch": round(k_ms * 1e3, 3)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -180,7 +180,7 @@ def alloc_workspace(nbytes: int, device=None) -> torch.Tensor:
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device or "cuda")
 
 
-def index_score(cache: Cache, qix_codes, qix_scales, w, q_pos=None, cand=None, out=None):
+def index_score(cache: Cache, qix_codes, qix_scales, w, q_pos=None, cand=None, out=None, hist=None):
     B, nq = qix_codes.shape[0], qix_codes.shape[1]
     _dev(qix_codes, torch.uint8, "qix_codes", (B, nq, 4, 32))
     _dev(qix_scales, torch.uint8, "qix_scales", (B, nq, 4, 4))
@@ -194,10 +194,11 @@ def index_score(cache: Cache, qix_codes, qix_scales, w, q_pos=None, cand=None, o
     if out is None:
         out = torch.empty(B, nq, n_cols, dtype=torch.float32, device=qix_codes.device)
     _dev(out, torch.float32, "scores", (B, nq, n_cols))
+    _dev(hist, torch.int32, "hist", (B, nq, 4096))
     cs = cache.struct()
     _check(lib().csa2_index_score(C.byref(cs), _ptr(qix_codes), _ptr(qix_scales), _ptr(w), _ptr(q_pos),
                                   _ptr(cand), C.c_int32(n_cand), C.c_int32(B), C.c_int32(nq),
-                                  _ptr(out), _stream()))
+                                  _ptr(out), _ptr(hist), _stream()))
     return out
 
 

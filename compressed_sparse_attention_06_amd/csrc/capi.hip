@@ -233,7 +233,7 @@ size_t csa2_workspace_bytes(csa2_mode mode, int32_t batch, int32_t nq, int32_t n
 csa2_status csa2_index_score(const csa2_cache *cache, const uint8_t *qix_codes,
                              const uint8_t *qix_scales, const float *w, const int32_t *q_pos,
                              const int32_t *cand, int32_t n_cand, int32_t batch, int32_t nq,
-                             float *scores, void *stream) {
+                             float *scores, uint32_t *hist, void *stream) {
   csa2_status s = check_cache(cache, false, true);
   if (s) return s;
   if (!qix_codes || !qix_scales || !w || !scores) return fail(CSA2_EINVAL, "NULL indexer query, weights or scores");
@@ -250,7 +250,7 @@ csa2_status csa2_index_score(const csa2_cache *cache, const uint8_t *qix_codes,
   a.nq = nq;
   a.n_cols = cand ? n_cand : cache->max_pages * cache->page_size;
   a.scores = scores;
-  a.hist = nullptr;
+  a.hist = hist;
   a.write_masked = 1;
   a.chunk = kScoreChunk;
   return hip_check(csa2::launch_index_score(a, batch * nq, (hipStream_t)stream), "index_score");

@@ -105,18 +105,23 @@ typedef struct {
  *  q_pos      [batch][nq] absolute token positions, or NULL (decode)
  *  cand       NULL: column j is entry j, n_cols = max_pages*page_size.
  *             else [batch][nq][n_cand] entry ids (a Reindex pool), n_cols = n_cand.
- *  scores     [batch][nq][n_cols] fp32 out; -inf for masked entries and pads. */
+ *  scores     [batch][nq][n_cols] fp32 out; -inf for masked entries and pads.
+ *  hist       NULL, or [batch][nq][4096] uint32 to which the count of each
+ *             finite score's top 12 order-key bits is added (the histogram
+ *             the selection starts from; the key of a score is its IEEE bits
+ *             with the sign bit flipped for non-negative values and all bits
+ *             flipped for negative ones, -0 counted as +0). */
 csa2_status csa2_index_score(const csa2_cache *cache, const uint8_t *qix_codes,
                              const uint8_t *qix_scales, const float *w, const int32_t *q_pos,
                              const int32_t *cand, int32_t n_cand, int32_t batch, int32_t nq,
-                             float *scores, void *stream);
+                             float *scores, uint32_t *hist, void *stream);
 
 /* Top-K selection ([P2] "CSA2": each selecting layer picks its own Top-K).
  * For each of the rows = batch*nq score rows of length n, selects the k
  * largest finite scores, ties broken towards the lower entry id; entry id of
  * column j is j, or cand[row][j] when cand != NULL. -inf columns are never
  * selected. idx_out [rows][k]: the selected ids in ascending order, then -1.
- * Workspace: csa2_workspace_bytes(CSA2_REINDEX, batch, nq, n, k, 0). */
+ * Workspace: csa2_workspace_bytes(CSA2_REINDEX, batch, nq, n, k, 0, 0). */
 csa2_status csa2_topk(const float *scores, const int32_t *cand, int32_t batch, int32_t nq,
                       int32_t n, int32_t k, int32_t *idx_out, void *ws, size_t ws_bytes,
                       void *stream);

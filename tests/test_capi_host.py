@@ -109,9 +109,9 @@ def test_other_entry_points_validation():
     L = csa2.lib()
     cs = _cache_struct()
     p = C.c_void_p(0x2000)
-    assert L.csa2_index_score(None, p, p, p, None, None, 0, 1, 1, p, None) == EINVAL
-    assert L.csa2_index_score(C.byref(cs), None, p, p, None, None, 0, 1, 1, p, None) == EINVAL
-    assert L.csa2_index_score(C.byref(cs), p, p, p, None, p, 0, 1, 1, p, None) == EINVAL
+    assert L.csa2_index_score(None, p, p, p, None, None, 0, 1, 1, p, None, None) == EINVAL
+    assert L.csa2_index_score(C.byref(cs), None, p, p, None, None, 0, 1, 1, p, None, None) == EINVAL
+    assert L.csa2_index_score(C.byref(cs), p, p, p, None, p, 0, 1, 1, p, None, None) == EINVAL
     assert L.csa2_topk(p, None, 1, 1, 100, 0, p, p, C.c_size_t(1 << 30), None) == EINVAL
     assert L.csa2_topk(p, None, 1, 1, 100, 8, p, None, C.c_size_t(0), None) == EWORKSPACE
     assert L.csa2_sparse_attend(C.byref(cs), p, 0, p, None, None, C.c_float(0.04), 1, 1, p, p, p,

@@ -90,6 +90,26 @@ def test_index_score_full(case):
     _check_scores(g, o, "full")
 
 
+def test_index_score_histogram():
+    """The optional histogram counts each finite score's top 12 order-key bits."""
+    wl = make_small_decode([4 * 9000, 4 * 100], layers="F", k=16, page_size=64, shuffle=True)
+    L, c = wl.layers[0], wl.caches[0]
+    hist = torch.zeros(2, 1, 4096, dtype=torch.int32, device="cuda")
+    g = csa2.index_score(dev_cache(c), t(L.qix_codes), t(L.qix_scales), t(L.w), hist=hist).cpu().numpy()
+    h = hist.cpu().numpy()
+    # expected from the oracle's scores rounded to fp32 (the key is defined on fp32 values)
+    o = oracle.index_score(c, L.qix_codes, L.qix_scales, L.w).astype(np.float32)
+    for b in range(2):
+        v = o[b, 0][np.isfinite(o[b, 0])]
+        u = v.view(np.uint32).copy()
+        u[u == 0x80000000] = 0
+        key = np.where(u & 0x80000000, ~u, u | 0x80000000).astype(np.uint32)
+        ref = np.bincount(key >> 20, minlength=4096)
+        # scores within fp32 rounding of a bin edge may land in the neighbouring bin
+        assert np.abs(h[b, 0] - ref).sum() <= 2 * max(1, int(1e-4 * len(v)))
+        assert h[b, 0].sum() == len(v) == np.isfinite(g[b, 0]).sum()
+
+
 def test_index_score_causal_and_candidates():
     _log("index_score q_pos + candidates")
     wl = make_small_decode([4 * 3000], layers="F", k=16, nq=6, prefill=True, page_size=32, shuffle=True)
@@ -296,3 +316,49 @@ def test_layer_step_repeatable():
         if x["idx"] is not None:
             assert (x["idx"] == y["idx"]).all()
         assert (x["out"] == y["out"]).all() and (x["lse"] == y["lse"]).all()
+
+
+def test_graph_capture_replays_match_eager():
+    """A captured Full/Reindex/Reuse chain replays to the eager result every time."""
+    _log("graph capture")
+    wl = make_small_decode([4 * 30000, 4 * 7000], layers="FRUU", k=512, pool=2048, shuffle=True)
+    dw = DevWorkload(wl)
+    calls = dw.calls()
+    for c in calls:
+        c()
+    torch.cuda.synchronize()
+    ref = [(c.out.clone(), c.lse.clone(), None if c.idx_out is None else c.idx_out.clone()) for c in calls]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for c in calls:
+            c()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for c in calls:
+            c()
+    for rep in range(4):
+        for c in calls:  # scribble over the outputs, then replay
+            c.out.fill_(float("nan"))
+            c.lse.zero_()
+            if c.idx_out is not None:
+                c.idx_out.fill_(-5)
+        junk = torch.randn(1 << 20, device="cuda").sum()  # unrelated eager work in between
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.isfinite(junk)
+        for c, (o, l, i) in zip(calls, ref):
+            assert torch.equal(c.out, o) and torch.equal(c.lse, l), f"replay {rep}"
+            if i is not None:
+                assert torch.equal(c.idx_out, i), f"replay {rep}"
+
+
+def test_full_size_tiny_config():
+    """The tiny benchmark workload (1 request, 8192-token context, top-256) at full size."""
+    from synth import make_decode_workload
+    wl = make_decode_workload("tiny_b1_8k_full")
+    res_g = run_gpu(wl)
+    res_o = oracle.run_workload(wl, want_scores=True)
+    _compare_workload(wl, res_g, res_o, "tiny config")
