@@ -26,35 +26,79 @@ csa2_status hip_check(hipError_t e, const char *what) {
   return fail(CSA2_EHIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-constexpr int kFinItems = 16384;     // rows up to this length select in LDS directly
-constexpr int kRowsPerSplit = 256;   // attention rows per workgroup
-constexpr int kScoreChunk = 2048;    // scoring columns per workgroup
-constexpr int kCompactChunk = 8192;  // compaction columns per workgroup
+constexpr int kFinItems = 4096;        // rows up to this length select in LDS directly
+constexpr int kScoreChunk = 2048;      // scoring columns per workgroup (contiguous entries)
+constexpr int kScoreChunkCand = 512;   // ... when gathering a candidate list
+constexpr int64_t kMaxSelectCols = CSA2_MAX_SELECT_COLS;
+static_assert(CSA2_MAX_SELECT_COLS <= SEL_MAX_WG * 8192, "the chunked selection takes SEL_MAX_WG chunks of 8192");
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Columns per selection chunk: the smallest of 2048, 4096, 8192 that cuts
+// the row into at most SEL_MAX_WG chunks and, where possible, keeps the
+// final pass (one workgroup per chunk, row and target) within two
+// workgroups per compute unit.
+int32_t select_chunk(int64_t n_cols, int64_t rows, int ntarget) {
+  int32_t fallback = 0;
+  for (int32_t c = 2048; c <= 8192; c <<= 1) {
+    const int64_t nwg = (n_cols + c - 1) / c;
+    if (nwg > SEL_MAX_WG) continue;
+    if (!fallback) fallback = c;
+    if (nwg * rows * ntarget <= 512) return c;
+  }
+  return fallback ? fallback : 8192;
+}
+
 struct WsLayout {
-  size_t scores = 0, hist = 0, ctr = 0, cand = 0, part = 0, total = 0;
+  size_t scores = 0, hist = 0, zero_end = 0, info = 0, counts = 0, suf = 0, list0 = 0, list1 = 0, eq0 = 0,
+         eq1 = 0, part = 0,
+         total = 0;
   bool compact = false;
-  int n_split = 0;
+  int max_wg = 0, chunk = 0, n_split = 0, rows_per_split = 256;
+  int64_t seg_stride = 0;
 };
 
-WsLayout ws_layout(csa2_mode mode, int64_t rows, int64_t n_cols, int32_t k, int32_t win_cap) {
+// Attention rows per workgroup: 256, or 128 when that leaves the GPU short of
+// workgroups (fewer than 512 at 256 rows each).
+int rows_per_split(int64_t rows, int64_t span) {
+  const int64_t wg256 = rows * ((span + 255) / 256);
+  return wg256 >= 512 ? 256 : 128;
+}
+
+WsLayout ws_layout(csa2_mode mode, int64_t rows, int64_t n_cols, int32_t k, int32_t win_cap, int ntarget) {
   WsLayout L;
   size_t off = 0;
   if (mode == CSA2_FULL || mode == CSA2_REINDEX) {
     L.compact = n_cols > kFinItems;
     L.scores = off;
     off = align256(off + (size_t)rows * n_cols * 4);
-    L.hist = off;
-    off = align256(off + (size_t)rows * HIST_BINS * 4);
-    L.ctr = off;
-    off = align256(off + (size_t)rows * 4 * 4);
-    L.cand = off;
-    if (L.compact) off = align256(off + (size_t)rows * n_cols * 4);
+    L.hist = off;  // zeroed by a fill before the scoring kernel adds to it
+    off += (size_t)rows * HIST_BINS * 4;
+    L.zero_end = off;
+    off = align256(off);
+    if (L.compact) {
+      L.chunk = select_chunk(n_cols, rows, ntarget);
+      L.max_wg = (int)((n_cols + L.chunk - 1) / L.chunk);
+      L.info = off;
+      off = align256(off + (size_t)rows * 2 * 4 * 4);
+      L.counts = off;
+      off = align256(off + (size_t)rows * 2 * L.max_wg * 4);
+      L.suf = off;
+      off = align256(off + (size_t)rows * 2 * L.max_wg * 256 * 4);
+      L.seg_stride = (int64_t)L.max_wg * L.chunk;
+      L.list0 = off;
+      off = align256(off + (size_t)rows * L.seg_stride * 8);
+      L.list1 = off;
+      off = align256(off + (size_t)rows * L.seg_stride * 8);
+      L.eq0 = off;
+      off = align256(off + (size_t)rows * L.seg_stride * 8);
+      L.eq1 = off;
+      off = align256(off + (size_t)rows * L.seg_stride * 8);
+    }
   }
   const int64_t span = (int64_t)k + (win_cap > 0 ? win_cap : 0);
-  L.n_split = (int)((span + kRowsPerSplit - 1) / kRowsPerSplit);
+  L.rows_per_split = rows_per_split(rows, span);
+  L.n_split = (int)((span + L.rows_per_split - 1) / L.rows_per_split);
   if (L.n_split < 1) L.n_split = 1;
   L.part = off;
   off = align256(off + (size_t)rows * L.n_split * CSA2_H * csa2::kPartStride * 4);
@@ -82,6 +126,7 @@ csa2_status check_cache(const csa2_cache *c, bool need_kv, bool need_ix) {
 csa2_status check_window(const csa2_window *w) {
   if (!w) return CSA2_OK;
   if (w->rows < 0 || w->rows > 65536) return fail(CSA2_EINVAL, "window rows %d outside [0, 65536]", w->rows);
+  if (!w->pos0 && w->rows > 4096) return fail(CSA2_EINVAL, "a decode window holds at most 4096 rows");
   if (w->window < 1 || w->window > 4096) return fail(CSA2_EINVAL, "window size %d outside [1, 4096]", w->window);
   if (w->rows > 0 && (!w->codes || !w->length)) return fail(CSA2_EINVAL, "window codes / length is NULL");
   return CSA2_OK;
@@ -114,14 +159,63 @@ csa2_status check_ws(void *ws, size_t ws_bytes, size_t need) {
   return CSA2_OK;
 }
 
-// Selection of the top-T columns of `rows` score rows (optionally the top K2
-// of that set too). Scores already sit in the workspace's score region, and
-// for the compact path the histogram was accumulated by the scoring kernel
-// (hist_ready) or is built here.
+// Selection of the top-T[t] columns of `rows` score rows for one or two
+// targets. Scores sit in the workspace's score region (or the caller's); in
+// the compact path the coarse histogram was accumulated by the scoring kernel
+// (hist_ready, after the zeroing fill) or is built here.
+struct SelTarget {
+  int32_t T;
+  int32_t *out;
+  int32_t stride;
+};
+
 csa2_status run_select(const WsLayout &L, char *ws, int rows, int32_t n_cols, const int32_t *cand_map,
-                       const int32_t *n_entries, const int32_t *q_pos, int32_t nq, int32_t T,
-                       int32_t *outT, int32_t outT_stride, int sortT, int32_t K2, int32_t *outK2,
-                       int32_t id_limit, bool hist_ready, const float *scores, hipStream_t st) {
+                       const int32_t *n_entries, const int32_t *q_pos, int32_t nq, const SelTarget *tg,
+                       int ntarget, bool hist_ready, const float *scores, hipStream_t st) {
+  if (!L.compact) {
+    csa2::DirectArgs d{};
+    d.scores = scores;
+    d.n_cols = n_cols;
+    d.cand_map = cand_map;
+    d.n_entries = n_entries;
+    d.q_pos = q_pos;
+    d.nq = nq;
+    for (int i = 0; i < ntarget; ++i) {
+      d.T[i] = tg[i].T;
+      d.out[i] = tg[i].out;
+      d.out_stride[i] = tg[i].stride;
+    }
+    return hip_check(csa2::launch_select_direct(d, rows, ntarget, st), "select");
+  }
+  csa2_status s;
+  if (!hist_ready) {
+    s = hip_check(csa2::launch_fill_u32((uint32_t *)(ws + L.hist), (int64_t)((L.zero_end - L.hist) / 4), 0u, st),
+                  "fill");
+    if (s) return s;
+    s = hip_check(csa2::launch_hist(scores, n_cols, rows, (uint32_t *)(ws + L.hist), st), "hist");
+    if (s) return s;
+  }
+  csa2::CompactArgs c{};
+  c.scores = scores;
+  c.n_cols = n_cols;
+  c.cand_map = cand_map;
+  c.n_entries = n_entries;
+  c.q_pos = q_pos;
+  c.nq = nq;
+  c.hist = (const uint32_t *)(ws + L.hist);
+  c.ntarget = ntarget;
+  for (int i = 0; i < ntarget; ++i) c.T[i] = tg[i].T;
+  c.info = (int32_t *)(ws + L.info);
+  c.counts = (uint32_t *)(ws + L.counts);
+  c.suf = (uint32_t *)(ws + L.suf);
+  c.list[0] = (uint64_t *)(ws + L.list0);
+  c.list[1] = (uint64_t *)(ws + L.list1);
+  c.eq[0] = (uint64_t *)(ws + L.eq0);
+  c.eq[1] = (uint64_t *)(ws + L.eq1);
+  c.seg_stride = L.seg_stride;
+  c.max_wg = L.max_wg;
+  c.chunk = L.chunk;
+  if ((s = hip_check(csa2::launch_compact(c, rows, st), "compact"))) return s;
   csa2::FinalArgs f{};
   f.scores = scores;
   f.n_cols = n_cols;
@@ -129,45 +223,22 @@ csa2_status run_select(const WsLayout &L, char *ws, int rows, int32_t n_cols, co
   f.n_entries = n_entries;
   f.q_pos = q_pos;
   f.nq = nq;
-  f.T = T;
-  f.outT = outT;
-  f.outT_stride = outT_stride;
-  f.sortT = sortT;
-  f.K2 = K2;
-  f.outK2 = outK2;
-  f.K2_stride = K2;
-  f.id_limit = id_limit;
-  if (L.compact) {
-    uint32_t *hist = (uint32_t *)(ws + L.hist);
-    uint32_t *ctr = (uint32_t *)(ws + L.ctr);
-    csa2_status s;
-    if (!hist_ready) {
-      s = hip_check(csa2::launch_fill_u32(hist, (int64_t)((L.cand - L.hist) / 4), 0u, st), "fill");
-      if (s) return s;
-      s = hip_check(csa2::launch_hist(scores, n_cols, rows, hist, st), "hist");
-      if (s) return s;
-    }
-    csa2::CompactArgs c{};
-    c.scores = scores;
-    c.n_cols = n_cols;
-    c.cand_map = cand_map;
-    c.n_entries = n_entries;
-    c.q_pos = q_pos;
-    c.nq = nq;
-    c.hist = hist;
-    c.T = T;
-    c.out = outT;
-    c.out_stride = outT_stride;
-    c.cand_cols = (int32_t *)(ws + L.cand);
-    c.ctr = ctr;
-    c.chunk = kCompactChunk;
-    s = hip_check(csa2::launch_compact(c, rows, st), "compact");
-    if (s) return s;
-    f.hist = hist;
-    f.cand_cols = c.cand_cols;
-    f.ctr = ctr;
+  f.info = c.info;
+  f.counts = c.counts;
+  f.suf = c.suf;
+  f.list[0] = c.list[0];
+  f.list[1] = c.list[1];
+  f.eq[0] = c.eq[0];
+  f.eq[1] = c.eq[1];
+  f.seg_stride = c.seg_stride;
+  f.max_wg = c.max_wg;
+  f.chunk = c.chunk;
+  for (int i = 0; i < ntarget; ++i) {
+    f.T[i] = tg[i].T;
+    f.out[i] = tg[i].out;
+    f.out_stride[i] = tg[i].stride;
   }
-  return hip_check(csa2::launch_final(f, rows, st), "select");
+  return hip_check(csa2::launch_final(f, rows, ntarget, st), "select");
 }
 
 csa2_status run_attend(const WsLayout &L, char *ws, const csa2_cache *cache, const int32_t *idx,
@@ -190,7 +261,7 @@ csa2_status run_attend(const WsLayout &L, char *ws, const csa2_cache *cache, con
   a.q_pos = q_pos;
   a.nq = nq;
   a.sm_scale = sm_scale;
-  a.rows_per_split = kRowsPerSplit;
+  a.rows_per_split = L.rows_per_split;
   a.n_split = L.n_split;
   a.part = (float *)(ws + L.part);
   csa2_status s = hip_check(csa2::launch_attend(a, rows, st), "attend");
@@ -224,10 +295,10 @@ const char *csa2_version(void) { return "csa2-mi355x 0.1 (gfx950)"; }
 
 size_t csa2_workspace_bytes(csa2_mode mode, int32_t batch, int32_t nq, int32_t n_cols, int32_t k,
                             int32_t pool, int32_t win_cap) {
-  (void)pool;
   if (batch <= 0 || nq <= 0 || k <= 0) return 0;
   if (mode == CSA2_REUSE) n_cols = 0;
-  return ws_layout(mode, (int64_t)batch * nq, n_cols < 0 ? 0 : n_cols, k, win_cap).total;
+  const int ntarget = (mode == CSA2_FULL && pool > 0) ? 2 : 1;
+  return ws_layout(mode, (int64_t)batch * nq, n_cols < 0 ? 0 : n_cols, k, win_cap, ntarget).total;
 }
 
 csa2_status csa2_index_score(const csa2_cache *cache, const uint8_t *qix_codes,
@@ -261,13 +332,17 @@ csa2_status csa2_topk(const float *scores, const int32_t *cand, int32_t batch, i
   if (!scores || !idx_out) return fail(CSA2_EINVAL, "NULL scores or idx_out");
   if (batch <= 0 || nq <= 0 || n <= 0) return fail(CSA2_EINVAL, "batch, nq and n must be positive");
   if (k <= 0 || k > CSA2_MAX_K) return fail(CSA2_EINVAL, "k = %d outside [1, %d]", k, CSA2_MAX_K);
-  const WsLayout L = ws_layout(CSA2_REINDEX, (int64_t)batch * nq, n, k, 0);
+  if ((int64_t)n > kMaxSelectCols)
+    return fail(CSA2_EUNSUPPORTED, "more than %lld scores per row", (long long)kMaxSelectCols);
+  const WsLayout L = ws_layout(CSA2_REINDEX, (int64_t)batch * nq, n, k, 0, 1);
   csa2_status s = check_ws(ws, ws_bytes, L.total);
   if (s) return s;
-  // ids of a candidate map are unbounded: sort them over the int32 range only when they are columns
-  const int32_t id_limit = cand ? 0x7FFFFFFF : n;
-  return run_select(L, (char *)ws, batch * nq, n, cand, nullptr, nullptr, nq, k, idx_out, k, 1, 0,
-                    nullptr, id_limit, false, scores, (hipStream_t)stream);
+  const SelTarget tg{k, idx_out, k};
+  s = run_select(L, (char *)ws, batch * nq, n, cand, nullptr, nullptr, nq, &tg, 1, false, scores,
+                 (hipStream_t)stream);
+  if (s || !cand || !L.compact) return s;
+  // the chunked path writes ids in column order: sort them when ids are a map
+  return hip_check(csa2::launch_sort_rows(idx_out, k, k, batch * nq, (hipStream_t)stream), "sort");
 }
 
 csa2_status csa2_sparse_attend(const csa2_cache *cache, const int32_t *idx, int32_t k, const float *q,
@@ -281,7 +356,7 @@ csa2_status csa2_sparse_attend(const csa2_cache *cache, const int32_t *idx, int3
   if (batch <= 0 || nq <= 0) return fail(CSA2_EINVAL, "batch (%d) and nq (%d) must be positive", batch, nq);
   if (k <= 0 || k > CSA2_MAX_K) return fail(CSA2_EINVAL, "k = %d outside [1, %d]", k, CSA2_MAX_K);
   if (!isfinite(sm_scale)) return fail(CSA2_EINVAL, "sm_scale is not finite");
-  const WsLayout L = ws_layout(CSA2_REUSE, (int64_t)batch * nq, 0, k, win_cap_of(win, q_pos));
+  const WsLayout L = ws_layout(CSA2_REUSE, (int64_t)batch * nq, 0, k, win_cap_of(win, q_pos), 1);
   if ((s = check_ws(ws, ws_bytes, L.total))) return s;
   return run_attend(L, (char *)ws, cache, idx, k, q, win, q_pos, sm_scale, batch * nq, nq, out, lse,
                     (hipStream_t)stream);
@@ -316,9 +391,11 @@ csa2_status csa2_layer_step(const csa2_layer_args *p, void *stream) {
 
   const int rows = p->batch * p->nq;
   const int32_t capacity = p->cache->max_pages * p->cache->page_size;
+  if (selecting && (int64_t)(p->mode == CSA2_FULL ? capacity : p->pool) > kMaxSelectCols)
+    return fail(CSA2_EUNSUPPORTED, "more than %lld entries per row to select from", (long long)kMaxSelectCols);
   const int32_t n_cols = p->mode == CSA2_FULL ? capacity : (p->mode == CSA2_REINDEX ? p->pool : 0);
   const int32_t wcap = win_cap_of(p->win, p->q_pos);
-  const WsLayout L = ws_layout(p->mode, rows, n_cols, p->k, wcap);
+  const WsLayout L = ws_layout(p->mode, rows, n_cols, p->k, wcap, (p->mode == CSA2_FULL && p->pool > 0) ? 2 : 1);
   if ((s = check_ws(p->ws, p->ws_bytes, L.total))) return s;
   hipStream_t st = (hipStream_t)stream;
   char *ws = (char *)p->ws;
@@ -327,7 +404,8 @@ csa2_status csa2_layer_step(const csa2_layer_args *p, void *stream) {
   if (selecting) {
     float *scores = (float *)(ws + L.scores);
     if (L.compact) {
-      s = hip_check(csa2::launch_fill_u32((uint32_t *)(ws + L.hist), (int64_t)((L.cand - L.hist) / 4), 0u, st), "fill");
+      s = hip_check(csa2::launch_fill_u32((uint32_t *)(ws + L.hist), (int64_t)((L.zero_end - L.hist) / 4), 0u, st),
+                    "fill");
       if (s) return s;
     }
     csa2::ScoreArgs a{};
@@ -343,18 +421,18 @@ csa2_status csa2_layer_step(const csa2_layer_args *p, void *stream) {
     a.scores = scores;
     a.hist = L.compact ? (uint32_t *)(ws + L.hist) : nullptr;
     a.write_masked = 0;
-    a.chunk = kScoreChunk;
+    a.chunk = p->mode == CSA2_REINDEX ? kScoreChunkCand : kScoreChunk;
+    // the pool and the top-K of a Full layer are both selected over every visible entry
+    const SelTarget tgf[2] = {{p->k, p->idx_out, p->k}, {p->pool, p->pool_out, p->pool}};
+    const SelTarget tgr{p->k, p->idx_out, p->k};
+    const SelTarget *tg = p->mode == CSA2_FULL ? tgf : &tgr;
+    const int ntarget = (p->mode == CSA2_FULL && p->pool > 0) ? 2 : 1;
     if ((s = hip_check(csa2::launch_index_score(a, rows, st), "index_score"))) return s;
-    if (p->mode == CSA2_FULL) {
-      const bool with_pool = p->pool > 0;
-      s = run_select(L, ws, rows, n_cols, nullptr, p->cache->n_entries, p->q_pos, p->nq,
-                     with_pool ? p->pool : p->k, with_pool ? p->pool_out : p->idx_out,
-                     with_pool ? p->pool : p->k, with_pool ? 0 : 1, with_pool ? p->k : 0,
-                     with_pool ? p->idx_out : nullptr, capacity, true, scores, st);
-    } else {
-      s = run_select(L, ws, rows, n_cols, p->idx_in, nullptr, nullptr, p->nq, p->k, p->idx_out,
-                     p->k, 1, 0, nullptr, capacity, true, scores, st);
-    }
+    if (p->mode == CSA2_FULL)
+      s = run_select(L, ws, rows, n_cols, nullptr, p->cache->n_entries, p->q_pos, p->nq, tg, ntarget, true,
+                     scores, st);
+    else
+      s = run_select(L, ws, rows, n_cols, p->idx_in, nullptr, nullptr, p->nq, tg, 1, true, scores, st);
     if (s) return s;
     att_idx = p->idx_out;
   }

@@ -30,7 +30,46 @@ namespace csa2 {
 
 typedef __attribute__((address_space(3))) v4s *lds_v4s_ptr;
 
+// Inputs of one row slice of one tile: an FP4 entry uses c[0..1] (32 code
+// bytes) and sc (4 scale bytes), a window row uses c[0..3] (64 E4M3 bytes).
+struct RowFetch {
+  v4i c[4];
+  uint32_t sc;
+  float rs;
+  int kind;  // 0 none, 1 entry, 2 window row
+};
+
+// Loads of one slice are issued unconditionally from clamped, in-range
+// addresses (row 0 stands in for a missing row) and level by level (ids, then
+// block-table words, then data), so that no branch or wait separates loads
+// that could be in flight together; validity is applied afterwards.
+__device__ __forceinline__ void fetch_entry(const AttendArgs &a, int32_t id, int32_t page, bool in_range,
+                                            int32_t nent, int gpart, RowFetch &f) {
+  const int sh = a.c.page_shift;
+  const bool ok = in_range && id >= 0 && id < nent && (id >> sh) < a.c.max_pages && page >= 0 &&
+                  page < a.c.num_pages;
+  const int64_t crow = ok ? ((int64_t)page << sh) + (id & ((1 << sh) - 1)) : 0;
+  f.c[0] = *(const v4i *)(a.c.kv_codes + crow * 256 + gpart * 32);
+  f.c[1] = *(const v4i *)(a.c.kv_codes + crow * 256 + gpart * 32 + 16);
+  f.sc = *(const uint32_t *)(a.c.kv_scales + crow * 32 + gpart * 4);
+  f.rs = 1.f;
+  f.kind = ok ? 1 : 0;
+}
+
+__device__ __forceinline__ void fetch_window(const AttendArgs &a, int b, int32_t j, bool ok, int gpart,
+                                             RowFetch &f) {
+  const int64_t wr = (int64_t)b * a.win_rows + (ok ? j : 0);
+  const uint8_t *src = a.win_codes + wr * CSA2_D + gpart * 64;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) f.c[i] = *(const v4i *)(src + 16 * i);
+  f.sc = 0;
+  f.rs = a.win_row_scale ? a.win_row_scale[wr] : 1.f;
+  f.kind = ok ? 2 : 0;
+}
+
+template <int RPS>
 __global__ __launch_bounds__(256) void k_attend(AttendArgs a) {
+  constexpr int NT = RPS / AT_TILE;
   __shared__ __attribute__((aligned(16))) _Float16 sQ[CSA2_H * AT_PITCH];
   __shared__ __attribute__((aligned(16))) _Float16 sQlo[CSA2_H * AT_PITCH];
   __shared__ __attribute__((aligned(16))) _Float16 sR[AT_TILE * AT_PITCH];
@@ -44,11 +83,58 @@ __global__ __launch_bounds__(256) void k_attend(AttendArgs a) {
   const int b = r / a.nq;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int32_t total_pos = a.k + a.win_cap;
-  const int32_t p0 = split * a.rows_per_split;
-  const int32_t p1 = min(p0 + a.rows_per_split, total_pos);
+  const int32_t p0 = split * RPS;
+  const int32_t p1 = min(p0 + RPS, total_pos);
   const int32_t nent = a.c.n_entries[b];
 
-  // ---- Q: per-head power-of-two normalisation, fp16, into LDS ----
+  // window geometry for this query
+  int32_t w_first = 0, w_last = -1;
+  if (a.win_codes) {
+    const int32_t len = a.win_len[b];
+    if (a.win_pos0) {
+      const int32_t pq = a.q_pos ? a.q_pos[r] : 0x7FFFFFFF;
+      const int64_t rel = (int64_t)pq - a.win_pos0[b];
+      w_first = (int32_t)max((int64_t)0, rel - a.win_window + 1);
+      w_last = (int32_t)min(min((int64_t)len, (int64_t)a.win_rows) - 1, rel);
+    } else {
+      w_first = 0;
+      w_last = min(len, a.win_rows) - 1;
+    }
+  }
+
+  // ---- issue every global load of this slice first ----
+  // A split holds only selected entries, only window rows, or (when k is not
+  // a multiple of the split length) both; the first two take the batched
+  // path, the mixed split fetches each tile just before it is used.
+  const int grow = tid >> 3, gpart = tid & 7;
+  const int kind = (p1 <= a.k) ? 0 : (p0 >= a.k ? 1 : 2);  // uniform per workgroup
+  RowFetch pf[NT];
+  if (kind == 0) {
+    int32_t idv[NT], pgv[NT];
+    const int32_t nent_c = max(nent, 1);
+#pragma unroll
+    for (int ti = 0; ti < NT; ++ti) {
+      const int32_t pos = min(p0 + ti * AT_TILE + grow, p1 - 1);
+      idv[ti] = a.idx[(int64_t)r * a.k + pos];
+    }
+#pragma unroll
+    for (int ti = 0; ti < NT; ++ti) {
+      const int32_t pg = min(min(max(idv[ti], 0), nent_c - 1) >> a.c.page_shift, a.c.max_pages - 1);
+      pgv[ti] = a.c.block_table[(int64_t)b * a.c.max_pages + pg];
+    }
+#pragma unroll
+    for (int ti = 0; ti < NT; ++ti)
+      fetch_entry(a, idv[ti], pgv[ti], p0 + ti * AT_TILE + grow < p1, nent, gpart, pf[ti]);
+  } else if (kind == 1) {
+#pragma unroll
+    for (int ti = 0; ti < NT; ++ti) {
+      const int32_t pos = p0 + ti * AT_TILE + grow;
+      const int32_t j = w_first + (pos - a.k);
+      fetch_window(a, b, j, pos < p1 && j <= w_last, gpart, pf[ti]);
+    }
+  }
+
+  // ---- Q: per-head power-of-two normalisation, fp16 hi + lo, into LDS ----
   {
     const int h = tid >> 4, part = tid & 15;
     const float *qh = a.q + ((int64_t)r * CSA2_H + h) * CSA2_D + part * 32;
@@ -87,21 +173,6 @@ __global__ __launch_bounds__(256) void k_attend(AttendArgs a) {
       sL[h] = 0.f;
     }
   }
-
-  // window geometry for this query
-  int32_t w_first = 0, w_last = -1;
-  if (a.win_codes) {
-    const int32_t len = a.win_len[b];
-    if (a.win_pos0) {
-      const int32_t pq = a.q_pos ? a.q_pos[r] : 0x7FFFFFFF;
-      const int64_t rel = (int64_t)pq - a.win_pos0[b];
-      w_first = (int32_t)max((int64_t)0, rel - a.win_window + 1);
-      w_last = (int32_t)min(min((int64_t)len, (int64_t)a.win_rows) - 1, rel);
-    } else {
-      w_first = 0;
-      w_last = min(len, a.win_rows) - 1;
-    }
-  }
   const float kLog2e = 1.4426950408889634f;
   const float zscale = a.sm_scale * kLog2e;
 
@@ -109,57 +180,54 @@ __global__ __launch_bounds__(256) void k_attend(AttendArgs a) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) accO[i] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-  for (int32_t t0 = p0; t0 < p1; t0 += AT_TILE) {
-    // ---- gather + dequantise one tile into sR ----
-    {
-      const int row = tid >> 3, part = tid & 7;
-      const int32_t pos = t0 + row;
-      bool valid = false;
-      float rs = 1.f;
-      _Float16 *dst = &sR[row * AT_PITCH + part * 64];
-      if (pos < p1 && pos < a.k) {
+#pragma unroll
+  for (int ti = 0; ti < NT; ++ti) {
+    if (p0 + ti * AT_TILE >= p1) break;  // uniform
+    if (kind == 2) {
+      const int32_t pos = p0 + ti * AT_TILE + grow;
+      if (pos < a.k) {
         const int32_t id = a.idx[(int64_t)r * a.k + pos];
-        const int64_t crow = cache_row(a.c, b, id, nent);
-        if (crow >= 0) {
-          valid = true;
-          const v4i c0 = *(const v4i *)(a.c.kv_codes + crow * 256 + part * 32);
-          const v4i c1 = *(const v4i *)(a.c.kv_codes + crow * 256 + part * 32 + 16);
-          const uint32_t sw = *(const uint32_t *)(a.c.kv_scales + crow * 32 + part * 4);
-          const uint32_t cw[8] = {(uint32_t)c0[0], (uint32_t)c0[1], (uint32_t)c0[2], (uint32_t)c0[3],
-                                  (uint32_t)c1[0], (uint32_t)c1[1], (uint32_t)c1[2], (uint32_t)c1[3]};
-#pragma unroll
-          for (int gi = 0; gi < 4; ++gi) {
-            const _Float16 s = (_Float16)e4m3_to_f32((sw >> (8 * gi)) & 0xFFu);
-            *(v8h *)(dst + gi * 16) = fp4x8_dequant(cw[2 * gi], s);
-            *(v8h *)(dst + gi * 16 + 8) = fp4x8_dequant(cw[2 * gi + 1], s);
-          }
-        }
-      } else if (pos < p1) {
+        const int32_t pg = min(min(max(id, 0), max(nent, 1) - 1) >> a.c.page_shift, a.c.max_pages - 1);
+        const int32_t page = a.c.block_table[(int64_t)b * a.c.max_pages + pg];
+        fetch_entry(a, id, page, true, nent, gpart, pf[ti]);
+      } else {
         const int32_t j = w_first + (pos - a.k);
-        if (j <= w_last) {
-          valid = true;
-          const uint8_t *src = a.win_codes + ((int64_t)b * a.win_rows + j) * CSA2_D + part * 64;
-          if (a.win_row_scale) rs = a.win_row_scale[(int64_t)b * a.win_rows + j];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const v4i x = *(const v4i *)(src + 16 * i);
-            const v4h h0 = e4m3x4_to_f16((uint32_t)x[0]), h1 = e4m3x4_to_f16((uint32_t)x[1]);
-            const v4h h2 = e4m3x4_to_f16((uint32_t)x[2]), h3 = e4m3x4_to_f16((uint32_t)x[3]);
-            const v8h lo = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
-            const v8h hi = {h2[0], h2[1], h2[2], h2[3], h3[0], h3[1], h3[2], h3[3]};
-            *(v8h *)(dst + 16 * i) = lo;
-            *(v8h *)(dst + 16 * i + 8) = hi;
-          }
-        }
+        fetch_window(a, b, j, pos < p1 && j <= w_last, gpart, pf[ti]);
       }
-      if (!valid) {
+    }
+    // ---- dequantise this thread's slice of the tile into sR ----
+    {
+      _Float16 *dst = &sR[grow * AT_PITCH + gpart * 64];
+      if (pf[ti].kind == 1) {
+        const uint32_t sw = pf[ti].sc;
+        const uint32_t cw[8] = {(uint32_t)pf[ti].c[0][0], (uint32_t)pf[ti].c[0][1], (uint32_t)pf[ti].c[0][2],
+                                (uint32_t)pf[ti].c[0][3], (uint32_t)pf[ti].c[1][0], (uint32_t)pf[ti].c[1][1],
+                                (uint32_t)pf[ti].c[1][2], (uint32_t)pf[ti].c[1][3]};
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi) {
+          const _Float16 sg = (_Float16)e4m3_to_f32((sw >> (8 * gi)) & 0xFFu);
+          *(v8h *)(dst + gi * 16) = fp4x8_dequant(cw[2 * gi], sg);
+          *(v8h *)(dst + gi * 16 + 8) = fp4x8_dequant(cw[2 * gi + 1], sg);
+        }
+      } else if (pf[ti].kind == 2) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const v4i x = pf[ti].c[i];
+          const v4h h0 = e4m3x4_to_f16((uint32_t)x[0]), h1 = e4m3x4_to_f16((uint32_t)x[1]);
+          const v4h h2 = e4m3x4_to_f16((uint32_t)x[2]), h3 = e4m3x4_to_f16((uint32_t)x[3]);
+          const v8h lo = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+          const v8h hi = {h2[0], h2[1], h2[2], h2[3], h3[0], h3[1], h3[2], h3[3]};
+          *(v8h *)(dst + 16 * i) = lo;
+          *(v8h *)(dst + 16 * i + 8) = hi;
+        }
+      } else {
         const v8h zero = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
         for (int i = 0; i < 8; ++i) *(v8h *)(dst + 8 * i) = zero;
       }
-      if (part == 0) {
-        sValid[row] = valid ? 1 : 0;
-        sRscale[row] = rs;
+      if (gpart == 0) {
+        sValid[grow] = pf[ti].kind != 0;
+        sRscale[grow] = pf[ti].rs;
       }
     }
     __syncthreads();
@@ -196,8 +264,8 @@ __global__ __launch_bounds__(256) void k_attend(AttendArgs a) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int row = rr + u;
-        const float s = sS[0][h][row] + sS[1][h][row] + sS[2][h][row] + sS[3][h][row];
-        z[u] = sValid[row] ? s * qs * sRscale[row] : -INFINITY;
+        const float sv = sS[0][h][row] + sS[1][h][row] + sS[2][h][row] + sS[3][h][row];
+        z[u] = sValid[row] ? sv * qs * sRscale[row] : -INFINITY;
       }
       float tmax = fmaxf(z[0], z[1]);
       tmax = fmaxf(tmax, __shfl_xor(tmax, 1));
@@ -272,38 +340,60 @@ __global__ __launch_bounds__(256) void k_attend(AttendArgs a) {
   }
 }
 
-// Combine split partials: out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
+// Combine split partials of one (row, head): out = sum_s 2^(m_s - M) O_s /
+// sum_s 2^(m_s - M) l_s, one thread per channel. Splits are read in batches
+// of 16 so their loads are in flight together.
 __global__ __launch_bounds__(512) void k_merge(MergeArgs a) {
-  const int r = blockIdx.x, c = threadIdx.x;
-  const float *base = a.part + (int64_t)r * a.n_split * CSA2_H * kPartStride;
-  for (int h = 0; h < CSA2_H; ++h) {
-    float M = -INFINITY;
-    for (int s = 0; s < a.n_split; ++s)
-      M = fmaxf(M, base[((int64_t)s * CSA2_H + h) * kPartStride + CSA2_D]);
-    float L = 0.f, o = 0.f;
-    if (M != -INFINITY) {
-      for (int s = 0; s < a.n_split; ++s) {
-        const float *ps = base + ((int64_t)s * CSA2_H + h) * kPartStride;
-        const float ms = ps[CSA2_D];
-        if (ms == -INFINITY) continue;
-        const float wgt = exp2f(ms - M);
-        L += wgt * ps[CSA2_D + 1];
-        o += wgt * ps[c];
+  constexpr int BATCH = 16;
+  const int h = blockIdx.x, r = blockIdx.y, c = threadIdx.x;
+  const float *base = a.part + (int64_t)r * a.n_split * CSA2_H * kPartStride + (int64_t)h * kPartStride;
+  const int64_t sstride = (int64_t)CSA2_H * kPartStride;
+  const int last = a.n_split - 1;
+  float M = -INFINITY;
+  for (int s0 = 0; s0 < a.n_split; s0 += BATCH) {
+    float mv[BATCH];
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) mv[u] = base[min(s0 + u, last) * sstride + CSA2_D];
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) M = fmaxf(M, mv[u]);  // repeats of the last split change nothing
+  }
+  float L = 0.f, o = 0.f;
+  if (M != -INFINITY) {
+    for (int s0 = 0; s0 < a.n_split; s0 += BATCH) {
+      float mv[BATCH], lv[BATCH], ov[BATCH];
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u) {
+        const float *ps = base + min(s0 + u, last) * sstride;
+        mv[u] = ps[CSA2_D];
+        lv[u] = ps[CSA2_D + 1];
+        ov[u] = ps[c];
+      }
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u) {
+        const float wgt = (s0 + u < a.n_split && mv[u] != -INFINITY) ? exp2f(mv[u] - M) : 0.f;
+        L += wgt * lv[u];
+        o += wgt * ov[u];
       }
     }
-    a.out[((int64_t)r * CSA2_H + h) * CSA2_D + c] = (L > 0.f) ? o / L : 0.f;
-    if (c == 0)
-      a.lse[(int64_t)r * CSA2_H + h] = (L > 0.f) ? (M + log2f(L)) * 0.6931471805599453f : -INFINITY;
   }
+  a.out[((int64_t)r * CSA2_H + h) * CSA2_D + c] = (L > 0.f) ? o / L : 0.f;
+  if (c == 0)
+    a.lse[(int64_t)r * CSA2_H + h] = (L > 0.f) ? (M + log2f(L)) * 0.6931471805599453f : -INFINITY;
 }
 
 hipError_t launch_attend(const AttendArgs &a, int rows, hipStream_t st) {
-  hipLaunchKernelGGL(k_attend, dim3((unsigned)a.n_split, (unsigned)rows), dim3(256), 0, st, a);
+  dim3 grid((unsigned)a.n_split, (unsigned)rows);
+  if (a.rows_per_split == 128)
+    hipLaunchKernelGGL(k_attend<128>, grid, dim3(256), 0, st, a);
+  else if (a.rows_per_split == 256)
+    hipLaunchKernelGGL(k_attend<256>, grid, dim3(256), 0, st, a);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
 hipError_t launch_merge(const MergeArgs &a, int rows, hipStream_t st) {
-  hipLaunchKernelGGL(k_merge, dim3((unsigned)rows), dim3(512), 0, st, a);
+  hipLaunchKernelGGL(k_merge, dim3(CSA2_H, (unsigned)rows), dim3(512), 0, st, a);
   return hipGetLastError();
 }
 

@@ -28,8 +28,16 @@
 
 namespace csa2 {
 
+#define SC_UNROLL 4          // 32-entry groups per wave batch (all loads issued first)
+#define SC_MAX_PAGES 80      // page ids cached per workgroup (chunk / 32 + 2)
+
+// CAND: columns are a candidate list of entry ids; PCACHE: contiguous columns
+// whose page ids are cached in LDS (pages of at least 32 entries). Both are
+// template parameters so no branch sits between a load and its use.
+template <bool CAND, bool PCACHE>
 __global__ __launch_bounds__(256) void k_index_score(ScoreArgs a) {
   __shared__ uint32_t lhist[HIST_BINS];
+  __shared__ int32_t spage[SC_MAX_PAGES];
   const int r = blockIdx.y;
   const int b = r / a.nq, t = r % a.nq;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -38,12 +46,20 @@ __global__ __launch_bounds__(256) void k_index_score(ScoreArgs a) {
   const int64_t col0 = (int64_t)blockIdx.x * a.chunk;
   const int64_t col_end = min(col0 + (int64_t)a.chunk, (int64_t)a.n_cols);
   const int64_t work_end = (a.cand || a.write_masked) ? col_end : min(col_end, (int64_t)V);
-  if (col0 >= work_end) return;  // uniform across the block
   const bool do_hist = a.hist != nullptr;
-  if (do_hist) {
-    for (int i = threadIdx.x; i < HIST_BINS; i += 256) lhist[i] = 0;
-    __syncthreads();
+  if (col0 < work_end) {  // uniform across the block
+  for (int i = threadIdx.x; i < HIST_BINS; i += 256) lhist[i] = 0;
+  // Full rows with pages of >= 32 entries: cache this chunk's page ids in LDS
+  const int shift = a.c.page_shift;
+  const int64_t pg0 = col0 >> shift;
+  if (PCACHE) {
+    const int64_t npg = ((col_end - 1) >> shift) - pg0 + 1;
+    for (int i = threadIdx.x; i < npg; i += 256) {
+      const int64_t pg = pg0 + i;
+      spage[i] = (pg < a.c.max_pages) ? a.c.block_table[(int64_t)b * a.c.max_pages + pg] : -1;
+    }
   }
+  __syncthreads();
 
   // A operands (block-diagonal indexer query), rows m = 4h + g.
   const int m = lane & 15, h = m >> 2, g = m & 3, kg = lane >> 4;
@@ -65,58 +81,98 @@ __global__ __launch_bounds__(256) void k_index_score(ScoreArgs a) {
   const float wh = a.w[(int64_t)r * CSA2_HI + hc];
   const int64_t out_base = (int64_t)r * a.n_cols;
   const int32_t *cand_row = a.cand ? a.cand + (int64_t)r * a.n_cand : nullptr;
+  const int half = (lane >> 4) & 1;
+  const int lcol = ((lane >> 5) << 4) + (lane & 15);  // column this lane loads within a group
 
-  for (int64_t e0 = col0 + wave * 32; e0 < work_end; e0 += 4 * 32) {
-    // load: lane l covers column e0 + 16*(l/32) + l%16, half (l/16)%2 of its 32 code bytes
-    const int64_t jl = e0 + ((lane >> 5) << 4) + (lane & 15);
-    const int half = (lane >> 4) & 1;
-    int32_t row_l = -1;
-    if (jl < col_end) {
-      const int32_t s = cand_row ? cand_row[jl] : (int32_t)jl;
-      if (s < V) row_l = (int32_t)cache_row(a.c, b, s, nent);
+  for (int64_t e_base = col0 + wave * 32; e_base < work_end; e_base += 4 * 32 * SC_UNROLL) {
+    // Loads are issued unconditionally from clamped, in-range addresses and
+    // batched per dependency level (candidate id -> page id -> codes), so a
+    // level's loads are all in flight together; validity is applied after.
+    int32_t row_l[SC_UNROLL];
+    int32_t sid_l[SC_UNROLL];
+#pragma unroll
+    for (int u = 0; u < SC_UNROLL; ++u) {
+      const int64_t jl = e_base + (int64_t)u * 128 + lcol;
+      const int64_t jc = min(jl, col_end - 1);
+      if constexpr (CAND) sid_l[u] = cand_row[jc];
+      else sid_l[u] = (int32_t)jl;
     }
-    v8i B = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (row_l >= 0) {
-      const v4i x = *(const v4i *)(a.c.ix_codes + (int64_t)row_l * 32 + half * 16);
-      B[0] = x[0]; B[1] = x[1]; B[2] = x[2]; B[3] = x[3];
+    int32_t page_l[SC_UNROLL];
+#pragma unroll
+    for (int u = 0; u < SC_UNROLL; ++u) {
+      const int32_t sc = min(max(sid_l[u], 0), max(nent - 1, 0));
+      if constexpr (PCACHE) {
+        page_l[u] = spage[min(max((int64_t)(sc >> shift) - pg0, (int64_t)0), (int64_t)SC_MAX_PAGES - 1)];
+      } else {
+        const int32_t pg = min(sc >> shift, a.c.max_pages - 1);
+        page_l[u] = a.c.block_table[(int64_t)b * a.c.max_pages + pg];
+      }
     }
-    const v4f z = {0.f, 0.f, 0.f, 0.f};
-    const v4f C1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A1, B, z, 4, 4, 0, 127, 0, 127);
-    const v4f C2 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A2, B, z, 4, 4, 0, 127, 0, 127);
-    const int32_t row1 = __shfl(row_l, lane & 15);
-    const int32_t row2 = __shfl(row_l, 32 + (lane & 15));
-    float t1 = 0.f, t2 = 0.f;
-    if (row1 >= 0) {
-      const uint32_t sw = *(const uint32_t *)(a.c.ix_scales + (int64_t)row1 * 4);
-      v2f lo = e4m3x2_lo_to_f32(sw), hi = e4m3x2_hi_to_f32(sw);
-      float p = C1[0] * (sq[0] * lo[0]);
-      p = fmaf(C1[1], sq[1] * lo[1], p);
-      p = fmaf(C1[2], sq[2] * hi[0], p);
-      p = fmaf(C1[3], sq[3] * hi[1], p);
-      t1 = wh * fmaxf(p, 0.f);
+#pragma unroll
+    for (int u = 0; u < SC_UNROLL; ++u) {
+      const int64_t e0 = e_base + (int64_t)u * 128;
+      const int64_t jl = e0 + lcol;
+      const int32_t sidx = sid_l[u];
+      const int32_t page = page_l[u];
+      const bool ok = e0 < work_end && jl < col_end && sidx >= 0 && sidx < V && sidx < nent &&
+                      page >= 0 && page < a.c.num_pages;
+      row_l[u] = ok ? (page << shift) + (sidx & ((1 << shift) - 1)) : -1;
     }
-    if (row2 >= 0) {
-      const uint32_t sw = *(const uint32_t *)(a.c.ix_scales + (int64_t)row2 * 4);
-      v2f lo = e4m3x2_lo_to_f32(sw), hi = e4m3x2_hi_to_f32(sw);
-      float p = C2[0] * (sq[0] * lo[0]);
-      p = fmaf(C2[1], sq[1] * lo[1], p);
-      p = fmaf(C2[2], sq[2] * hi[0], p);
-      p = fmaf(C2[3], sq[3] * hi[1], p);
-      t2 = wh * fmaxf(p, 0.f);
+    // 2. issue every data load of the batch (row 0 stands in for missing rows)
+    v4i code[SC_UNROLL];
+    uint32_t ks1[SC_UNROLL], ks2[SC_UNROLL];
+    int32_t row1[SC_UNROLL], row2[SC_UNROLL];
+#pragma unroll
+    for (int u = 0; u < SC_UNROLL; ++u) {
+      row1[u] = __shfl(row_l[u], lane & 15);
+      row2[u] = __shfl(row_l[u], 32 + (lane & 15));
+      code[u] = *(const v4i *)(a.c.ix_codes + (int64_t)max(row_l[u], 0) * 32 + half * 16);
+      ks1[u] = *(const uint32_t *)(a.c.ix_scales + (int64_t)max(row1[u], 0) * 4);
+      ks2[u] = *(const uint32_t *)(a.c.ix_scales + (int64_t)max(row2[u], 0) * 4);
     }
-    // sum the four heads (lanes n, n+16, n+32, n+48 hold heads 0..3 of column n)
-    t1 += __shfl_xor(t1, 16);
-    t1 += __shfl_xor(t1, 32);
-    t2 += __shfl_xor(t2, 16);
-    t2 += __shfl_xor(t2, 32);
-    if (lane < 32) {
-      const int64_t col = e0 + lane;  // lanes 0..15: first tile; 16..31: second tile
-      const float sc = (lane < 16) ? t1 : t2;
-      const int32_t rv = (lane < 16) ? row1 : row2;
-      if (col < col_end) {
-        const float o = (rv >= 0) ? sc : -INFINITY;
-        a.scores[out_base + col] = o;
-        if (do_hist && rv >= 0) atomicAdd(&lhist[score_key(o) >> HIST_SHIFT], 1u);
+#pragma unroll
+    for (int u = 0; u < SC_UNROLL; ++u)
+      if (row_l[u] < 0) code[u] = (v4i){0, 0, 0, 0};
+    // 3. compute
+#pragma unroll
+    for (int u = 0; u < SC_UNROLL; ++u) {
+      const int64_t e0 = e_base + (int64_t)u * 128;
+      if (e0 >= work_end) break;  // uniform within the wave
+      const v8i B = {code[u][0], code[u][1], code[u][2], code[u][3], 0, 0, 0, 0};
+      const v4f z = {0.f, 0.f, 0.f, 0.f};
+      const v4f C1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A1, B, z, 4, 4, 0, 127, 0, 127);
+      const v4f C2 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A2, B, z, 4, 4, 0, 127, 0, 127);
+      float t1, t2;
+      {
+        const v2f lo = e4m3x2_lo_to_f32(ks1[u]), hi = e4m3x2_hi_to_f32(ks1[u]);
+        float p = C1[0] * (sq[0] * lo[0]);
+        p = fmaf(C1[1], sq[1] * lo[1], p);
+        p = fmaf(C1[2], sq[2] * hi[0], p);
+        p = fmaf(C1[3], sq[3] * hi[1], p);
+        t1 = wh * fmaxf(p, 0.f);
+      }
+      {
+        const v2f lo = e4m3x2_lo_to_f32(ks2[u]), hi = e4m3x2_hi_to_f32(ks2[u]);
+        float p = C2[0] * (sq[0] * lo[0]);
+        p = fmaf(C2[1], sq[1] * lo[1], p);
+        p = fmaf(C2[2], sq[2] * hi[0], p);
+        p = fmaf(C2[3], sq[3] * hi[1], p);
+        t2 = wh * fmaxf(p, 0.f);
+      }
+      // sum the four heads (lanes n, n+16, n+32, n+48 hold heads 0..3 of column n)
+      t1 += __shfl_xor(t1, 16);
+      t1 += __shfl_xor(t1, 32);
+      t2 += __shfl_xor(t2, 16);
+      t2 += __shfl_xor(t2, 32);
+      if (lane < 32) {
+        const int64_t col = e0 + lane;  // lanes 0..15: first tile; 16..31: second tile
+        const float sc = (lane < 16) ? t1 : t2;
+        const int32_t rv = (lane < 16) ? row1[u] : row2[u];
+        if (col < col_end) {
+          const float o = (rv >= 0) ? sc : -INFINITY;
+          a.scores[out_base + col] = o;
+          if (do_hist && rv >= 0) atomicAdd(&lhist[score_key(o) >> HIST_SHIFT], 1u);
+        }
       }
     }
   }
@@ -128,12 +184,20 @@ __global__ __launch_bounds__(256) void k_index_score(ScoreArgs a) {
       if (v) atomicAdd(&gh[i], v);
     }
   }
+  }  // active workgroup
 }
 
 hipError_t launch_index_score(const ScoreArgs &a, int rows, hipStream_t st) {
   const int64_t chunks = (a.n_cols + a.chunk - 1) / a.chunk;
   dim3 grid((unsigned)chunks, (unsigned)rows);
-  hipLaunchKernelGGL(k_index_score, grid, dim3(256), 0, st, a);
+  // a chunk spans at most chunk / page + 1 pages
+  const bool pcache = a.c.page_shift >= 5 && (a.chunk >> a.c.page_shift) + 2 <= SC_MAX_PAGES;
+  if (a.cand)
+    hipLaunchKernelGGL((k_index_score<true, false>), grid, dim3(256), 0, st, a);
+  else if (pcache)
+    hipLaunchKernelGGL((k_index_score<false, true>), grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((k_index_score<false, false>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -5,25 +5,36 @@
 // 干翻大模型" section "CSA2").
 //
 // Order: score descending, entry id ascending on exact ties. Scores map to
-// order-preserving 32-bit keys. Pipeline for a row of n scores and target T:
-//  1. a 4096-bin histogram of the top 12 key bits (fused into the scoring
-//     kernel, or k_hist for standalone scores);
-//  2. k_compact (many workgroups per row): every workgroup finds the bin
-//     that holds the T-th key, appends the ids of keys in higher bins to the
-//     output and the columns of keys in that bin to a candidate list;
-//  3. k_final (one workgroup per row): radix select, 8 bits per pass in LDS,
-//     of the missing count among the candidates, then exact ties by id;
-//     optionally the top K2 of the selected set (the Full layer's top-K out
-//     of its pool); ids of a top-K are emitted in ascending order through a
-//     bitmap, pads are -1.
-// Rows short enough to sit in LDS skip steps 1-2 (direct mode).
+// order-preserving 32-bit keys. A row is cut into chunks of `chunk` columns.
+// For rows longer than fit in LDS, with one or two targets (the Full layer's
+// pool and its top-K, both over every entry):
+//  1. the scoring kernel adds each key's top 12 bits to a 4096-bin histogram
+//     (LDS per workgroup, then fire-and-forget global atomics);
+//  2. k_compact (one workgroup per chunk) finds every target's threshold bin
+//     in that histogram, counts its keys above the bin, and writes its keys
+//     in the bin, with their ids, grouped by key bits 19..12 (the "digit"),
+//     plus a table of where each digit's group starts;
+//  3. k_final (one workgroup per chunk again) reads every chunk's counts and
+//     digit tables, finds the digit that holds the boundary, loads the few
+//     keys of the row at that digit and settles the exact boundary among them
+//     (radix select on the remaining key bits, then the id for exact ties),
+//     and writes the selected ids of its own chunk in column order at the
+//     offset given by the chunks before it.
+// Plain stores only: on MI355X device-scope fences and value-returning global
+// atomics cross the non-coherent per-XCD L2s and cost microseconds each.
+// Output in column order is ascending id order whenever ids grow with the
+// column (no candidate map, or an ascending one).
+// Rows that fit in LDS use k_select_direct: one workgroup loads every key,
+// selects, and writes ids through a bitmap sort.
 #include "csa2_dev.h"
 #include "kernels.h"
+#include "block_ops.h"
 
 namespace csa2 {
 
 #define FIN_NT 512
-#define FIN_ITEMS 16384
+#define FIN_ITEMS 8192  // direct mode: items held in LDS
+#define FB_ITEMS 1024   // compact mode: keys at the boundary digit held in LDS
 #define BM_WORDS 4096
 #define BM_BITS (BM_WORDS * 32)
 
@@ -39,75 +50,6 @@ hipError_t launch_fill_u32(uint32_t *p, int64_t n, uint32_t v, hipStream_t st) {
   if (blocks > 4096) blocks = 4096;
   hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)blocks), dim3(256), 0, st, p, n, v);
   return hipGetLastError();
-}
-
-// ---- block helpers (every thread of the block must call them) ----------------
-
-// s[0..255] <- suffix sums of in[0..255]; s[256] = 0.  Uses threads < 256.
-__device__ void suffix_scan256(const uint32_t *in, uint32_t *s) {
-  const int t = threadIdx.x;
-  if (t < 256) s[t] = in[t];
-  if (t == 0) s[256] = 0;
-  __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {
-    uint32_t add = 0;
-    if (t < 256 && t + off < 256) add = s[t + off];
-    __syncthreads();
-    if (t < 256) s[t] += add;
-    __syncthreads();
-  }
-}
-
-// Exclusive prefix sum of one value per thread (blockDim.x <= 1024); returns
-// this thread's offset, *total gets the block total.
-__device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *s, uint32_t *total) {
-  const int t = threadIdx.x, n = blockDim.x;
-  s[t] = v;
-  __syncthreads();
-  for (int off = 1; off < n; off <<= 1) {
-    uint32_t add = (t >= off) ? s[t - off] : 0;
-    __syncthreads();
-    s[t] += add;
-    __syncthreads();
-  }
-  const uint32_t incl = s[t];
-  *total = s[n - 1];
-  __syncthreads();
-  return incl - v;
-}
-
-// Threshold bin of the T-th largest key from a HIST_BINS histogram held in
-// LDS (256 threads or more). Returns bin (-1 when at most T valid keys) and
-// the number of keys in higher bins.
-__device__ void find_threshold_bin(const uint32_t *h, int T, uint32_t *s_tmp, uint32_t *s_suf,
-                                   int *s_out) {
-  const int t = threadIdx.x;
-  constexpr int PER = HIST_BINS / 256;
-  if (t < 256) {
-    uint32_t sum = 0;
-    for (int i = 0; i < PER; ++i) sum += h[t * PER + i];
-    s_tmp[t] = sum;
-  }
-  __syncthreads();
-  suffix_scan256(s_tmp, s_suf);
-  if (t == 0) {
-    s_out[0] = -1;
-    s_out[1] = (int)s_suf[0];  // total valid
-  }
-  __syncthreads();
-  if (t < 256 && s_suf[0] > (uint32_t)T && s_suf[t] >= (uint32_t)T && s_suf[t + 1] < (uint32_t)T) {
-    uint32_t cum = s_suf[t + 1];
-    for (int i = PER - 1; i >= 0; --i) {
-      const uint32_t c = h[t * PER + i];
-      if (cum + c >= (uint32_t)T) {
-        s_out[0] = t * PER + i;
-        s_out[2] = (int)cum;
-        break;
-      }
-      cum += c;
-    }
-  }
-  __syncthreads();
 }
 
 __device__ __forceinline__ int32_t row_limit(const int32_t *n_entries, const int32_t *q_pos,
@@ -151,188 +93,560 @@ hipError_t launch_hist(const float *scores, int32_t n_cols, int rows, uint32_t *
   return hipGetLastError();
 }
 
-// ---- compaction against the threshold bin ----------------------------------------
-__global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
+__device__ __forceinline__ int key_digit(uint32_t k) { return (int)((k >> 12) & 0xFFu); }
+
+// ---- compaction against the threshold bins ----------------------------------------
+// NT threads, PER = chunk / NT columns per thread, NTG targets. Each lane
+// owns PER consecutive columns: thread t holds c0 + t * PER + [0, PER),
+// so (thread, item) is column order and a lane's place in an ordered output is
+// an exclusive scan of per-lane counts. VEC: rows start 16-byte aligned
+// (n_cols a multiple of 4), so the columns load as float4.
+template <int PER, int NTG, bool VEC, int NT>
+__global__ __launch_bounds__(NT) void k_compact(CompactArgs a) {
   __shared__ uint32_t lh[HIST_BINS];
-  __shared__ uint32_t s_tmp[256], s_suf[257];
-  __shared__ int s_out[4];
-  const int r = blockIdx.y;
+  __shared__ uint32_t scan[8];
+  __shared__ uint32_t dcnt[NTG][256];
+  __shared__ int s_out[4], s_thr[NTG];
+  const int r = blockIdx.y, w = blockIdx.x, tid = threadIdx.x;
   const int32_t lim = row_limit(a.n_entries, a.q_pos, a.nq, r, a.n_cols);
-  const int64_t c0 = (int64_t)blockIdx.x * a.chunk;
-  if (c0 >= lim) return;
+  const int64_t c0 = (int64_t)w * a.chunk;
+  if (c0 >= lim && w != 0) return;  // uniform; workgroup 0 always publishes the thresholds
   const int64_t c1 = min(c0 + (int64_t)a.chunk, (int64_t)lim);
-  for (int i = threadIdx.x; i < HIST_BINS; i += 256) lh[i] = a.hist[(int64_t)r * HIST_BINS + i];
-  __syncthreads();
-  find_threshold_bin(lh, a.T, s_tmp, s_suf, s_out);
-  const int thr = s_out[0];
+  const int64_t cb = c0 + (int64_t)tid * PER;
   const float *row = a.scores + (int64_t)r * a.n_cols;
   const int32_t *map = a.cand_map ? a.cand_map + (int64_t)r * a.n_cols : nullptr;
-  int32_t *out = a.out + (int64_t)r * a.out_stride;
-  int32_t *cand = a.cand_cols + (int64_t)r * a.n_cols;
-  uint32_t *ctr = a.ctr + (int64_t)r * 4;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int64_t base = c0 + wave * 64; base < c1; base += 256) {
-    const int64_t j = base + lane;
-    bool up = false, eq = false;
-    if (j < c1) {
-      const uint32_t k = score_key(row[j]);
-      if (k > KEY_NEG_INF) {
-        const int bin = (int)(k >> HIST_SHIFT);
-        up = (thr < 0) || (bin > thr);
-        eq = (thr >= 0) && (bin == thr);
+  // every load is issued unconditionally from an in-range address, so they are
+  // all in flight together (a guarded load would be followed by a wait)
+  float sv[PER];
+  int32_t idv[PER];
+  if constexpr (VEC) {
+    const int64_t vmax = a.n_cols - 4;  // last aligned float4 inside the row
+#pragma unroll
+    for (int k = 0; k < PER / 4; ++k) {
+      const v4f x = *(const v4f *)(row + min(cb + 4 * k, vmax));
+      sv[4 * k] = x[0];
+      sv[4 * k + 1] = x[1];
+      sv[4 * k + 2] = x[2];
+      sv[4 * k + 3] = x[3];
+    }
+    if (map) {
+#pragma unroll
+      for (int k = 0; k < PER / 4; ++k) {
+        const v4i x = *(const v4i *)(map + min(cb + 4 * k, vmax));
+        idv[4 * k] = x[0];
+        idv[4 * k + 1] = x[1];
+        idv[4 * k + 2] = x[2];
+        idv[4 * k + 3] = x[3];
       }
     }
-    const int p = wave_append(up, &ctr[0]);
-    if (up && p < a.out_stride) out[p] = map ? map[j] : (int32_t)j;
-    const int q = wave_append(eq, &ctr[1]);
-    if (eq && q < a.n_cols) cand[q] = (int32_t)j;
+  } else {
+    const int64_t jmax = a.n_cols - 1;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) sv[i] = row[min(cb + i, jmax)];
+    if (map) {
+#pragma unroll
+      for (int i = 0; i < PER; ++i) idv[i] = map[min(cb + i, jmax)];
+    }
   }
+  if (!map) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) idv[i] = (int32_t)(cb + i);
+  }
+  uint32_t hv[HIST_BINS / NT];
+#pragma unroll
+  for (int i = 0; i < HIST_BINS / NT; ++i) hv[i] = a.hist[(int64_t)r * HIST_BINS + tid + NT * i];
+  uint32_t key[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const uint32_t k = score_key(sv[i]);
+    key[i] = (cb + i < c1) ? k : 0u;
+  }
+#pragma unroll
+  for (int i = 0; i < HIST_BINS / NT; ++i) lh[tid + NT * i] = hv[i];
+  if (tid < 256) {
+#pragma unroll
+    for (int tg = 0; tg < NTG; ++tg) dcnt[tg][tid] = 0;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int tg = 0; tg < NTG; ++tg) {
+    hist_threshold_n<HIST_BINS, NT, true>(lh, (uint32_t)a.T[tg], scan, s_out);
+    if (tid == 0) {
+      s_thr[tg] = s_out[0];
+      if (w == 0) {
+        int32_t *info = a.info + ((int64_t)r * 2 + tg) * 4;
+        info[0] = s_out[0];
+        info[1] = s_out[1];
+        info[2] = s_out[2];
+      }
+    }
+  }
+  __syncthreads();
+  if (c0 >= lim) return;  // uniform: workgroup 0 of a row with nothing visible
+
+  // classify with integer arithmetic (bit i of cbits: candidate, at or above
+  // the threshold bin; of eqbits: in the bin); keys in the bin count towards
+  // their digit
+  uint32_t n_up[NTG], eqbits[NTG], cbits[NTG];
+#pragma unroll
+  for (int tg = 0; tg < NTG; ++tg) {
+    const int thr = s_thr[tg];
+    uint32_t eb = 0, ub = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const uint32_t valid = min(key[i] >> 23, 1u);                // key > KEY_NEG_INF
+      const int bin = (int)(key[i] >> HIST_SHIFT);
+      const uint32_t up = valid & ((uint32_t)(thr - bin) >> 31);   // bin > thr (any bin when thr < 0)
+      const uint32_t iq = (thr >= 0 && bin == thr) ? valid : 0u;
+      ub |= up << i;
+      eb |= iq << i;
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      if ((eb >> i) & 1u) atomicAdd(&dcnt[tg][key_digit(key[i])], 1u);
+    eqbits[tg] = eb;
+    cbits[tg] = eb | ub;
+    n_up[tg] = block_sum((uint32_t)__popc(ub), scan);
+  }
+#pragma unroll
+  for (int tg = 0; tg < NTG; ++tg) {
+    // thread t takes digit 255 - t: the exclusive scan in thread order is the
+    // start of each digit's group when groups run from digit 255 down
+    const int d = 255 - tid;
+    const uint32_t c = (tid < 256) ? dcnt[tg][d] : 0u;
+    uint32_t n_eq;
+    const uint32_t start = block_exclusive_scan(c, scan, &n_eq);
+    const int64_t slot = ((int64_t)r * 2 + tg) * a.max_wg + w;
+    if (tid < 256) {
+      a.suf[slot * 256 + d] = start + c;  // keys of this chunk in the bin with digit >= d
+      dcnt[tg][d] = start;                // from here on: the group's write cursor
+    }
+    if (tid == 0) a.counts[slot] = n_up[tg] | (n_eq << 16);
+  }
+#pragma unroll
+  for (int tg = 0; tg < NTG; ++tg) {
+    uint64_t *list = a.list[tg] + (int64_t)r * a.seg_stride + c0;
+    uint64_t *eq = a.eq[tg] + (int64_t)r * a.seg_stride + c0;
+    const uint32_t cbit = cbits[tg], eb = eqbits[tg];
+    // candidates in column order: this lane's first slot is the count before it
+    uint32_t tot;
+    uint32_t pos = block_exclusive_scan((uint32_t)__popc(cbit), scan, &tot);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const uint32_t c = (cbit >> i) & 1u;
+      if (c) list[pos] = ((uint64_t)key[i] << 32) | (uint32_t)idv[i];
+      pos += c;
+    }
+    // keys in the bin, grouped by digit: every slot first, then the stores
+    uint32_t p[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      p[i] = 0;
+      if ((eb >> i) & 1u) p[i] = atomicAdd(&dcnt[tg][key_digit(key[i])], 1u);
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      if ((eb >> i) & 1u) eq[p[i]] = ((uint64_t)key[i] << 32) | (uint32_t)idv[i];
+  }
+}
+
+template <int NTG, bool VEC>
+hipError_t launch_compact_n(const CompactArgs &a, dim3 grid, hipStream_t st) {
+  switch (a.chunk) {
+    case 2048: hipLaunchKernelGGL((k_compact<8, NTG, VEC, 256>), grid, dim3(256), 0, st, a); break;
+    case 4096: hipLaunchKernelGGL((k_compact<16, NTG, VEC, 256>), grid, dim3(256), 0, st, a); break;
+    case 8192: hipLaunchKernelGGL((k_compact<16, NTG, VEC, 512>), grid, dim3(512), 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_compact(const CompactArgs &a, int rows, hipStream_t st) {
   dim3 grid((unsigned)((a.n_cols + a.chunk - 1) / a.chunk), (unsigned)rows);
-  hipLaunchKernelGGL(k_compact, grid, dim3(256), 0, st, a);
-  return hipGetLastError();
+  if ((int)grid.x > a.max_wg || a.max_wg > SEL_MAX_WG) return hipErrorInvalidValue;
+  const bool vec = a.n_cols % 4 == 0 && ((uintptr_t)a.scores & 15) == 0 &&
+                   (!a.cand_map || ((uintptr_t)a.cand_map & 15) == 0);
+  if (a.ntarget == 1) return vec ? launch_compact_n<1, true>(a, grid, st) : launch_compact_n<1, false>(a, grid, st);
+  if (a.ntarget == 2) return vec ? launch_compact_n<2, true>(a, grid, st) : launch_compact_n<2, false>(a, grid, st);
+  return hipErrorInvalidValue;
 }
 
-// ---- item accessors for the block radix select ------------------------------------
-struct LdsItems {
-  const uint32_t *key;
-  const int32_t *id;
-  __device__ void get(int i, uint32_t &k, int32_t &d) const { k = key[i]; d = id[i]; }
-};
-struct CandItems {  // candidate columns of a score row
-  const float *row;
-  const int32_t *cols;
-  const int32_t *map;
-  __device__ void get(int i, uint32_t &k, int32_t &d) const {
-    const int32_t c = cols[i];
-    k = score_key(row[c]);
-    d = map ? map[c] : c;
-  }
-};
-struct IdItems {  // a list of entry ids whose score sits at column = id
-  const float *row;
-  const int32_t *ids;
-  __device__ void get(int i, uint32_t &k, int32_t &d) const {
-    d = ids[i];
-    k = score_key(row[d]);
-  }
-};
-
+// ---- exact selection at the boundary ------------------------------------------------
+template <int BITS>
 struct SelShared {
-  uint32_t hist[256];
-  uint32_t suf[257];
-  int vars[8];
+  uint32_t hist[1 << BITS];
+  uint32_t scan[16];
+  int out[4];
+  uint32_t kmin, kmax, mcount, cnt;
 };
 
-// Appends to dst the `need` best items (key desc, id asc) out of `count`.
-// known_bits: number of leading key bits shared by every item (kpref0).
-template <class Acc>
-__device__ void block_select(const Acc &acc, int count, int need, uint32_t kpref0,
-                             int known_bits, int32_t *dst, SelShared &sh) {
-  const int t = threadIdx.x, nt = blockDim.x;
-  if (t == 0) sh.vars[0] = 0;
-  __syncthreads();
-  if (need <= 0) return;
-  if (need >= count) {
-    for (int i = t; i < count; i += nt) {
-      uint32_t k;
-      int32_t d;
-      acc.get(i, k, d);
-      dst[atomicAdd((uint32_t *)&sh.vars[0], 1u)] = d;
-    }
-    __syncthreads();
-    return;
+// An item with key k and id d is selected iff (k & kmask) > kpref, or
+// (k & kmask) == kpref and d <= idthr.
+struct SelRule {
+  uint32_t kmask, kpref, idthr;
+};
+
+__device__ __forceinline__ bool rule_pass(const SelRule &R, uint32_t k, int32_t d) {
+  const uint32_t km = k & R.kmask;
+  return km > R.kpref || (km == R.kpref && (uint32_t)d <= R.idthr);
+}
+
+// The rule that keeps the `need` best (key desc, id asc) of the items whose
+// key is above KEY_NEG_INF (need >= 1). Keys are settled BITS bits at a time
+// after the leading bits every item shares; exact key ties are settled on the
+// id the same way.
+template <int BITS, int NT, class Acc>
+__device__ SelRule block_rule(const Acc &acc, int count, int need, SelShared<BITS> &sh) {
+  constexpr int NB = 1 << BITS;
+  const int t = threadIdx.x, nt = NT;
+  if (t == 0) {
+    sh.kmin = 0xFFFFFFFFu;
+    sh.kmax = 0u;
+    sh.mcount = 0;
   }
-  uint32_t kpref = kpref0;
-  uint32_t kmask = known_bits ? (0xFFFFFFFFu << (32 - known_bits)) : 0u;
-  int bits_left = 32 - known_bits;
+  __syncthreads();
+  {
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u, c = 0;
+    for (int i = t; i < count; i += nt) {
+      uint32_t k;
+      int32_t d;
+      acc.get(i, k, d);
+      if (k > KEY_NEG_INF) {
+        lo = min(lo, k);
+        hi = max(hi, k);
+        ++c;
+      }
+    }
+    if (c) {
+      atomicMin(&sh.kmin, lo);
+      atomicMax(&sh.kmax, hi);
+      atomicAdd(&sh.mcount, c);
+    }
+  }
+  __syncthreads();
+  const uint32_t diff = sh.kmin ^ sh.kmax;
+  int known = (sh.mcount == 0) ? 32 : (diff ? __clz(diff) : 32);
+  uint32_t kmask = known ? (0xFFFFFFFFu << (32 - known)) : 0u;
+  uint32_t kpref = sh.kmin & kmask;
   int left = need;
-  int eqcnt = count;
-  while (bits_left > 0) {
-    const int width = bits_left < 8 ? bits_left : 8;
-    const int shift = bits_left - width;
+  int eqcnt = (int)sh.mcount;
+  bool take_all_eq = (left >= eqcnt);
+  __syncthreads();
+  while (!take_all_eq && known < 32) {
+    const int width = (32 - known) < BITS ? (32 - known) : BITS;
+    const int shift = 32 - known - width;
     const uint32_t dmask = (1u << width) - 1u;
-    if (t < 256) sh.hist[t] = 0;
+    for (int i = t; i < NB; i += nt) sh.hist[i] = 0;
     __syncthreads();
     for (int i = t; i < count; i += nt) {
       uint32_t k;
       int32_t d;
       acc.get(i, k, d);
-      if ((k & kmask) == kpref) atomicAdd(&sh.hist[(k >> shift) & dmask], 1u);
+      if (k > KEY_NEG_INF && (k & kmask) == kpref) atomicAdd(&sh.hist[(k >> shift) & dmask], 1u);
     }
     __syncthreads();
-    suffix_scan256(sh.hist, sh.suf);
-    if (t < 256 && sh.suf[t] >= (uint32_t)left && sh.suf[t + 1] < (uint32_t)left) sh.vars[1] = t;
-    __syncthreads();
-    const int dsel = sh.vars[1];
-    left -= (int)sh.suf[dsel + 1];
-    eqcnt = (int)sh.hist[dsel];
-    kpref |= (uint32_t)dsel << shift;
-    kmask |= dmask << shift;
-    bits_left -= width;
+    hist_threshold_n<NB, NT, true>(sh.hist, (uint32_t)left, sh.scan, sh.out);
+    const int dsel = sh.out[0];
+    if (dsel < 0) {  // every item with this prefix is needed
+      take_all_eq = true;
+    } else {
+      left -= sh.out[1];
+      eqcnt = (int)sh.hist[dsel];
+      kpref |= (uint32_t)dsel << shift;
+      kmask |= dmask << shift;
+      known += width;
+      take_all_eq = (left >= eqcnt);
+    }
     __syncthreads();
   }
   uint32_t idthr = 0xFFFFFFFFu;
-  if (left < eqcnt) {  // exact key ties at the boundary: keep the lowest ids
+  if (!take_all_eq) {  // exact key ties at the boundary: keep the lowest ids
     uint32_t ipref = 0, imask = 0;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      if (t < 256) sh.hist[t] = 0;
+    int ib = 32;
+    while (ib > 0) {
+      const int width = ib < BITS ? ib : BITS;
+      const int shift = ib - width;
+      const uint32_t dmask = (1u << width) - 1u;
+      for (int i = t; i < NB; i += nt) sh.hist[i] = 0;
       __syncthreads();
       for (int i = t; i < count; i += nt) {
         uint32_t k;
         int32_t d;
         acc.get(i, k, d);
         if (k == kpref && ((uint32_t)d & imask) == ipref)
-          atomicAdd(&sh.hist[((uint32_t)d >> shift) & 255u], 1u);
+          atomicAdd(&sh.hist[((uint32_t)d >> shift) & dmask], 1u);
       }
       __syncthreads();
-      suffix_scan256(sh.hist, sh.suf);
-      // inclusive prefix(d) = suf[0] - suf[d + 1]
-      if (t < 256) {
-        const uint32_t pre = sh.suf[0] - sh.suf[t + 1];
-        const uint32_t pre_prev = sh.suf[0] - sh.suf[t];
-        if (pre >= (uint32_t)left && pre_prev < (uint32_t)left) sh.vars[1] = t;
-      }
-      __syncthreads();
-      const int dsel = sh.vars[1];
-      left -= (int)(sh.suf[0] - sh.suf[dsel]);
+      hist_threshold_n<NB, NT, false>(sh.hist, (uint32_t)left, sh.scan, sh.out);
+      const int dsel = sh.out[0] < 0 ? (int)dmask : sh.out[0];
+      if (sh.out[0] >= 0) left -= sh.out[1];
       ipref |= (uint32_t)dsel << shift;
-      imask |= 255u << shift;
+      imask |= dmask << shift;
+      ib -= width;
       __syncthreads();
     }
     idthr = ipref;
   }
-  for (int i = t; i < count; i += nt) {
-    uint32_t k;
-    int32_t d;
-    acc.get(i, k, d);
-    if (k > kpref || (k == kpref && (uint32_t)d <= idthr))
-      dst[atomicAdd((uint32_t *)&sh.vars[0], 1u)] = d;
-  }
-  __syncthreads();
+  return SelRule{kmask, kpref, idthr};
 }
 
-// Sorts n distinct non-negative ids (n <= CSA2_MAX_K) held in global memory
-// ascending, in place, then writes -1 to positions n..pad_to-1. Ids spanning
-// at most 16 bitmap windows are placed through a bitmap and a prefix sum;
-// wider ranges fall back to a bitonic sort in LDS.
-__device__ void block_sort_ids(int32_t *ids, int n, int pad_to, uint32_t *bm, int32_t *sorted,
-                               uint32_t *scan_buf, int *vars) {
+// ---- final pass: one workgroup per chunk ------------------------------------------
+// Workgroup of the flat index i in a prefix array (pre[w] <= i < pre[w+1]).
+__device__ __forceinline__ int seg_of(const uint32_t *pre, int nwg, uint32_t i) {
+  int lo = 0, hi = nwg - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (pre[mid] <= i) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Keys at the boundary digit read from the chunks' groups in global memory
+// (when there are too many for LDS).
+struct FbGlobal {
+  const uint64_t *eq;
+  int32_t chunk;
+  const uint32_t *pre, *start;
+  int nwg;
+  __device__ void get(int i, uint32_t &k, int32_t &d) const {
+    const int w = seg_of(pre, nwg, (uint32_t)i);
+    const uint64_t v = eq[(int64_t)w * chunk + start[w] + ((uint32_t)i - pre[w])];
+    k = (uint32_t)(v >> 32);
+    d = (int32_t)(uint32_t)v;
+  }
+};
+
+// The chunk's candidates (keys at or above the threshold bin, in column
+// order, from k_compact) are read two per thread per round; the first round's
+// loads are issued with the others before anything else is known.
+__global__ __launch_bounds__(FIN_NT) void k_final(FinalArgs a) {
+  __shared__ uint16_t s_suf[SEL_MAX_WG * 256];
+  __shared__ uint32_t s_cnt[SEL_MAX_WG];
+  __shared__ uint32_t s_fpre[SEL_MAX_WG + 1], s_fstart[SEL_MAX_WG];
+  __shared__ uint64_t s_fb[FB_ITEMS];
+  __shared__ uint32_t s_tot[2][256], s_pre[2][256];
+  __shared__ uint32_t s_wave[2][FIN_NT / 64];
+  __shared__ SelShared<8> sh;
+  const int w0 = blockIdx.x, r = blockIdx.y, tg = blockIdx.z, t = threadIdx.x;
+  const int lane = t & 63, wv = t >> 6;
+  const int T = a.T[tg];
+  int32_t *out = a.out[tg] + (int64_t)r * a.out_stride[tg];
+  const int32_t lim = row_limit(a.n_entries, a.q_pos, a.nq, r, a.n_cols);
+  const int nwg = (int)((lim + a.chunk - 1) / a.chunk);
+  const int32_t *info = a.info + ((int64_t)r * 2 + tg) * 4;
+  const int thr = info[0], above = info[1], total = info[2];
+  const int selT = min(T, total);
+  for (int i = selT + w0 * FIN_NT + t; i < T; i += (int)gridDim.x * FIN_NT) out[i] = -1;
+  if (w0 >= nwg) return;  // uniform: a chunk past the visible entries
+
+  // ---- loads that do not depend on each other: candidates, counts, digit tables
+  const uint64_t *list = a.list[tg] + (int64_t)r * a.seg_stride + (int64_t)w0 * a.chunk;
+  uint64_t cv[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) cv[u] = list[min(t + FIN_NT * u, a.chunk - 1)];
+  const int64_t slot0 = ((int64_t)r * 2 + tg) * a.max_wg;
+  {
+    const uint32_t cw = a.counts[slot0 + min(t, nwg - 1)];
+    if (t < nwg) s_cnt[t] = cw;
+  }
+  // digit tables of all chunks into LDS; thread t meets only digit t & 255
+  // (of chunks 2u + t / 256), so it sums that digit's column on the way
+  uint32_t sa = 0, sp = 0;
+  if (thr >= 0) {  // uniform
+    const uint32_t *suf = a.suf + slot0 * 256;
+    const int n = nwg * 256;
+    constexpr int U = 16;
+    for (int i0 = 0; i0 < n; i0 += FIN_NT * U) {
+      uint32_t v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = suf[min(i0 + t + FIN_NT * u, n - 1)];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int idx = i0 + t + FIN_NT * u;
+        if (idx < n) {
+          s_suf[idx] = (uint16_t)v[u];
+          sa += v[u];
+          sp += ((idx >> 8) < w0) ? v[u] : 0u;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  const uint32_t up_before = block_sum((t < w0) ? (s_cnt[t] & 0xFFFFu) : 0u, sh.scan);
+  const uint32_t n_list = (s_cnt[w0] & 0xFFFFu) + (s_cnt[w0] >> 16);
+
+  // ---- boundary inside the threshold bin
+  int fthr = 256;        // digits above fthr are taken whole
+  bool fine_all = true;  // every key at digit fthr is taken
+  SelRule rule{0u, 0u, 0xFFFFFFFFu};
+  uint32_t gt_before = 0, fine_before = 0;
+  if (thr >= 0) {
+    const int need = selT - above;  // keys to take from the threshold bin (>= 1)
+    s_tot[t >> 8][t & 255] = sa;
+    s_pre[t >> 8][t & 255] = sp;
+    __syncthreads();
+    if (t < 256) {
+      s_tot[0][t] += s_tot[1][t];
+      s_pre[0][t] += s_pre[1][t];
+    }
+    __syncthreads();
+    // keys with digit >= d, summed over the row, fall as d grows: the boundary
+    // digit is the largest d at which they still reach `need`
+    fthr = max((int)block_sum((t < 256 && s_tot[0][t] >= (uint32_t)need) ? 1u : 0u, sh.scan) - 1, 0);
+    const uint32_t above2 = (fthr < 255) ? s_tot[0][fthr + 1] : 0u;
+    const uint32_t need2 = (uint32_t)need - above2;
+    const uint32_t F = s_tot[0][fthr] - above2;
+    gt_before = (fthr < 255) ? s_pre[0][fthr + 1] : 0u;
+    uint32_t fc = 0;
+    if (t < nwg) {
+      const uint32_t st = (fthr < 255) ? s_suf[t * 256 + fthr + 1] : 0u;
+      s_fstart[t] = st;
+      fc = s_suf[t * 256 + fthr] - st;
+    }
+    uint32_t ftot;
+    const uint32_t fo = block_exclusive_scan(fc, sh.scan, &ftot);
+    if (t < nwg) s_fpre[t] = fo;
+    if (t == 0) s_fpre[nwg] = ftot;
+    __syncthreads();
+    const uint32_t fine_lim = s_fpre[w0];  // flat index of this chunk's first key at the digit
+    if (need2 >= F) {
+      fine_before = fine_lim;
+    } else {
+      fine_all = false;
+      const uint64_t *eq = a.eq[tg] + (int64_t)r * a.seg_stride;
+      if (F <= FB_ITEMS) {
+        for (uint32_t i0 = 0; i0 < F; i0 += FIN_NT * 2) {
+          uint64_t v[2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const uint32_t i = min(i0 + t + FIN_NT * u, F - 1);
+            const int w = seg_of(s_fpre, nwg, i);
+            v[u] = eq[(int64_t)w * a.chunk + s_fstart[w] + (i - s_fpre[w])];
+          }
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+            if (i0 + t + FIN_NT * u < F) s_fb[i0 + t + FIN_NT * u] = v[u];
+        }
+        if (t == 0) {  // replaced by the last key taken (ids are distinct)
+          sh.kmin = 0xFFFFFFFFu;
+          sh.kmax = 0u;
+        }
+        __syncthreads();
+        // rank of each key among the F at the digit (keys ahead of it: larger
+        // key, or equal key and lower id); the one ranked need2 - 1 is the last
+        // taken, and a key is taken iff it is not behind that one
+        uint32_t c = 0;
+        for (uint32_t i = t; i < F; i += FIN_NT) {
+          const uint64_t vi = s_fb[i];
+          const uint32_t ki = (uint32_t)(vi >> 32), di = (uint32_t)vi;
+          uint32_t rank = 0;
+          for (uint32_t j = 0; j < F; ++j) {
+            const uint64_t vj = s_fb[j];
+            const uint32_t kj = (uint32_t)(vj >> 32), dj = (uint32_t)vj;
+            rank += (kj > ki || (kj == ki && dj < di)) ? 1u : 0u;
+          }
+          if (rank == need2 - 1) {
+            sh.kmin = ki;
+            sh.kmax = di;
+          }
+          c += (i < fine_lim && rank < need2) ? 1u : 0u;
+        }
+        fine_before = block_sum(c, sh.scan);
+        rule = SelRule{0xFFFFFFFFu, sh.kmin, sh.kmax};
+      } else {
+        const FbGlobal acc{eq, a.chunk, s_fpre, s_fstart, nwg};
+        rule = block_rule<8, FIN_NT>(acc, (int)F, (int)need2, sh);
+        uint32_t c = 0;
+        for (uint32_t i = t; i < fine_lim; i += FIN_NT) {
+          uint32_t k;
+          int32_t d;
+          acc.get((int)i, k, d);
+          c += rule_pass(rule, k, d) ? 1u : 0u;
+        }
+        fine_before = block_sum(c, sh.scan);
+      }
+    }
+  }
+
+  // ---- emit this chunk's selected candidates in column order
+  uint32_t pos = up_before + gt_before + fine_before;
+  for (uint32_t j0 = 0; j0 < n_list; j0 += 2 * FIN_NT) {
+    if (j0 > 0) {  // uniform: more than 2 * FIN_NT candidates
+#pragma unroll
+      for (int u = 0; u < 2; ++u) cv[u] = list[min(j0 + t + FIN_NT * u, n_list - 1)];
+    }
+    bool pass[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const uint32_t k = (uint32_t)(cv[u] >> 32);
+      const int32_t d = (int32_t)(uint32_t)cv[u];
+      bool ok = j0 + t + FIN_NT * u < n_list;
+      if (thr >= 0) {
+        const int bin = (int)(k >> HIST_SHIFT);
+        const int dg = key_digit(k);
+        ok = ok && (bin > thr || dg > fthr || (dg == fthr && (fine_all || rule_pass(rule, k, d))));
+      }
+      pass[u] = ok;
+      const uint64_t m = __ballot(ok);
+      if (lane == 0) s_wave[u][wv] = (uint32_t)__popcll(m);
+    }
+    __syncthreads();
+    uint32_t tot0 = 0, before0 = 0, before1 = 0, tot1 = 0;
+    for (int v = 0; v < FIN_NT / 64; ++v) {
+      tot0 += s_wave[0][v];
+      tot1 += s_wave[1][v];
+      before0 += (v < wv) ? s_wave[0][v] : 0u;
+      before1 += (v < wv) ? s_wave[1][v] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const uint64_t m = __ballot(pass[u]);
+      if (pass[u]) {
+        const uint32_t p = pos + (u ? tot0 + before1 : before0) +
+                           __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+        if (p < (uint32_t)T) out[p] = (int32_t)(uint32_t)cv[u];
+      }
+    }
+    pos += tot0 + tot1;
+    __syncthreads();  // s_wave is rewritten next round
+  }
+}
+
+hipError_t launch_final(const FinalArgs &a, int rows, int ntarget, hipStream_t st) {
+  dim3 grid((unsigned)a.max_wg, (unsigned)rows, (unsigned)ntarget);
+  if (a.max_wg > SEL_MAX_WG || a.chunk > 65535) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_final, grid, dim3(FIN_NT), 0, st, a);
+  return hipGetLastError();
+}
+
+// ---- ascending output through a bitmap ----------------------------------------------
+// Writes the n distinct non-negative ids held in LDS (n <= FIN_ITEMS) to
+// `out` in ascending order, then -1 to positions n..pad_to-1. Ids spanning at
+// most 16 bitmap windows are placed through a bitmap and a prefix sum; wider
+// ranges fall back to a bitonic sort in LDS. bm: BM_WORDS words, sorted: at
+// least the next power of two >= n entries (both LDS, distinct from ids).
+__device__ void block_sort_out(const int32_t *ids, int n, int pad_to, int32_t *out, uint32_t *bm,
+                               int32_t *sorted, uint32_t *scan_buf, int *vars) {
   const int t = threadIdx.x, nt = blockDim.x;
   if (t == 0) {
+    vars[0] = 0;
+    vars[1] = 0x7FFFFFFF;
     vars[2] = 0;
-    vars[4] = 0x7FFFFFFF;
-    vars[5] = 0;
   }
   __syncthreads();
-  for (int i = t; i < n; i += nt) {
-    atomicMin(&vars[4], ids[i]);
-    atomicMax(&vars[5], ids[i]);
+  {
+    int lo = 0x7FFFFFFF, hi = 0;
+    for (int i = t; i < n; i += nt) {
+      lo = min(lo, ids[i]);
+      hi = max(hi, ids[i]);
+    }
+    if (n > 0) {
+      atomicMin(&vars[1], lo);
+      atomicMax(&vars[2], hi);
+    }
   }
   __syncthreads();
-  const int64_t lo0 = (int64_t)(vars[4] & ~31), hi = (int64_t)vars[5];
+  const int64_t lo0 = (int64_t)(vars[1] & ~31), hi = (int64_t)vars[2];
   if (n > 0 && hi - lo0 < 16LL * BM_BITS) {
     for (int64_t lo = lo0; lo <= hi; lo += BM_BITS) {
       for (int i = t; i < BM_WORDS; i += nt) bm[i] = 0;
@@ -347,17 +661,18 @@ __device__ void block_sort_ids(int32_t *ids, int n, int pad_to, uint32_t *bm, in
       for (int i = 0; i < per; ++i) cnt += __popc(bm[t * per + i]);
       uint32_t total;
       const uint32_t off = block_exclusive_scan(cnt, scan_buf, &total);
-      uint32_t pos = (uint32_t)vars[2] + off;
+      uint32_t pos = (uint32_t)vars[0] + off;
       for (int i = 0; i < per; ++i) {
         uint32_t word = bm[t * per + i];
         while (word) {
           const int bit = __ffs(word) - 1;
           word &= word - 1;
-          sorted[pos++] = (int32_t)(lo + (int64_t)(t * per + i) * 32 + bit);
+          if (pos < (uint32_t)n) sorted[pos] = (int32_t)(lo + (int64_t)(t * per + i) * 32 + bit);
+          ++pos;
         }
       }
       __syncthreads();
-      if (t == 0) vars[2] += (int)total;
+      if (t == 0) vars[0] += (int)total;
       __syncthreads();
     }
   } else if (n > 0) {
@@ -370,11 +685,11 @@ __device__ void block_sort_ids(int32_t *ids, int n, int pad_to, uint32_t *bm, in
         for (int i = t; i < np; i += nt) {
           const int p = i ^ j;
           if (p > i) {
-            const int32_t a = sorted[i], b = sorted[p];
+            const int32_t x = sorted[i], y = sorted[p];
             const bool up = (i & kk) == 0;
-            if ((a > b) == up) {
-              sorted[i] = b;
-              sorted[p] = a;
+            if ((x > y) == up) {
+              sorted[i] = y;
+              sorted[p] = x;
             }
           }
         }
@@ -383,105 +698,112 @@ __device__ void block_sort_ids(int32_t *ids, int n, int pad_to, uint32_t *bm, in
     }
   }
   __syncthreads();
-  for (int i = t; i < n; i += nt) ids[i] = sorted[i];
-  for (int i = n + t; i < pad_to; i += nt) ids[i] = -1;
+  for (int i = t; i < pad_to; i += nt) out[i] = (i < n) ? sorted[i] : -1;
   __syncthreads();
 }
 
-__global__ __launch_bounds__(FIN_NT) void k_final(FinalArgs a) {
+// ---- rows that fit in LDS: one workgroup per row and target -------------------------
+struct LdsItems {
+  const uint32_t *key;
+  const int32_t *id;
+  __device__ void get(int i, uint32_t &k, int32_t &d) const {
+    k = key[i];
+    d = id[i];
+  }
+};
+
+#define DIR_U 8
+
+__global__ __launch_bounds__(FIN_NT) void k_select_direct(DirectArgs a) {
   __shared__ uint32_t skey[FIN_ITEMS];
   __shared__ int32_t sid[FIN_ITEMS];
-  __shared__ SelShared sh;
-  __shared__ uint32_t scan_buf[FIN_NT];
-  __shared__ int s_misc[4];
-  const int r = blockIdx.x, t = threadIdx.x;
+  __shared__ int32_t ssel[FIN_ITEMS];
+  __shared__ SelShared<12> sh;
+  __shared__ uint32_t s_n[2];
+  const int r = blockIdx.x, tg = blockIdx.y, t = threadIdx.x;
   const float *row = a.scores + (int64_t)r * a.n_cols;
   const int32_t *map = a.cand_map ? a.cand_map + (int64_t)r * a.n_cols : nullptr;
-  int32_t *outT = a.outT + (int64_t)r * a.outT_stride;
-
-  int selT;  // final size of the T-set
-  if (a.hist) {
-    // compact mode: ids in higher bins are already in outT[0..n_above)
-    uint32_t part = 0;
-    for (int i = t; i < HIST_BINS; i += FIN_NT) part += a.hist[(int64_t)r * HIST_BINS + i];
-    uint32_t total;
-    block_exclusive_scan(part, scan_buf, &total);
-    const int n_above = (int)a.ctr[(int64_t)r * 4 + 0];
-    const int n_cand = (int)a.ctr[(int64_t)r * 4 + 1];
-    selT = (int)min((uint32_t)a.T, total);
-    const int need = selT - n_above;
-    const int32_t *cols = a.cand_cols + (int64_t)r * a.n_cols;
-    if (need > 0) {
-      if (n_cand <= FIN_ITEMS) {
-        for (int i = t; i < n_cand; i += FIN_NT) {
-          const int32_t c = cols[i];
-          skey[i] = score_key(row[c]);
-          sid[i] = map ? map[c] : c;
-        }
-        __syncthreads();
-        block_select(LdsItems{skey, sid}, n_cand, need, 0u, 0, outT + n_above, sh);
-      } else {
-        block_select(CandItems{row, cols, map}, n_cand, need, 0u, 0, outT + n_above, sh);
-      }
-    }
-  } else {
-    // direct mode: every valid column of the row is an item (row fits in LDS)
-    const int32_t lim = row_limit(a.n_entries, a.q_pos, a.nq, r, a.n_cols);
-    if (t == 0) s_misc[0] = 0;
-    __syncthreads();
-    for (int base = (t >> 6) * 64; base < lim; base += FIN_NT) {
-      const int j = base + (t & 63);
-      bool ok = false;
-      uint32_t k = 0;
-      if (j < lim) {
-        k = score_key(row[j]);
-        ok = k > KEY_NEG_INF;
-      }
-      const uint64_t m = __ballot(ok);
-      int basepos = 0;
-      const int leader = m ? (__ffsll((unsigned long long)m) - 1) : 0;
-      if (m && (t & 63) == leader) basepos = atomicAdd(&s_misc[0], __popcll(m));
-      basepos = __shfl(basepos, leader);
-      if (ok) {
-        const uint32_t lo = (uint32_t)m, hi = (uint32_t)(m >> 32);
-        const int p = basepos + __builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, 0));
-        skey[p] = k;
-        sid[p] = map ? map[j] : j;
-      }
-    }
-    __syncthreads();
-    const int n_valid = s_misc[0];
-    selT = min(a.T, n_valid);
-    block_select(LdsItems{skey, sid}, n_valid, selT, 0u, 0, outT, sh);
+  int32_t *gout = a.out[tg] + (int64_t)r * a.out_stride[tg];
+  const int T = a.T[tg];
+  const int32_t lim = min(row_limit(a.n_entries, a.q_pos, a.nq, r, a.n_cols), FIN_ITEMS);
+  if (t == 0) {
+    s_n[0] = 0;
+    s_n[1] = 0;
   }
   __syncthreads();
-
-  if (a.K2 > 0) {
-    int32_t *outK = a.outK2 + (int64_t)r * a.K2_stride;
-    const int selK = min(a.K2, selT);
-    if (selT <= FIN_ITEMS) {
-      for (int i = t; i < selT; i += FIN_NT) {
-        const int32_t d = outT[i];
-        sid[i] = d;
-        skey[i] = score_key(row[d]);
-      }
-      __syncthreads();
-      block_select(LdsItems{skey, sid}, selT, selK, 0u, 0, outK, sh);
+  for (int base = 0; base < lim; base += FIN_NT * DIR_U) {
+    float v[DIR_U];
+    int32_t d[DIR_U];
+#pragma unroll
+    for (int u = 0; u < DIR_U; ++u) v[u] = row[min(base + t + FIN_NT * u, lim - 1)];
+    if (map) {
+#pragma unroll
+      for (int u = 0; u < DIR_U; ++u) d[u] = map[min(base + t + FIN_NT * u, lim - 1)];
     } else {
-      block_select(IdItems{row, outT}, selT, selK, 0u, 0, outK, sh);
+#pragma unroll
+      for (int u = 0; u < DIR_U; ++u) d[u] = base + t + FIN_NT * u;
     }
-    __syncthreads();
-    block_sort_ids(outK, selK, a.K2, skey, sid, scan_buf, sh.vars);
-    for (int i = selT + t; i < a.T; i += FIN_NT) outT[i] = -1;
-  } else if (a.sortT) {
-    block_sort_ids(outT, selT, a.T, skey, sid, scan_buf, sh.vars);
-  } else {
-    for (int i = selT + t; i < a.T; i += FIN_NT) outT[i] = -1;
+#pragma unroll
+    for (int u = 0; u < DIR_U; ++u) {
+      const uint32_t k = score_key(v[u]);
+      const bool ok = base + t + FIN_NT * u < lim && k > KEY_NEG_INF;
+      const int p = wave_append(ok, &s_n[0]);
+      if (ok) {
+        skey[p] = k;
+        sid[p] = d[u];
+      }
+    }
   }
+  __syncthreads();
+  const int n_valid = (int)s_n[0];
+  const int selT = min(T, n_valid);
+  if (selT >= n_valid) {
+    for (int i = t; i < n_valid; i += FIN_NT) ssel[i] = sid[i];
+  } else {
+    const LdsItems acc{skey, sid};
+    const SelRule rule = block_rule<12, FIN_NT>(acc, n_valid, selT, sh);
+    for (int i0 = 0; i0 < n_valid; i0 += FIN_NT) {
+      const int i = i0 + t;
+      uint32_t k = 0;
+      int32_t d = 0;
+      if (i < n_valid) acc.get(i, k, d);
+      const bool ok = i < n_valid && rule_pass(rule, k, d);
+      const int p = wave_append(ok, &s_n[1]);
+      if (ok) ssel[p] = d;
+    }
+  }
+  __syncthreads();
+  block_sort_out(ssel, selT, T, gout, skey, sid, sh.scan, sh.out);
 }
 
-hipError_t launch_final(const FinalArgs &a, int rows, hipStream_t st) {
-  hipLaunchKernelGGL(k_final, dim3((unsigned)rows), dim3(FIN_NT), 0, st, a);
+hipError_t launch_select_direct(const DirectArgs &a, int rows, int ntarget, hipStream_t st) {
+  hipLaunchKernelGGL(k_select_direct, dim3((unsigned)rows, (unsigned)ntarget), dim3(FIN_NT), 0, st, a);
+  return hipGetLastError();
+}
+
+// ---- ascending order for ids that did not come in column order ----------------------
+// Row r of `ids` holds its selected ids first, then -1 up to T.
+__global__ __launch_bounds__(FIN_NT) void k_sort_rows(int32_t *ids, int32_t stride, int32_t T) {
+  __shared__ int32_t sin_[CSA2_MAX_K];
+  __shared__ int32_t ssorted[CSA2_MAX_K];
+  __shared__ uint32_t bm[BM_WORDS];
+  __shared__ uint32_t scan[16];
+  __shared__ int vars[4];
+  const int t = threadIdx.x;
+  int32_t *row = ids + (int64_t)blockIdx.x * stride;
+  uint32_t c = 0;
+  for (int i = t; i < T; i += FIN_NT) {
+    const int32_t v = row[i];
+    sin_[i] = v;
+    c += v >= 0 ? 1u : 0u;
+  }
+  const uint32_t n = block_sum(c, scan);
+  block_sort_out(sin_, (int)n, T, row, bm, ssorted, scan, vars);
+}
+
+hipError_t launch_sort_rows(int32_t *ids, int32_t stride, int32_t T, int rows, hipStream_t st) {
+  if (T > CSA2_MAX_K) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_sort_rows, dim3((unsigned)rows), dim3(FIN_NT), 0, st, ids, stride, T);
   return hipGetLastError();
 }
 

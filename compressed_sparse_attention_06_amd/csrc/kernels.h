@@ -23,7 +23,20 @@ struct ScoreArgs {
   int32_t chunk;         // columns per workgroup (multiple of 128)
 };
 
-// Candidate compaction against the coarse threshold bin.
+// Selection of one or two targets (T[t] largest keys of each score row) over
+// rows cut into chunks of `chunk` columns (2048, 4096 or 8192), at most
+// SEL_MAX_WG chunks per row.
+#define SEL_MAX_WG 64
+
+// k_compact, workgroup w of row r, for each target t:
+//  info[(r*2+t)*4 + 0..2]  (workgroup 0 only) threshold bin, keys above it,
+//                          keys in the row (histogram total)
+//  counts[(r*2+t)*max_wg + w] = keys above the bin | keys in the bin << 16
+//  suf[((r*2+t)*max_wg + w)*256 + d] = keys in the bin with digit >= d
+//  list[t][r*seg_stride + w*chunk + ...] (key << 32 | id) of the keys at or
+//                          above the bin, in column order
+//  eq[t][r*seg_stride + w*chunk + ...] (key << 32 | id) of the keys in the
+//                          bin, grouped by digit from 255 down
 struct CompactArgs {
   const float *scores;
   int32_t n_cols;
@@ -31,12 +44,16 @@ struct CompactArgs {
   const int32_t *n_entries;  // [batch] or null: limit columns to the visible entries
   const int32_t *q_pos;      // [rows] or null
   int32_t nq;
-  const uint32_t *hist;      // [rows][HIST_BINS]
-  int32_t T;                 // target count
-  int32_t *out;              // [rows][out_stride]
-  int32_t out_stride;
-  int32_t *cand_cols;        // [rows][n_cols]
-  uint32_t *ctr;             // [rows][4]: 0 = emitted, 1 = candidates
+  const uint32_t *hist;      // coarse [rows][HIST_BINS]
+  int32_t ntarget;
+  int32_t T[2];
+  int32_t *info;
+  uint32_t *counts;
+  uint32_t *suf;
+  uint64_t *list[2];
+  uint64_t *eq[2];
+  int64_t seg_stride;        // per row, >= max_wg * chunk
+  int32_t max_wg;
   int32_t chunk;
 };
 
@@ -47,17 +64,30 @@ struct FinalArgs {
   const int32_t *n_entries;
   const int32_t *q_pos;
   int32_t nq;
-  const uint32_t *hist;       // null: direct mode (every column is an item)
-  const int32_t *cand_cols;   // compact mode lists
-  const uint32_t *ctr;
-  int32_t T;
-  int32_t *outT;              // [rows][outT_stride]
-  int32_t outT_stride;
-  int32_t sortT;              // sort outT ascending (T <= CSA2_MAX_K)
-  int32_t K2;                 // > 0: also select top K2 of the T-set (keys scores[row][id])
-  int32_t *outK2;
-  int32_t K2_stride;
-  int32_t id_limit;           // every id is < id_limit
+  const int32_t *info;
+  const uint32_t *counts;
+  const uint32_t *suf;
+  const uint64_t *list[2];
+  const uint64_t *eq[2];
+  int64_t seg_stride;
+  int32_t max_wg;
+  int32_t chunk;
+  int32_t T[2];
+  int32_t *out[2];
+  int32_t out_stride[2];
+};
+
+// Rows of at most 8192 columns: one workgroup per row and target.
+struct DirectArgs {
+  const float *scores;
+  int32_t n_cols;
+  const int32_t *cand_map;
+  const int32_t *n_entries;
+  const int32_t *q_pos;
+  int32_t nq;
+  int32_t T[2];
+  int32_t *out[2];
+  int32_t out_stride[2];
 };
 
 struct AttendArgs {
@@ -89,7 +119,9 @@ hipError_t launch_index_score(const ScoreArgs &a, int rows, hipStream_t st);
 hipError_t launch_hist(const float *scores, int32_t n_cols, int rows, uint32_t *hist,
                        hipStream_t st);
 hipError_t launch_compact(const CompactArgs &a, int rows, hipStream_t st);
-hipError_t launch_final(const FinalArgs &a, int rows, hipStream_t st);
+hipError_t launch_final(const FinalArgs &a, int rows, int ntarget, hipStream_t st);
+hipError_t launch_select_direct(const DirectArgs &a, int rows, int ntarget, hipStream_t st);
+hipError_t launch_sort_rows(int32_t *ids, int32_t stride, int32_t T, int rows, hipStream_t st);
 hipError_t launch_attend(const AttendArgs &a, int rows, hipStream_t st);
 hipError_t launch_merge(const MergeArgs &a, int rows, hipStream_t st);
 hipError_t launch_dequant_fp4(const uint8_t *codes, const uint8_t *scales, int64_t n_rows,

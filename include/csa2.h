@@ -56,6 +56,7 @@ extern "C" {
 #define CSA2_TOKENS_PER_ENTRY 4
 #define CSA2_MAX_K 4096
 #define CSA2_MAX_POOL 65536
+#define CSA2_MAX_SELECT_COLS 524288  /* longest score row a selection takes (2M tokens) */
 
 typedef enum {
   CSA2_OK = 0,
@@ -121,6 +122,7 @@ csa2_status csa2_index_score(const csa2_cache *cache, const uint8_t *qix_codes,
  * largest finite scores, ties broken towards the lower entry id; entry id of
  * column j is j, or cand[row][j] when cand != NULL. -inf columns are never
  * selected. idx_out [rows][k]: the selected ids in ascending order, then -1.
+ * n <= CSA2_MAX_SELECT_COLS, else CSA2_EUNSUPPORTED.
  * Workspace: csa2_workspace_bytes(CSA2_REINDEX, batch, nq, n, k, 0, 0). */
 csa2_status csa2_topk(const float *scores, const int32_t *cand, int32_t batch, int32_t nq,
                       int32_t n, int32_t k, int32_t *idx_out, void *ws, size_t ws_bytes,
@@ -144,11 +146,15 @@ csa2_status csa2_sparse_attend(const csa2_cache *cache, const int32_t *idx, int3
 /* One CSA2 layer ([P1], [P2] "CSA2").
  *  FULL:    score every visible entry with this layer's indexer query; select
  *           the top `pool` entries into pool_out [batch][nq][pool] (when
- *           pool > 0; order unspecified, -1 padded) and the top k into
- *           idx_out [batch][nq][k] (ascending, -1 padded); attend.
- *  REINDEX: idx_in is the pool of the preceding Full layer [batch][nq][pool];
- *           rescore only those entries with this layer's own indexer query,
- *           select the top k into idx_out; attend.
+ *           pool > 0) and the top k into idx_out [batch][nq][k]; both hold
+ *           ascending ids followed by -1 pads; attend. The cache capacity
+ *           max_pages*page_size is at most CSA2_MAX_SELECT_COLS.
+ *  REINDEX: idx_in is the pool of the preceding Full layer [batch][nq][pool]
+ *           as pool_out wrote it (ascending ids, then -1); rescore only those
+ *           entries with this layer's own indexer query, select the top k
+ *           into idx_out; attend. With a pool that is not ascending, idx_out
+ *           holds the same selected set, in pool order rather than ascending
+ *           once pool > 4096.
  *  REUSE:   idx_in [batch][nq][k] inherited; no indexer work; attend.
  * All modes use this layer's own q and window. */
 typedef struct {

@@ -253,6 +253,9 @@ def _compare_workload(wl, res_g, res_o, what):
                 for q in range(nq):
                     assert_selection_matches(o["scores"][b, q], o["pool"][b, q], g["pool"][b, q],
                                              what=f"{what} L{li} pool b{b}")
+                    gp = g["pool"][b, q]
+                    nv = int((gp >= 0).sum())
+                    assert (gp[nv:] == -1).all() and (np.diff(gp[:nv]) > 0).all(), "pool not ascending, -1 tail"
     # attention: compare rows whose selection (and inherited selection) agrees exactly
     _log(f"{what}: {n_exact}/{n_rows} selections identical")
     for li, (g, o) in enumerate(zip(res_g, res_o)):
@@ -282,11 +285,14 @@ LAYER_CASES = [
     dict(contexts=[4 * 20000, 4 * 9000, 4 * 600], layers="FRUU", k=256, pool=2048, page_size=64, shuffle=True),
     dict(contexts=[4 * 20000, 4 * 300], layers="FRU", k=512, pool=1024, page_size=64, row_scale=True),
     dict(contexts=[4 * 40], layers="FRU", k=64, pool=128, page_size=8),  # N < K < pool
+    # Reindex over a pool long enough for the chunked selection; request 1 has
+    # fewer entries than the pool, so its pool ends in -1 pads
+    dict(contexts=[4 * 60000, 4 * 9000], layers="FRU", k=1024, pool=12000, page_size=64, shuffle=True),
 ]
 
 
 @pytest.mark.parametrize("case", LAYER_CASES, ids=["tiny_full", "full_reuse", "full_reindex_reuse",
-                                                   "rowscale", "short_ctx"])
+                                                   "rowscale", "short_ctx", "long_pool"])
 def test_layer_step_chain(case):
     _log(f"layer chain {case}")
     wl = make_small_decode(**case)
