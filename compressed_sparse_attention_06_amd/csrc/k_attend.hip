@@ -5,19 +5,22 @@
 // latent row is both key and value).
 //
 // One workgroup (4 waves) owns a (query row, split) pair: a contiguous slice of
-// the attention set, processed in tiles of 32 rows.
-//  * gather: each thread fetches 64 channels of one row (32 code bytes + 4
-//    scale bytes for an FP4 entry, 64 bytes for an E4M3 window row) and
-//    dequantises them exactly to fp16 into an LDS tile [32][512];
-//  * S = Q R^T with v_mfma_f32_16x16x32_f16 (M = the 16 heads), the 512
-//    channels split across the 4 waves and summed through LDS; after a
-//    per-head power-of-two normalisation Q is carried as an fp16 hi + lo pair
-//    (about 22 significant bits), since a single fp16 rounding of Q shifts
-//    every logit of a head coherently;
-//  * online softmax in fp32 (base-2 exponent) per head;
-//  * O += P R, each wave owning 128 output channels; the R operand of this
-//    product needs rows along K, which ds_read_b64_tr_b16 reads straight out
-//    of the row-major LDS tile.
+// the attention set, processed in tiles of 64 rows, 16 per wave.
+//  * each lane holds one quarter (128 channels) of one row of its wave's 16:
+//    the FP4 codes (64 bytes + 8 scale bytes) of a selected entry, or the E4M3
+//    bytes of a window row, all loaded before any compute;
+//  * S = Q R^T with v_mfma_f32_16x16x32_f16 (M = the 16 heads, N = the wave's
+//    16 rows, K = 512 channels in 16 steps). The channel order inside a step
+//    is free as long as both operands share it: step ks, lane quarter kq and
+//    element j stand for channel 128 kq + 8 ks + j, so each lane dequantises
+//    its own B operand straight from registers (E2M1 x E4M3 and E4M3 are exact
+//    in fp16). Q is carried as an fp16 hi + lo pair after a per-head
+//    power-of-two normalisation (about 22 significant bits);
+//  * the dequantised rows also go to an LDS tile [64][512] fp16 for O += P R,
+//    where each wave owns 128 output channels and reads R with rows along K
+//    through ds_read_b64_tr_b16;
+//  * online softmax in fp32 (base-2) across tiles; three workgroup barriers
+//    per tile.
 // The partial (unnormalised O, running max, running sum) of each split goes to
 // the workspace; k_merge combines the splits.
 #include "csa2_dev.h"
@@ -25,68 +28,334 @@
 
 namespace csa2 {
 
-#define AT_TILE 32
-#define AT_PITCH 520  // halfs per LDS row (512 + 8) to spread banks
+#define AT_ROWS 64     // rows per tile (4 waves x 16)
+#define AT_PITCH 520   // halfs per LDS row of Q and of the R tile (512 + 8)
+#define AT_PPITCH 72   // halfs per LDS row of P (64 + 8)
 
 typedef __attribute__((address_space(3))) v4s *lds_v4s_ptr;
 
-// Inputs of one row slice of one tile: an FP4 entry uses c[0..1] (32 code
-// bytes) and sc (4 scale bytes), a window row uses c[0..3] (64 E4M3 bytes).
-struct RowFetch {
-  v4i c[4];
-  uint32_t sc;
-  float rs;
-  int kind;  // 0 none, 1 entry, 2 window row
+// One lane's quarter of one tile row. FP4 entry: c[0..3] hold the 64 code
+// bytes, c[4].x and c[4].y the 8 group scales; window row: c[0..7] hold the
+// 128 E4M3 bytes.
+struct Slice {
+  v4i c[8];
+  float rs;   // window row scale (1 for entries)
+  int kind;   // 0 no row, 1 entry, 2 window row
 };
 
-// Loads of one slice are issued unconditionally from clamped, in-range
-// addresses (row 0 stands in for a missing row) and level by level (ids, then
-// block-table words, then data), so that no branch or wait separates loads
-// that could be in flight together; validity is applied afterwards.
-__device__ __forceinline__ void fetch_entry(const AttendArgs &a, int32_t id, int32_t page, bool in_range,
-                                            int32_t nent, int gpart, RowFetch &f) {
+enum { SPLIT_ENTRIES = 0, SPLIT_WINDOW = 1, SPLIT_MIXED = 2 };
+
+// Reductions over each row of 16 lanes with DPP moves (no LDS round trip):
+// swap neighbours, swap pairs, mirror within 8 lanes, mirror within 16.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f32<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_f32<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_f32<0x141>(v));  // row_half_mirror
+  v = fmaxf(v, dpp_f32<0x140>(v));  // row_mirror
+  return v;
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f32<0xB1>(v);
+  v += dpp_f32<0x4E>(v);
+  v += dpp_f32<0x141>(v);
+  v += dpp_f32<0x140>(v);
+  return v;
+}
+
+// Loads are unconditional from clamped, in-range addresses (row 0 stands in
+// for a missing row: its values are finite and get zero weight).
+__device__ __forceinline__ void load_entry(const AttendArgs &a, int32_t id, int32_t page, bool in_range,
+                                           int32_t nent, int kq, Slice &f) {
   const int sh = a.c.page_shift;
   const bool ok = in_range && id >= 0 && id < nent && (id >> sh) < a.c.max_pages && page >= 0 &&
                   page < a.c.num_pages;
   const int64_t crow = ok ? ((int64_t)page << sh) + (id & ((1 << sh) - 1)) : 0;
-  f.c[0] = *(const v4i *)(a.c.kv_codes + crow * 256 + gpart * 32);
-  f.c[1] = *(const v4i *)(a.c.kv_codes + crow * 256 + gpart * 32 + 16);
-  f.sc = *(const uint32_t *)(a.c.kv_scales + crow * 32 + gpart * 4);
+  const uint8_t *cp = a.c.kv_codes + crow * 256 + kq * 64;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) f.c[i] = *(const v4i *)(cp + 16 * i);
+  const v2f sc = *(const v2f *)(a.c.kv_scales + crow * 32 + kq * 8);
+  f.c[4][0] = __float_as_int(sc[0]);
+  f.c[4][1] = __float_as_int(sc[1]);
   f.rs = 1.f;
   f.kind = ok ? 1 : 0;
 }
 
-__device__ __forceinline__ void fetch_window(const AttendArgs &a, int b, int32_t j, bool ok, int gpart,
-                                             RowFetch &f) {
+__device__ __forceinline__ void load_window(const AttendArgs &a, int b, int32_t j, bool ok, int kq, Slice &f) {
   const int64_t wr = (int64_t)b * a.win_rows + (ok ? j : 0);
-  const uint8_t *src = a.win_codes + wr * CSA2_D + gpart * 64;
+  const uint8_t *src = a.win_codes + wr * CSA2_D + kq * 128;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) f.c[i] = *(const v4i *)(src + 16 * i);
-  f.sc = 0;
+  for (int i = 0; i < 8; ++i) f.c[i] = *(const v4i *)(src + 16 * i);
   f.rs = a.win_row_scale ? a.win_row_scale[wr] : 1.f;
   f.kind = ok ? 2 : 0;
 }
 
-template <int RPS>
-__global__ __launch_bounds__(256) void k_attend(AttendArgs a) {
-  constexpr int NT = RPS / AT_TILE;
-  __shared__ __attribute__((aligned(16))) _Float16 sQ[CSA2_H * AT_PITCH];
-  __shared__ __attribute__((aligned(16))) _Float16 sQlo[CSA2_H * AT_PITCH];
-  __shared__ __attribute__((aligned(16))) _Float16 sR[AT_TILE * AT_PITCH];
-  __shared__ float sS[4][CSA2_H][AT_TILE];
-  __shared__ __attribute__((aligned(16))) _Float16 sP[CSA2_H * 40];
-  __shared__ int sValid[AT_TILE];
-  __shared__ float sRscale[AT_TILE];
-  __shared__ float sM[CSA2_H], sL[CSA2_H], sAlpha[CSA2_H], sQexp[CSA2_H];
+// B operand of step ks: channels 128 kq + 8 ks + [0, 8) of the lane's row.
+template <int KS>
+__device__ __forceinline__ v8h entry_operand(const Slice &f) {
+  const uint32_t word = (uint32_t)f.c[KS / 4][KS % 4];
+  const uint32_t sw = (uint32_t)f.c[4][KS / 8];
+  const _Float16 s = (_Float16)e4m3_to_f32((sw >> (8 * ((KS / 2) % 4))) & 0xFFu);
+  return fp4x8_dequant(word, s);
+}
 
+template <int KS>
+__device__ __forceinline__ v8h window_operand(const Slice &f) {
+  const v4h h0 = e4m3x4_to_f16((uint32_t)f.c[(2 * KS) / 4][(2 * KS) % 4]);
+  const v4h h1 = e4m3x4_to_f16((uint32_t)f.c[(2 * KS + 1) / 4][(2 * KS + 1) % 4]);
+  const v8h r = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+  return r;
+}
+
+template <int KS, int KIND>
+__device__ __forceinline__ v8h slice_operand(const Slice &f) {
+  if constexpr (KIND == SPLIT_ENTRIES) return entry_operand<KS>(f);
+  if constexpr (KIND == SPLIT_WINDOW) return window_operand<KS>(f);
+  return (f.kind == 2) ? window_operand<KS>(f) : entry_operand<KS>(f);
+}
+
+// Q (hi, lo) is staged in LDS only until every lane holds its operands in
+// registers; the R tile then reuses that space.
+struct AttShared {
+  union {
+    struct {
+      _Float16 q[CSA2_H * AT_PITCH];
+      _Float16 qlo[CSA2_H * AT_PITCH];
+    };
+    _Float16 r[AT_ROWS * AT_PITCH];
+  };
+  _Float16 p[CSA2_H * AT_PPITCH];
+  float wmax[4][CSA2_H], wsum[4][CSA2_H];
+  float m[CSA2_H], l[CSA2_H], qexp[CSA2_H];
+};
+
+template <int NT, int KIND>
+__device__ __forceinline__ void attend_split(const AttendArgs &a, AttShared &sh, int r, int b, int split,
+                                             int32_t p0, int32_t p1, int32_t nent, int32_t w_first,
+                                             int32_t w_last) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, g = lane >> 4;  // row of the wave's 16 / channel quarter; head group in C
+  const int trow = wave * 16 + n;          // this lane's row inside a tile
+
+  // ---- every global load of the split first: Q, then the rows level by level ----
+  const int qh = tid >> 4, qpart = tid & 15;
+  float qv[32];
+  {
+    const float *src = a.q + ((int64_t)r * CSA2_H + qh) * CSA2_D + qpart * 32;
+#pragma unroll
+    for (int i = 0; i < 32; i += 4) {
+      const v4f x = *(const v4f *)(src + i);
+      qv[i] = x[0];
+      qv[i + 1] = x[1];
+      qv[i + 2] = x[2];
+      qv[i + 3] = x[3];
+    }
+  }
+  Slice sl[NT];
+  if constexpr (KIND == SPLIT_WINDOW) {
+#pragma unroll
+    for (int ti = 0; ti < NT; ++ti) {
+      const int32_t pos = p0 + ti * AT_ROWS + trow;
+      const int32_t j = w_first + (pos - a.k);
+      load_window(a, b, j, pos < p1 && j <= w_last, g, sl[ti]);
+    }
+  } else {
+    int32_t idv[NT], pgv[NT];
+    const int32_t nent_c = max(nent, 1);
+#pragma unroll
+    for (int ti = 0; ti < NT; ++ti) {
+      const int32_t pos = min(p0 + ti * AT_ROWS + trow, min(p1, a.k) - 1);
+      idv[ti] = a.idx[(int64_t)r * a.k + pos];
+    }
+#pragma unroll
+    for (int ti = 0; ti < NT; ++ti) {
+      const int32_t pg = min(min(max(idv[ti], 0), nent_c - 1) >> a.c.page_shift, a.c.max_pages - 1);
+      pgv[ti] = a.c.block_table[(int64_t)b * a.c.max_pages + pg];
+    }
+#pragma unroll
+    for (int ti = 0; ti < NT; ++ti) {
+      const int32_t pos = p0 + ti * AT_ROWS + trow;
+      if constexpr (KIND == SPLIT_ENTRIES) {
+        load_entry(a, idv[ti], pgv[ti], pos < p1, nent, g, sl[ti]);
+      } else {
+        // a lane reads an entry or a window row; both paths are issued
+        Slice e, wr;
+        load_entry(a, idv[ti], pgv[ti], pos < p1 && pos < a.k, nent, g, e);
+        const int32_t j = w_first + (pos - a.k);
+        load_window(a, b, j, pos < p1 && pos >= a.k && j <= w_last, g, wr);
+        sl[ti] = (pos < a.k) ? e : wr;
+      }
+    }
+  }
+
+  // ---- Q: per-head power-of-two normalisation, fp16 hi + lo, into LDS ----
+  {
+    const int h = qh, part = qpart;
+    const float *v = qv;
+    float mx = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) mx = fmaxf(mx, fabsf(v[i]));
+    mx = row16_max(mx);  // the 16 threads of head h are one row of lanes
+    int e = 0;
+    if (mx > 0.f) frexpf(mx, &e);  // mx = f * 2^e, f in [0.5, 1)
+    const float sc = ldexpf(1.f, -e);
+#pragma unroll
+    for (int i = 0; i < 32; i += 8) {
+      v8h hv, lv;
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const float x = v[i + jj] * sc;
+        const _Float16 hi = (_Float16)x;
+        hv[jj] = hi;
+        lv[jj] = (_Float16)(x - (float)hi);
+      }
+      *(v8h *)&sh.q[h * AT_PITCH + part * 32 + i] = hv;
+      *(v8h *)&sh.qlo[h * AT_PITCH + part * 32 + i] = lv;
+    }
+    if (part == 0) {
+      sh.qexp[h] = (float)e;
+      sh.m[h] = -INFINITY;
+      sh.l[h] = 0.f;
+    }
+  }
+  __syncthreads();
+  const float kLog2e = 1.4426950408889634f;
+  const float zscale = a.sm_scale * kLog2e;
+  float qs[4];  // logit scale of heads 4g + i
+#pragma unroll
+  for (int i = 0; i < 4; ++i) qs[i] = ldexpf(zscale, (int)sh.qexp[4 * g + i]);
+  // Q operands are the same for every tile: into registers once (A of step
+  // ks: head n, channels 128 g + 8 ks + [0, 8))
+  v8h qa[16], ql[16];
+#pragma unroll
+  for (int ks = 0; ks < 16; ++ks) {
+    qa[ks] = *(const v8h *)&sh.q[n * AT_PITCH + g * 128 + 8 * ks];
+    ql[ks] = *(const v8h *)&sh.qlo[n * AT_PITCH + g * 128 + 8 * ks];
+  }
+  __syncthreads();  // the R tile overwrites the staged Q
+
+  v4f accO[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) accO[i] = (v4f){0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int ti = 0; ti < NT; ++ti) {
+    if (p0 + ti * AT_ROWS >= p1) break;  // uniform
+    // ---- S = Q R^T for the wave's 16 rows; the same operands fill the R tile ----
+    v4f acc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = (v4f){0.f, 0.f, 0.f, 0.f};
+    _Float16 *rrow = &sh.r[trow * AT_PITCH + g * 128];
+#define CSA2_QK_STEP(KS)                                                                            \
+    {                                                                                               \
+      const v8h bop = slice_operand<KS, KIND>(sl[ti]);                                              \
+      *(v8h *)(rrow + 8 * (KS)) = bop;                                                              \
+      acc[(KS) & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[KS], bop, acc[(KS) & 1], 0, 0, 0);   \
+      acc[2 + ((KS) & 1)] =                                                                         \
+          __builtin_amdgcn_mfma_f32_16x16x32_f16(ql[KS], bop, acc[2 + ((KS) & 1)], 0, 0, 0);        \
+    }
+    CSA2_QK_STEP(0) CSA2_QK_STEP(1) CSA2_QK_STEP(2) CSA2_QK_STEP(3)
+    CSA2_QK_STEP(4) CSA2_QK_STEP(5) CSA2_QK_STEP(6) CSA2_QK_STEP(7)
+    CSA2_QK_STEP(8) CSA2_QK_STEP(9) CSA2_QK_STEP(10) CSA2_QK_STEP(11)
+    CSA2_QK_STEP(12) CSA2_QK_STEP(13) CSA2_QK_STEP(14) CSA2_QK_STEP(15)
+#undef CSA2_QK_STEP
+    // lane holds S[head 4g + i][row n]
+    const bool valid = sl[ti].kind != 0;
+    const float rs = sl[ti].rs;
+    float z[4], mx[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float sv = (acc[0][i] + acc[1][i]) + (acc[2][i] + acc[3][i]);
+      z[i] = valid ? sv * qs[i] * rs : -INFINITY;
+      mx[i] = row16_max(z[i]);  // over the wave's 16 rows
+    }
+    if (n == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sh.wmax[wave][4 * g + i] = mx[i];
+    }
+    __syncthreads();  // R tile and the waves' maxima are in LDS
+    float alpha[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = 4 * g + i;
+      const float m_old = sh.m[h];
+      const float m_new =
+          fmaxf(fmaxf(m_old, fmaxf(sh.wmax[0][h], sh.wmax[1][h])), fmaxf(sh.wmax[2][h], sh.wmax[3][h]));
+      alpha[i] = (m_new == -INFINITY) ? 1.f : ((m_old == -INFINITY) ? 0.f : exp2f(m_old - m_new));
+      const float pv = (z[i] == -INFINITY) ? 0.f : exp2f(z[i] - m_new);
+      const float ps = row16_sum(pv);
+      if (n == 0) sh.wsum[wave][h] = ps;
+      sh.p[h * AT_PPITCH + trow] = (_Float16)(pv * rs);
+      z[i] = m_new;  // kept for the state update below
+    }
+    __syncthreads();  // P and the row sums are in LDS; every read of m is done
+    if (tid < CSA2_H) {
+      const float m_old = sh.m[tid];
+      const float m_new =
+          fmaxf(fmaxf(m_old, fmaxf(sh.wmax[0][tid], sh.wmax[1][tid])), fmaxf(sh.wmax[2][tid], sh.wmax[3][tid]));
+      const float al = (m_new == -INFINITY) ? 1.f : ((m_old == -INFINITY) ? 0.f : exp2f(m_old - m_new));
+      sh.l[tid] = sh.l[tid] * al + ((sh.wsum[0][tid] + sh.wsum[1][tid]) + (sh.wsum[2][tid] + sh.wsum[3][tid]));
+      sh.m[tid] = m_new;
+    }
+    // ---- O = O * alpha + P R  (wave owns channels 128 wave .. +127) ----
+    {
+      const int c = n >> 2, rq = n & 3;
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) accO[nt][i] *= alpha[i];
+      }
+#pragma unroll
+      for (int kstep = 0; kstep < 2; ++kstep) {
+        const v8h pa = *(const v8h *)&sh.p[n * AT_PPITCH + 32 * kstep + 8 * g];
+        v4s t0v[8], t1v[8];
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) {
+          const int n0 = wave * 128 + nt * 16;
+          const _Float16 *base0 = &sh.r[(32 * kstep + 8 * g + c) * AT_PITCH + n0 + 4 * rq];
+          const _Float16 *base1 = &sh.r[(32 * kstep + 8 * g + 4 + c) * AT_PITCH + n0 + 4 * rq];
+          t0v[nt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(base0));
+          t1v[nt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(base1));
+        }
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) {
+          // whole-vector bit casts only: this clang mistranslates a bit cast of
+          // a single vector element (it reads element 0)
+          const v4h h0 = __builtin_bit_cast(v4h, t0v[nt]), h1 = __builtin_bit_cast(v4h, t1v[nt]);
+          const v8h rb = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+          accO[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, rb, accO[nt], 0, 0, 0);
+        }
+      }
+    }
+    __syncthreads();  // the R tile and P are free for the next tile
+  }
+
+  // ---- write this split's partial state ----
+  float *part = a.part + ((int64_t)r * a.n_split + split) * CSA2_H * kPartStride;
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt) {
+    const int ch = wave * 128 + nt * 16 + n;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) part[(4 * g + i) * kPartStride + ch] = accO[nt][i];
+  }
+  if (tid < CSA2_H) {
+    part[tid * kPartStride + CSA2_D] = sh.m[tid];
+    part[tid * kPartStride + CSA2_D + 1] = sh.l[tid];
+  }
+}
+
+template <int NT>
+__global__ __launch_bounds__(256) void k_attend(AttendArgs a) {
+  __shared__ __attribute__((aligned(16))) AttShared sh;
   const int r = blockIdx.y, split = blockIdx.x;
   const int b = r / a.nq;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int32_t total_pos = a.k + a.win_cap;
-  const int32_t p0 = split * RPS;
-  const int32_t p1 = min(p0 + RPS, total_pos);
+  const int32_t p0 = split * (NT * AT_ROWS);
+  const int32_t p1 = min(p0 + NT * AT_ROWS, total_pos);
   const int32_t nent = a.c.n_entries[b];
-
   // window geometry for this query
   int32_t w_first = 0, w_last = -1;
   if (a.win_codes) {
@@ -101,280 +370,51 @@ __global__ __launch_bounds__(256) void k_attend(AttendArgs a) {
       w_last = min(len, a.win_rows) - 1;
     }
   }
-
-  // ---- issue every global load of this slice first ----
-  // A split holds only selected entries, only window rows, or (when k is not
-  // a multiple of the split length) both; the first two take the batched
-  // path, the mixed split fetches each tile just before it is used.
-  const int grow = tid >> 3, gpart = tid & 7;
-  const int kind = (p1 <= a.k) ? 0 : (p0 >= a.k ? 1 : 2);  // uniform per workgroup
-  RowFetch pf[NT];
-  if (kind == 0) {
-    int32_t idv[NT], pgv[NT];
-    const int32_t nent_c = max(nent, 1);
-#pragma unroll
-    for (int ti = 0; ti < NT; ++ti) {
-      const int32_t pos = min(p0 + ti * AT_TILE + grow, p1 - 1);
-      idv[ti] = a.idx[(int64_t)r * a.k + pos];
-    }
-#pragma unroll
-    for (int ti = 0; ti < NT; ++ti) {
-      const int32_t pg = min(min(max(idv[ti], 0), nent_c - 1) >> a.c.page_shift, a.c.max_pages - 1);
-      pgv[ti] = a.c.block_table[(int64_t)b * a.c.max_pages + pg];
-    }
-#pragma unroll
-    for (int ti = 0; ti < NT; ++ti)
-      fetch_entry(a, idv[ti], pgv[ti], p0 + ti * AT_TILE + grow < p1, nent, gpart, pf[ti]);
-  } else if (kind == 1) {
-#pragma unroll
-    for (int ti = 0; ti < NT; ++ti) {
-      const int32_t pos = p0 + ti * AT_TILE + grow;
-      const int32_t j = w_first + (pos - a.k);
-      fetch_window(a, b, j, pos < p1 && j <= w_last, gpart, pf[ti]);
-    }
-  }
-
-  // ---- Q: per-head power-of-two normalisation, fp16 hi + lo, into LDS ----
-  {
-    const int h = tid >> 4, part = tid & 15;
-    const float *qh = a.q + ((int64_t)r * CSA2_H + h) * CSA2_D + part * 32;
-    float v[32];
-    float mx = 0.f;
-#pragma unroll
-    for (int i = 0; i < 32; i += 4) {
-      const v4f x = *(const v4f *)(qh + i);
-      v[i] = x[0]; v[i + 1] = x[1]; v[i + 2] = x[2]; v[i + 3] = x[3];
-    }
-#pragma unroll
-    for (int i = 0; i < 32; ++i) mx = fmaxf(mx, fabsf(v[i]));
-    mx = fmaxf(mx, __shfl_xor(mx, 1));
-    mx = fmaxf(mx, __shfl_xor(mx, 2));
-    mx = fmaxf(mx, __shfl_xor(mx, 4));
-    mx = fmaxf(mx, __shfl_xor(mx, 8));
-    int e = 0;
-    if (mx > 0.f) frexpf(mx, &e);  // mx = f * 2^e, f in [0.5, 1)
-    const float sc = ldexpf(1.f, -e);
-#pragma unroll
-    for (int i = 0; i < 32; i += 8) {
-      v8h hv, lv;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float x = v[i + j] * sc;
-        const _Float16 hi = (_Float16)x;
-        hv[j] = hi;
-        lv[j] = (_Float16)(x - (float)hi);
-      }
-      *(v8h *)&sQ[h * AT_PITCH + part * 32 + i] = hv;
-      *(v8h *)&sQlo[h * AT_PITCH + part * 32 + i] = lv;
-    }
-    if (part == 0) {
-      sQexp[h] = (float)e;
-      sM[h] = -INFINITY;
-      sL[h] = 0.f;
-    }
-  }
-  const float kLog2e = 1.4426950408889634f;
-  const float zscale = a.sm_scale * kLog2e;
-
-  v4f accO[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) accO[i] = (v4f){0.f, 0.f, 0.f, 0.f};
-
-#pragma unroll
-  for (int ti = 0; ti < NT; ++ti) {
-    if (p0 + ti * AT_TILE >= p1) break;  // uniform
-    if (kind == 2) {
-      const int32_t pos = p0 + ti * AT_TILE + grow;
-      if (pos < a.k) {
-        const int32_t id = a.idx[(int64_t)r * a.k + pos];
-        const int32_t pg = min(min(max(id, 0), max(nent, 1) - 1) >> a.c.page_shift, a.c.max_pages - 1);
-        const int32_t page = a.c.block_table[(int64_t)b * a.c.max_pages + pg];
-        fetch_entry(a, id, page, true, nent, gpart, pf[ti]);
-      } else {
-        const int32_t j = w_first + (pos - a.k);
-        fetch_window(a, b, j, pos < p1 && j <= w_last, gpart, pf[ti]);
-      }
-    }
-    // ---- dequantise this thread's slice of the tile into sR ----
-    {
-      _Float16 *dst = &sR[grow * AT_PITCH + gpart * 64];
-      if (pf[ti].kind == 1) {
-        const uint32_t sw = pf[ti].sc;
-        const uint32_t cw[8] = {(uint32_t)pf[ti].c[0][0], (uint32_t)pf[ti].c[0][1], (uint32_t)pf[ti].c[0][2],
-                                (uint32_t)pf[ti].c[0][3], (uint32_t)pf[ti].c[1][0], (uint32_t)pf[ti].c[1][1],
-                                (uint32_t)pf[ti].c[1][2], (uint32_t)pf[ti].c[1][3]};
-#pragma unroll
-        for (int gi = 0; gi < 4; ++gi) {
-          const _Float16 sg = (_Float16)e4m3_to_f32((sw >> (8 * gi)) & 0xFFu);
-          *(v8h *)(dst + gi * 16) = fp4x8_dequant(cw[2 * gi], sg);
-          *(v8h *)(dst + gi * 16 + 8) = fp4x8_dequant(cw[2 * gi + 1], sg);
-        }
-      } else if (pf[ti].kind == 2) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const v4i x = pf[ti].c[i];
-          const v4h h0 = e4m3x4_to_f16((uint32_t)x[0]), h1 = e4m3x4_to_f16((uint32_t)x[1]);
-          const v4h h2 = e4m3x4_to_f16((uint32_t)x[2]), h3 = e4m3x4_to_f16((uint32_t)x[3]);
-          const v8h lo = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
-          const v8h hi = {h2[0], h2[1], h2[2], h2[3], h3[0], h3[1], h3[2], h3[3]};
-          *(v8h *)(dst + 16 * i) = lo;
-          *(v8h *)(dst + 16 * i + 8) = hi;
-        }
-      } else {
-        const v8h zero = {0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) *(v8h *)(dst + 8 * i) = zero;
-      }
-      if (gpart == 0) {
-        sValid[grow] = pf[ti].kind != 0;
-        sRscale[grow] = pf[ti].rs;
-      }
-    }
-    __syncthreads();
-
-    // ---- S = Q R^T (partial over this wave's 128 channels) ----
-    {
-      v4f s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-      const int m = lane & 15, kq = lane >> 4;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int c0 = wave * 128 + ks * 32 + kq * 8;
-        const v8h qa = *(const v8h *)&sQ[m * AT_PITCH + c0];
-        const v8h ql = *(const v8h *)&sQlo[m * AT_PITCH + c0];
-        const v8h r0 = *(const v8h *)&sR[m * AT_PITCH + c0];
-        const v8h r1 = *(const v8h *)&sR[(16 + m) * AT_PITCH + c0];
-        s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa, r0, s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa, r1, s1, 0, 0, 0);
-        s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ql, r0, s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ql, r1, s1, 0, 0, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sS[wave][4 * kq + i][m] = s0[i];
-        sS[wave][4 * kq + i][16 + m] = s1[i];
-      }
-    }
-    __syncthreads();
-
-    // ---- online softmax (base 2): thread -> (head, two rows) ----
-    {
-      const int h = tid >> 4, rr = (tid & 15) * 2;
-      const float qs = ldexpf(zscale, (int)sQexp[h]);
-      float z[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int row = rr + u;
-        const float sv = sS[0][h][row] + sS[1][h][row] + sS[2][h][row] + sS[3][h][row];
-        z[u] = sValid[row] ? sv * qs * sRscale[row] : -INFINITY;
-      }
-      float tmax = fmaxf(z[0], z[1]);
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 1));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 2));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 4));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 8));
-      const float m_old = sM[h];
-      const float m_new = fmaxf(m_old, tmax);
-      float alpha = 1.f, p[2] = {0.f, 0.f};
-      if (m_new != -INFINITY) {
-        alpha = (m_old == -INFINITY) ? 0.f : exp2f(m_old - m_new);
-#pragma unroll
-        for (int u = 0; u < 2; ++u) p[u] = (z[u] == -INFINITY) ? 0.f : exp2f(z[u] - m_new);
-      }
-      float ps = p[0] + p[1];
-      ps += __shfl_xor(ps, 1);
-      ps += __shfl_xor(ps, 2);
-      ps += __shfl_xor(ps, 4);
-      ps += __shfl_xor(ps, 8);
-#pragma unroll
-      for (int u = 0; u < 2; ++u) sP[h * 40 + rr + u] = (_Float16)(p[u] * sRscale[rr + u]);
-      __syncthreads();  // everyone has read sM before it changes
-      if ((tid & 15) == 0) {
-        sM[h] = m_new;
-        sL[h] = sL[h] * alpha + ps;
-        sAlpha[h] = alpha;
-      }
-    }
-    __syncthreads();
-
-    // ---- O = O * alpha + P R  (wave owns channels 128*wave .. +127) ----
-    {
-      const int g = lane >> 4, j = lane & 15, c = j >> 2, rq = j & 3;
-      const v8h pa = *(const v8h *)&sP[(lane & 15) * 40 + 8 * g];
-      float al[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) al[i] = sAlpha[4 * g + i];
-#pragma unroll
-      for (int nt = 0; nt < 8; ++nt) {
-        const int n0 = wave * 128 + nt * 16;
-        const _Float16 *base0 = &sR[(8 * g + c) * AT_PITCH + n0 + 4 * rq];
-        const _Float16 *base1 = &sR[(8 * g + 4 + c) * AT_PITCH + n0 + 4 * rq];
-        const v4s t0v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(base0));
-        const v4s t1v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(base1));
-        // whole-vector bit casts only: this clang mistranslates a bit cast of
-        // a single vector element (it reads element 0)
-        const v4h h0 = __builtin_bit_cast(v4h, t0v), h1 = __builtin_bit_cast(v4h, t1v);
-        const v8h rb = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
-        v4f o = accO[nt];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o[i] *= al[i];
-        accO[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, rb, o, 0, 0, 0);
-      }
-    }
-    __syncthreads();
-  }
-
-  // ---- write this split's partial state ----
-  float *part = a.part + ((int64_t)r * a.n_split + split) * CSA2_H * kPartStride;
-  {
-    const int g = lane >> 4, j = lane & 15;
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
-      const int ch = wave * 128 + nt * 16 + j;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) part[(4 * g + i) * kPartStride + ch] = accO[nt][i];
-    }
-  }
-  if (tid < CSA2_H) {
-    part[tid * kPartStride + CSA2_D] = sM[tid];
-    part[tid * kPartStride + CSA2_D + 1] = sL[tid];
-  }
+  // a split holds only selected entries, only window rows, or both
+  if (p1 <= a.k)
+    attend_split<NT, SPLIT_ENTRIES>(a, sh, r, b, split, p0, p1, nent, w_first, w_last);
+  else if (p0 >= a.k)
+    attend_split<NT, SPLIT_WINDOW>(a, sh, r, b, split, p0, p1, nent, w_first, w_last);
+  else
+    attend_split<NT, SPLIT_MIXED>(a, sh, r, b, split, p0, p1, nent, w_first, w_last);
 }
 
 // Combine split partials of one (row, head): out = sum_s 2^(m_s - M) O_s /
-// sum_s 2^(m_s - M) l_s, one thread per channel. Splits are read in batches
-// of 16 so their loads are in flight together.
+// sum_s 2^(m_s - M) l_s, one thread per channel. Splits are read 48 at a time
+// (all loads in flight together) and folded into a running maximum.
 __global__ __launch_bounds__(512) void k_merge(MergeArgs a) {
-  constexpr int BATCH = 16;
+  constexpr int BATCH = 48;
   const int h = blockIdx.x, r = blockIdx.y, c = threadIdx.x;
   const float *base = a.part + (int64_t)r * a.n_split * CSA2_H * kPartStride + (int64_t)h * kPartStride;
   const int64_t sstride = (int64_t)CSA2_H * kPartStride;
-  const int last = a.n_split - 1;
-  float M = -INFINITY;
+  float M = -INFINITY, L = 0.f, o = 0.f;
   for (int s0 = 0; s0 < a.n_split; s0 += BATCH) {
-    float mv[BATCH];
+    const int cnt = min(BATCH, a.n_split - s0);
+    float mv[BATCH], lv[BATCH], ov[BATCH];
 #pragma unroll
-    for (int u = 0; u < BATCH; ++u) mv[u] = base[min(s0 + u, last) * sstride + CSA2_D];
-#pragma unroll
-    for (int u = 0; u < BATCH; ++u) M = fmaxf(M, mv[u]);  // repeats of the last split change nothing
-  }
-  float L = 0.f, o = 0.f;
-  if (M != -INFINITY) {
-    for (int s0 = 0; s0 < a.n_split; s0 += BATCH) {
-      float mv[BATCH], lv[BATCH], ov[BATCH];
-#pragma unroll
-      for (int u = 0; u < BATCH; ++u) {
-        const float *ps = base + min(s0 + u, last) * sstride;
-        mv[u] = ps[CSA2_D];
-        lv[u] = ps[CSA2_D + 1];
-        ov[u] = ps[c];
-      }
-#pragma unroll
-      for (int u = 0; u < BATCH; ++u) {
-        const float wgt = (s0 + u < a.n_split && mv[u] != -INFINITY) ? exp2f(mv[u] - M) : 0.f;
-        L += wgt * lv[u];
-        o += wgt * ov[u];
-      }
+    for (int u = 0; u < BATCH; ++u) {
+      const float *ps = base + (s0 + min(u, cnt - 1)) * sstride;
+      mv[u] = ps[CSA2_D];
+      lv[u] = ps[CSA2_D + 1];
+      ov[u] = ps[c];
     }
+    // repeats of the batch's last split weigh nothing: their max is -inf
+#pragma unroll
+    for (int u = 1; u < BATCH; ++u) mv[u] = (u < cnt) ? mv[u] : -INFINITY;
+    float bm = M;
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) bm = fmaxf(bm, mv[u]);
+    if (bm == -INFINITY) continue;
+    const float f = exp2f(M - bm);  // 0 while M is -inf
+    L *= f;
+    o *= f;
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
+      const float wgt = exp2f(mv[u] - bm);  // 0 for an empty split (m = -inf)
+      L += wgt * lv[u];
+      o += wgt * ov[u];
+    }
+    M = bm;
   }
   a.out[((int64_t)r * CSA2_H + h) * CSA2_D + c] = (L > 0.f) ? o / L : 0.f;
   if (c == 0)
@@ -383,10 +423,10 @@ __global__ __launch_bounds__(512) void k_merge(MergeArgs a) {
 
 hipError_t launch_attend(const AttendArgs &a, int rows, hipStream_t st) {
   dim3 grid((unsigned)a.n_split, (unsigned)rows);
-  if (a.rows_per_split == 128)
-    hipLaunchKernelGGL(k_attend<128>, grid, dim3(256), 0, st, a);
-  else if (a.rows_per_split == 256)
-    hipLaunchKernelGGL(k_attend<256>, grid, dim3(256), 0, st, a);
+  if (a.rows_per_split == 64)
+    hipLaunchKernelGGL(k_attend<1>, grid, dim3(256), 0, st, a);
+  else if (a.rows_per_split == 128)
+    hipLaunchKernelGGL(k_attend<2>, grid, dim3(256), 0, st, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

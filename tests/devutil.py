@@ -176,3 +176,60 @@ def assert_selection_matches(o_scores_row, o_ids, g_ids, id_to_col=None, what=""
     a, b = band_sets(score_of, o_ids, g_ids)
     assert a == b, f"{what}: {len(a ^ b)} ids differ outside the tie band"
     return set(int(i) for i in o_ids if i >= 0) == set(go)
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def compare_workload(wl, res_g, res_o, what):
+    """Layer-by-layer comparison of a GPU run with the oracle: selections as sets
+    (near-tie band excluded), ascending order, pools; attention on the rows whose
+    selection (and inherited selection) agrees exactly."""
+    n_exact = n_rows = 0
+    for li, (g, o) in enumerate(zip(res_g, res_o)):
+        L = wl.layers[li]
+        B, nq = L.q.shape[0], L.q.shape[1]
+        if L.mode in ("F", "R"):
+            for b in range(B):
+                for q in range(nq):
+                    if L.mode == "F":
+                        same = assert_selection_matches(o["scores"][b, q], o["idx"][b, q], g["idx"][b, q],
+                                                        what=f"{what} L{li} b{b}")
+                    else:
+                        pool_ids = res_o[last_full(wl, li)]["pool"][b, q]
+                        id_to_col = {int(e): j for j, e in enumerate(pool_ids) if e >= 0}
+                        same = assert_selection_matches(o["scores"][b, q], o["idx"][b, q], g["idx"][b, q],
+                                                        id_to_col=id_to_col, what=f"{what} L{li} b{b}")
+                    assert (np.diff(g["idx"][b, q][g["idx"][b, q] >= 0]) > 0).all(), "idx not ascending"
+                    n_rows += 1
+                    n_exact += same
+        if o.get("pool") is not None and g.get("pool") is not None:
+            for b in range(B):
+                for q in range(nq):
+                    assert_selection_matches(o["scores"][b, q], o["pool"][b, q], g["pool"][b, q],
+                                             what=f"{what} L{li} pool b{b}")
+                    gp = g["pool"][b, q]
+                    nv = int((gp >= 0).sum())
+                    assert (gp[nv:] == -1).all() and (np.diff(gp[:nv]) > 0).all(), "pool not ascending, -1 tail"
+    # attention: compare rows whose selection (and inherited selection) agrees exactly
+    _log(f"{what}: {n_exact}/{n_rows} selections identical")
+    for li, (g, o) in enumerate(zip(res_g, res_o)):
+        L = wl.layers[li]
+        idx_g = g["idx"] if g["idx"] is not None else None
+        src = li
+        while wl.layers[src].mode == "U":
+            src -= 1
+        same = (res_g[src]["idx"] == res_o[src]["idx"]).all(axis=-1)
+        if wl.layers[src].mode == "R":
+            same &= np.array([[set(res_g[last_full(wl, src)]["pool"][b, q]) == set(res_o[last_full(wl, src)]["pool"][b, q])
+                               for q in range(L.q.shape[1])] for b in range(L.q.shape[0])])
+        assert same.mean() >= 0.5, f"{what} L{li}: too few identical selections"
+        assert_attention_close(g["out"][same], g["lse"][same], o["out"][same], o["lse"][same], f"{what} L{li}")
+        del idx_g
+
+
+def last_full(wl, li):
+    while wl.layers[li].mode != "F":
+        li -= 1
+    return li

@@ -19,7 +19,7 @@ pytestmark = pytest.mark.gpu
 
 import compressed_sparse_attention_06_amd as csa2  # noqa: E402
 import oracle  # noqa: E402
-from devutil import (SCORE_RTOL, DevWorkload, assert_attention_close,  # noqa: E402
+from devutil import (SCORE_RTOL, DevWorkload, assert_attention_close, compare_workload,  # noqa: E402
                      assert_selection_matches, dev_cache, dev_window, run_gpu, t)
 from helpers import hand_window  # noqa: E402
 from synth import make_small_decode  # noqa: E402
@@ -229,56 +229,6 @@ def test_sparse_attend_prefill_windows():
 
 # ------------------------------------------------------------------ layer steps
 
-def _compare_workload(wl, res_g, res_o, what):
-    n_exact = n_rows = 0
-    for li, (g, o) in enumerate(zip(res_g, res_o)):
-        L = wl.layers[li]
-        B, nq = L.q.shape[0], L.q.shape[1]
-        if L.mode in ("F", "R"):
-            for b in range(B):
-                for q in range(nq):
-                    if L.mode == "F":
-                        same = assert_selection_matches(o["scores"][b, q], o["idx"][b, q], g["idx"][b, q],
-                                                        what=f"{what} L{li} b{b}")
-                    else:
-                        pool_ids = res_o[_last_full(wl, li)]["pool"][b, q]
-                        id_to_col = {int(e): j for j, e in enumerate(pool_ids) if e >= 0}
-                        same = assert_selection_matches(o["scores"][b, q], o["idx"][b, q], g["idx"][b, q],
-                                                        id_to_col=id_to_col, what=f"{what} L{li} b{b}")
-                    assert (np.diff(g["idx"][b, q][g["idx"][b, q] >= 0]) > 0).all(), "idx not ascending"
-                    n_rows += 1
-                    n_exact += same
-        if o.get("pool") is not None and g.get("pool") is not None:
-            for b in range(B):
-                for q in range(nq):
-                    assert_selection_matches(o["scores"][b, q], o["pool"][b, q], g["pool"][b, q],
-                                             what=f"{what} L{li} pool b{b}")
-                    gp = g["pool"][b, q]
-                    nv = int((gp >= 0).sum())
-                    assert (gp[nv:] == -1).all() and (np.diff(gp[:nv]) > 0).all(), "pool not ascending, -1 tail"
-    # attention: compare rows whose selection (and inherited selection) agrees exactly
-    _log(f"{what}: {n_exact}/{n_rows} selections identical")
-    for li, (g, o) in enumerate(zip(res_g, res_o)):
-        L = wl.layers[li]
-        idx_g = g["idx"] if g["idx"] is not None else None
-        src = li
-        while wl.layers[src].mode == "U":
-            src -= 1
-        same = (res_g[src]["idx"] == res_o[src]["idx"]).all(axis=-1)
-        if wl.layers[src].mode == "R":
-            same &= np.array([[set(res_g[_last_full(wl, src)]["pool"][b, q]) == set(res_o[_last_full(wl, src)]["pool"][b, q])
-                               for q in range(L.q.shape[1])] for b in range(L.q.shape[0])])
-        assert same.mean() >= 0.5, f"{what} L{li}: too few identical selections"
-        assert_attention_close(g["out"][same], g["lse"][same], o["out"][same], o["lse"][same], f"{what} L{li}")
-        del idx_g
-
-
-def _last_full(wl, li):
-    while wl.layers[li].mode != "F":
-        li -= 1
-    return li
-
-
 LAYER_CASES = [
     dict(contexts=[8192], layers="F", k=256, pool=0),
     dict(contexts=[4 * 3000, 4 * 1200], layers="FUU", k=128, pool=0, page_size=32, shuffle=True),
@@ -298,7 +248,7 @@ def test_layer_step_chain(case):
     wl = make_small_decode(**case)
     res_g = run_gpu(wl)
     res_o = oracle.run_workload(wl, want_scores=True)
-    _compare_workload(wl, res_g, res_o, "chain")
+    compare_workload(wl, res_g, res_o, "chain")
 
 
 def test_reuse_equals_full_given_same_indices():
@@ -367,4 +317,4 @@ def test_full_size_tiny_config():
     wl = make_decode_workload("tiny_b1_8k_full")
     res_g = run_gpu(wl)
     res_o = oracle.run_workload(wl, want_scores=True)
-    _compare_workload(wl, res_g, res_o, "tiny config")
+    compare_workload(wl, res_g, res_o, "tiny config")
