@@ -25,6 +25,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 WORKLOAD = "b8_1m_full_reindex_reuse4"
+WORKLOAD_128K = "b32_128k_full_reuse5"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_index_score_b8_1m.json")
 SCORE_SRC = os.path.join(ROOT, "compressed_sparse_attention_06_amd", "csrc", "k_score.hip")
 
@@ -45,6 +46,8 @@ def parse():
     p.add_argument("--no-graph", action="store_true")
     p.add_argument("--copy-probe-mb", type=int, default=0,
                    help="also run a plain device copy of this size (counter calibration)")
+    p.add_argument("--no-secondary", action="store_true",
+                   help="skip the 128K-context (batch 32) workload reported beside the main one")
     return p.parse_args()
 
 
@@ -85,33 +88,18 @@ def score_kernel_bytes(wl) -> int:
     return int(sum(36 * int(n) + 160 for n in c.n_entries)) * wl.nq
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(decode requests shard by batch with no exchange, see DESIGN.md)", file=sys.stderr)
-        sys.exit(2)
+def upload_chains(wl, n_copies, dev):
+    """Device copies of a workload's inputs and the chained LayerCalls of each copy."""
     import numpy as np
     import torch
 
     import compressed_sparse_attention_06_amd as csa2
-    from synth import make_decode_workload
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    dev = torch.device("cuda:0")
-    csa2.lib()
-    t0 = time.time()
-    wl = make_decode_workload(WORKLOAD)
-    log(f"workload {WORKLOAD} generated in {time.time() - t0:.1f}s; modes {wl.modes}, "
-        f"N/request {int(wl.caches[0].n_entries[0])}")
-
-    def up(a, dtype=None):
+    def up(a):
         if a is None:
             return None
-        x = torch.from_numpy(np.ascontiguousarray(a))
-        return x.to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
-    # ---- device inputs, `copies` independent copies ----
     host = dict(caches=[], layers=[])
     for c in wl.caches:
         host["caches"].append(dict(kv_codes=up(c.kv_codes), kv_scales=up(c.kv_scales),
@@ -121,17 +109,13 @@ def main():
         host["layers"].append(dict(q=up(L.q), win_codes=up(L.win.codes), win_len=up(L.win.length),
                                    qix_codes=up(L.qix_codes), qix_scales=up(L.qix_scales), w=up(L.w)))
     copies = []
-    for ci in range(args.copies):
+    for ci in range(n_copies):
         cl = (lambda x: x) if ci == 0 else (lambda x: None if x is None else x.clone())
         caches = [csa2.Cache(**{k: cl(v) for k, v in c.items()}) for c in host["caches"]]
         layers = [{k: cl(v) for k, v in L.items()} for L in host["layers"]]
         copies.append((caches, layers))
     torch.cuda.synchronize()
-    log(f"inputs on device: {args.copies} copies, "
-        f"{torch.cuda.memory_allocated() / 2**30:.2f} GiB allocated")
-
-    # shared outputs and per-layer workspaces (reused by every copy)
-    B, nq, k, pool = wl.batch, wl.nq, wl.k, wl.pool
+    k, pool = wl.k, wl.pool
 
     def build_chain(caches, layers):
         calls, last_idx, last_pool = [], None, None
@@ -153,31 +137,27 @@ def main():
             calls.append(c)
         return calls
 
-    chains = [build_chain(*cp) for cp in copies]
+    return copies, [build_chain(*cp) for cp in copies]
+
+
+def time_steps(chains, steps, warmup, use_graph):
+    """Seconds for `steps` steps, eager and (optionally) replayed from HIP graphs."""
+    import torch
 
     def run_step(i):
         for c in chains[i % len(chains)]:
             c()
 
-    # ---- eager timing ----
-    for i in range(args.warmup):
+    for i in range(warmup):
         run_step(i)
-    torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
-    ev0.record()
-    for i in range(args.steps):
+    for i in range(steps):
         run_step(i)
-    ev1.record()
     torch.cuda.synchronize()
     eager_s = time.perf_counter() - w0
-    eager_ev_ms = ev0.elapsed_time(ev1) / args.steps
-    log(f"eager: {eager_s / args.steps * 1e3:.3f} ms/step wall, {eager_ev_ms:.3f} ms/step events")
-
-    # ---- HIP graph timing (one graph per input copy) ----
     graph_s = None
-    if not args.no_graph:
+    if use_graph:
         try:
             graphs = []
             s = torch.cuda.Stream()
@@ -193,19 +173,47 @@ def main():
                     run_step(ci)
                 graphs.append(g)
             torch.cuda.synchronize()
-            for i in range(args.warmup):
+            for i in range(warmup):
                 graphs[i % len(graphs)].replay()
             torch.cuda.synchronize()
             w0 = time.perf_counter()
-            for i in range(args.steps):
+            for i in range(steps):
                 graphs[i % len(graphs)].replay()
             torch.cuda.synchronize()
             graph_s = time.perf_counter() - w0
-            log(f"graph: {graph_s / args.steps * 1e3:.3f} ms/step wall")
         except Exception as e:  # capture unsupported: report eager only
             log(f"graph capture failed: {e!r}")
             graph_s = None
+    return eager_s, graph_s
 
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(decode requests shard by batch with no exchange, see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import compressed_sparse_attention_06_amd as csa2
+    from synth import make_decode_workload
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    csa2.lib()
+    t0 = time.time()
+    wl = make_decode_workload(WORKLOAD)
+    log(f"workload {WORKLOAD} generated in {time.time() - t0:.1f}s; modes {wl.modes}, "
+        f"N/request {int(wl.caches[0].n_entries[0])}")
+    copies, chains = upload_chains(wl, args.copies, dev)
+    log(f"inputs on device: {args.copies} copies, "
+        f"{torch.cuda.memory_allocated() / 2**30:.2f} GiB allocated")
+    B, nq, k, pool = wl.batch, wl.nq, wl.k, wl.pool
+
+    eager_s, graph_s = time_steps(chains, args.steps, args.warmup, not args.no_graph)
+    log(f"eager: {eager_s / args.steps * 1e3:.3f} ms/step" +
+        ("" if graph_s is None else f"; graph: {graph_s / args.steps * 1e3:.3f} ms/step"))
     best_s = min(x for x in (eager_s, graph_s) if x is not None)
     ms_per_step = best_s / args.steps * 1e3
     qps = B * nq * args.steps / best_s
@@ -216,21 +224,22 @@ def main():
     kb = score_kernel_bytes(wl)
     scores = torch.empty(B, nq, copies[0][0][0].capacity, dtype=torch.float32, device=dev)
     hist = torch.zeros(B, nq, 4096, dtype=torch.int32, device=dev)
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.kernel_iters)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.kernel_iters)]
     for i in range(5):
         caches, layers = copies[i % len(copies)]
         csa2.index_score(caches[0], layers[0]["qix_codes"], layers[0]["qix_scales"], layers[0]["w"],
                          out=scores, hist=hist)
     torch.cuda.synchronize()
+    # back-to-back launches on the stream they run on (torch's current stream,
+    # which the binding passes to the library), bracketed by two HIP events
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
     for i in range(args.kernel_iters):
         caches, layers = copies[i % len(copies)]
-        starts[i].record()
         csa2.index_score(caches[0], layers[0]["qix_codes"], layers[0]["qix_scales"], layers[0]["w"],
                          out=scores, hist=hist)
-        ends[i].record()
+    ev1.record()
     torch.cuda.synchronize()
-    k_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(starts, ends)]))
+    k_ms = ev0.elapsed_time(ev1) / args.kernel_iters
     k_gbps = kb / (k_ms * 1e-3) / 1e9
     log(f"index_score kernel: {k_ms * 1e3:.2f} us/launch, {k_gbps:.0f} GB/s algorithmic")
 
@@ -250,8 +259,35 @@ def main():
         y = torch.empty_like(x)
         for _ in range(5):
             y.copy_(x)
+        # the same copy through an elementwise kernel (16-byte vector loads and
+        # stores per lane, like the library's kernels)
+        xf, yf = x.view(torch.float32), y.view(torch.float32)
+        xf.zero_()
+        for _ in range(5):
+            torch.mul(xf, 1.0, out=yf)
         torch.cuda.synchronize()
-        log(f"copy probe: 5 x {args.copy_probe_mb} MiB device copies")
+        log(f"copy probe: 5 x {args.copy_probe_mb} MiB device copies (blit) + 5 (elementwise)")
+
+    # ---- the 128K-context workload (batch 32, [Full, Reuse x5]) beside it ----
+    secondary = None
+    if not args.no_secondary:
+        del chains, copies
+        torch.cuda.empty_cache()
+        wl2 = make_decode_workload(WORKLOAD_128K)
+        copies2, chains2 = upload_chains(wl2, args.copies, dev)
+        e2, g2 = time_steps(chains2, args.steps, args.warmup, not args.no_graph)
+        b2 = min(x for x in (e2, g2) if x is not None)
+        sb2 = step_bytes(wl2)
+        secondary = dict(workload=WORKLOAD_128K, batch=wl2.batch, context_tokens=int(wl2.contexts[0]),
+                         layers=wl2.modes, value=round(wl2.batch * wl2.nq * args.steps / b2, 1),
+                         unit="queries/s", ms_per_step=round(b2 / args.steps * 1e3, 4),
+                         step_gbps=round(sb2 / (b2 / args.steps) / 1e9, 1),
+                         step_pct_of_peak=round(100 * sb2 / (b2 / args.steps) / 1e9 / HBM_PEAK_GBPS, 2),
+                         step_algorithmic_bytes=sb2,
+                         eager_ms_per_step=round(e2 / args.steps * 1e3, 4),
+                         graph_ms_per_step=None if g2 is None else round(g2 / args.steps * 1e3, 4))
+        log(f"128K workload: {secondary['ms_per_step']} ms/step, {secondary['value']} queries/s")
+        del chains2, copies2
 
     # ---- CPU oracle baseline (bounded sample, host cores) ----
     cpu = None
@@ -270,7 +306,7 @@ def main():
         log(f"cpu oracle: {cpu['value']} queries/s on {cores} threads")
 
     line = {
-        "metric": "CSA2 decode queries/s + achieved HBM GB/s (% of peak) at 1M ctx",
+        "metric": "CSA2 decode queries/s + achieved HBM GB/s (% of peak) at 128K and 1M ctx",
         "value": round(qps, 1),
         "unit": "queries/s",
         "n_gpus": 1,
@@ -296,6 +332,7 @@ def main():
                      "frac": round(k_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "bytes_per_launch": kb, "us_per_launch": round(k_ms * 1e3, 3)},
         "cpu_baseline": cpu,
+        "secondary": secondary,
     }
     print(json.dumps(line), flush=True)
 

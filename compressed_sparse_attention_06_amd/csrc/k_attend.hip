@@ -380,10 +380,10 @@ __global__ __launch_bounds__(256) void k_attend(AttendArgs a) {
 }
 
 // Combine split partials of one (row, head): out = sum_s 2^(m_s - M) O_s /
-// sum_s 2^(m_s - M) l_s, one thread per channel. Splits are read 48 at a time
+// sum_s 2^(m_s - M) l_s, one thread per channel. Splits are read 32 at a time
 // (all loads in flight together) and folded into a running maximum.
 __global__ __launch_bounds__(512) void k_merge(MergeArgs a) {
-  constexpr int BATCH = 48;
+  constexpr int BATCH = 32;
   const int h = blockIdx.x, r = blockIdx.y, c = threadIdx.x;
   const float *base = a.part + (int64_t)r * a.n_split * CSA2_H * kPartStride + (int64_t)h * kPartStride;
   const int64_t sstride = (int64_t)CSA2_H * kPartStride;
