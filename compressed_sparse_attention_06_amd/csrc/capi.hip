@@ -29,6 +29,7 @@ csa2_status hip_check(hipError_t e, const char *what) {
 constexpr int kFinItems = 4096;        // rows up to this length select in LDS directly
 constexpr int kScoreChunk = 2048;      // scoring columns per workgroup (contiguous entries)
 constexpr int kScoreChunkCand = 512;   // ... when gathering a candidate list
+constexpr int64_t kRowAttendMin = 512;  // query rows from which attention runs one workgroup per row
 constexpr int64_t kMaxSelectCols = CSA2_MAX_SELECT_COLS;
 static_assert(CSA2_MAX_SELECT_COLS <= SEL_MAX_WG * 8192, "the chunked selection takes SEL_MAX_WG chunks of 8192");
 
@@ -58,10 +59,13 @@ struct WsLayout {
   int64_t seg_stride = 0;
 };
 
-// Attention rows per workgroup: 64 when 64-row splits still fit the GPU in
-// one round of one workgroup per compute unit, else 128 (fewer partials to
-// merge; measured faster on the 8 x 1M-context step).
+// Attention rows per workgroup. Many query rows (a prefill chunk): 0, one
+// workgroup per row walking all its tiles, no partials and no merge. Few rows
+// (decode): split-K, 64 rows per split when 64-row splits still fit the GPU
+// in one round of one workgroup per compute unit, else 128 (fewer partials
+// to merge; measured faster on the 8 x 1M-context step).
 int rows_per_split(int64_t rows, int64_t span) {
+  if (rows >= kRowAttendMin) return 0;
   const int64_t wg64 = rows * ((span + 63) / 64);
   return wg64 <= 256 ? 64 : 128;
 }
@@ -99,10 +103,10 @@ WsLayout ws_layout(csa2_mode mode, int64_t rows, int64_t n_cols, int32_t k, int3
   }
   const int64_t span = (int64_t)k + (win_cap > 0 ? win_cap : 0);
   L.rows_per_split = rows_per_split(rows, span);
-  L.n_split = (int)((span + L.rows_per_split - 1) / L.rows_per_split);
+  L.n_split = L.rows_per_split ? (int)((span + L.rows_per_split - 1) / L.rows_per_split) : 1;
   if (L.n_split < 1) L.n_split = 1;
   L.part = off;
-  off = align256(off + (size_t)rows * L.n_split * CSA2_H * csa2::kPartStride * 4);
+  if (L.rows_per_split) off = align256(off + (size_t)rows * L.n_split * CSA2_H * csa2::kPartStride * 4);
   L.total = off;
   return L;
 }
@@ -265,6 +269,7 @@ csa2_status run_attend(const WsLayout &L, char *ws, const csa2_cache *cache, con
   a.rows_per_split = L.rows_per_split;
   a.n_split = L.n_split;
   a.part = (float *)(ws + L.part);
+  if (L.rows_per_split == 0) return hip_check(csa2::launch_attend_rows(a, rows, out, lse, st), "attend");
   csa2_status s = hip_check(csa2::launch_attend(a, rows, st), "attend");
   if (s) return s;
   csa2::MergeArgs m{};

@@ -132,6 +132,181 @@ struct AttShared {
   float m[CSA2_H], l[CSA2_H], qexp[CSA2_H];
 };
 
+// Q of one query row: per-head power-of-two normalisation, fp16 hi + lo,
+// staged in LDS and then held in registers as the A operands of every step
+// (step ks: head n, channels 128 g + 8 ks + [0, 8)). qv: this thread's 32
+// fp32 values (head tid / 16, channels 32 (tid % 16) + [0, 32)).
+struct QOps {
+  v8h qa[16], ql[16];
+  float qs[4];  // logit scale (sm_scale * log2 e * 2^e) of heads 4g + i
+};
+
+__device__ __forceinline__ void prepare_q(const AttendArgs &a, AttShared &sh, const float *qv, QOps &q) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int n = lane & 15, g = lane >> 4;
+  {
+    const int h = tid >> 4, part = tid & 15;
+    float mx = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) mx = fmaxf(mx, fabsf(qv[i]));
+    mx = row16_max(mx);  // the 16 threads of head h are one row of lanes
+    int e = 0;
+    if (mx > 0.f) frexpf(mx, &e);  // mx = f * 2^e, f in [0.5, 1)
+    const float sc = ldexpf(1.f, -e);
+#pragma unroll
+    for (int i = 0; i < 32; i += 8) {
+      v8h hv, lv;
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const float x = qv[i + jj] * sc;
+        const _Float16 hi = (_Float16)x;
+        hv[jj] = hi;
+        lv[jj] = (_Float16)(x - (float)hi);
+      }
+      *(v8h *)&sh.q[h * AT_PITCH + part * 32 + i] = hv;
+      *(v8h *)&sh.qlo[h * AT_PITCH + part * 32 + i] = lv;
+    }
+    if (part == 0) {
+      sh.qexp[h] = (float)e;
+      sh.m[h] = -INFINITY;
+      sh.l[h] = 0.f;
+    }
+  }
+  __syncthreads();
+  const float zscale = a.sm_scale * 1.4426950408889634f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) q.qs[i] = ldexpf(zscale, (int)sh.qexp[4 * g + i]);
+#pragma unroll
+  for (int ks = 0; ks < 16; ++ks) {
+    q.qa[ks] = *(const v8h *)&sh.q[n * AT_PITCH + g * 128 + 8 * ks];
+    q.ql[ks] = *(const v8h *)&sh.qlo[n * AT_PITCH + g * 128 + 8 * ks];
+  }
+  __syncthreads();  // the R tile overwrites the staged Q
+}
+
+__device__ __forceinline__ void load_q(const AttendArgs &a, int r, float *qv) {
+  const int tid = threadIdx.x;
+  const float *src = a.q + ((int64_t)r * CSA2_H + (tid >> 4)) * CSA2_D + (tid & 15) * 32;
+#pragma unroll
+  for (int i = 0; i < 32; i += 4) {
+    const v4f x = *(const v4f *)(src + i);
+    qv[i] = x[0];
+    qv[i + 1] = x[1];
+    qv[i + 2] = x[2];
+    qv[i + 3] = x[3];
+  }
+}
+
+// One 64-row tile: S = Q R^T for the wave's 16 rows (the same operands fill
+// the R tile), the online-softmax update, and O = O * alpha + P R with the
+// wave owning output channels 128 wave .. +127.
+template <int KIND>
+__device__ __forceinline__ void attend_tile(AttShared &sh, const Slice &sl, const QOps &q, v4f *accO) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int trow = wave * 16 + n;
+  v4f acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = (v4f){0.f, 0.f, 0.f, 0.f};
+  _Float16 *rrow = &sh.r[trow * AT_PITCH + g * 128];
+#define CSA2_QK_STEP(KS)                                                                              \
+  {                                                                                                   \
+    const v8h bop = slice_operand<KS, KIND>(sl);                                                      \
+    *(v8h *)(rrow + 8 * (KS)) = bop;                                                                  \
+    acc[(KS) & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(q.qa[KS], bop, acc[(KS) & 1], 0, 0, 0);     \
+    acc[2 + ((KS) & 1)] = __builtin_amdgcn_mfma_f32_16x16x32_f16(q.ql[KS], bop, acc[2 + ((KS) & 1)], 0, 0, 0); \
+  }
+  CSA2_QK_STEP(0) CSA2_QK_STEP(1) CSA2_QK_STEP(2) CSA2_QK_STEP(3)
+  CSA2_QK_STEP(4) CSA2_QK_STEP(5) CSA2_QK_STEP(6) CSA2_QK_STEP(7)
+  CSA2_QK_STEP(8) CSA2_QK_STEP(9) CSA2_QK_STEP(10) CSA2_QK_STEP(11)
+  CSA2_QK_STEP(12) CSA2_QK_STEP(13) CSA2_QK_STEP(14) CSA2_QK_STEP(15)
+#undef CSA2_QK_STEP
+  // lane holds S[head 4g + i][row n]
+  const bool valid = sl.kind != 0;
+  const float rs = sl.rs;
+  float z[4], mx[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float sv = (acc[0][i] + acc[1][i]) + (acc[2][i] + acc[3][i]);
+    z[i] = valid ? sv * q.qs[i] * rs : -INFINITY;
+    mx[i] = row16_max(z[i]);  // over the wave's 16 rows
+  }
+  if (n == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sh.wmax[wave][4 * g + i] = mx[i];
+  }
+  __syncthreads();  // R tile and the waves' maxima are in LDS
+  float alpha[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int h = 4 * g + i;
+    const float m_old = sh.m[h];
+    const float m_new =
+        fmaxf(fmaxf(m_old, fmaxf(sh.wmax[0][h], sh.wmax[1][h])), fmaxf(sh.wmax[2][h], sh.wmax[3][h]));
+    alpha[i] = (m_new == -INFINITY) ? 1.f : ((m_old == -INFINITY) ? 0.f : exp2f(m_old - m_new));
+    const float pv = (z[i] == -INFINITY) ? 0.f : exp2f(z[i] - m_new);
+    const float ps = row16_sum(pv);
+    if (n == 0) sh.wsum[wave][h] = ps;
+    sh.p[h * AT_PPITCH + trow] = (_Float16)(pv * rs);
+  }
+  __syncthreads();  // P and the row sums are in LDS; every read of m is done
+  if (tid < CSA2_H) {
+    const float m_old = sh.m[tid];
+    const float m_new =
+        fmaxf(fmaxf(m_old, fmaxf(sh.wmax[0][tid], sh.wmax[1][tid])), fmaxf(sh.wmax[2][tid], sh.wmax[3][tid]));
+    const float al = (m_new == -INFINITY) ? 1.f : ((m_old == -INFINITY) ? 0.f : exp2f(m_old - m_new));
+    sh.l[tid] = sh.l[tid] * al + ((sh.wsum[0][tid] + sh.wsum[1][tid]) + (sh.wsum[2][tid] + sh.wsum[3][tid]));
+    sh.m[tid] = m_new;
+  }
+  {
+    const int c = n >> 2, rq = n & 3;
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) accO[nt][i] *= alpha[i];
+    }
+#pragma unroll
+    for (int kstep = 0; kstep < 2; ++kstep) {
+      const v8h pa = *(const v8h *)&sh.p[n * AT_PPITCH + 32 * kstep + 8 * g];
+      v4s t0v[8], t1v[8];
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) {
+        const int n0 = wave * 128 + nt * 16;
+        const _Float16 *base0 = &sh.r[(32 * kstep + 8 * g + c) * AT_PITCH + n0 + 4 * rq];
+        const _Float16 *base1 = &sh.r[(32 * kstep + 8 * g + 4 + c) * AT_PITCH + n0 + 4 * rq];
+        t0v[nt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(base0));
+        t1v[nt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(base1));
+      }
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) {
+        // whole-vector bit casts only: this clang mistranslates a bit cast of
+        // a single vector element (it reads element 0)
+        const v4h h0 = __builtin_bit_cast(v4h, t0v[nt]), h1 = __builtin_bit_cast(v4h, t1v[nt]);
+        const v8h rb = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+        accO[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, rb, accO[nt], 0, 0, 0);
+      }
+    }
+  }
+  __syncthreads();  // the R tile and P are free for the next tile
+}
+
+// Window geometry of query row r: rows w_first..w_last of its request's window.
+__device__ __forceinline__ void window_range(const AttendArgs &a, int r, int b, int32_t &w_first,
+                                             int32_t &w_last) {
+  w_first = 0;
+  w_last = -1;
+  if (!a.win_codes) return;
+  const int32_t len = a.win_len[b];
+  if (a.win_pos0) {
+    const int32_t pq = a.q_pos ? a.q_pos[r] : 0x7FFFFFFF;
+    const int64_t rel = (int64_t)pq - a.win_pos0[b];
+    w_first = (int32_t)max((int64_t)0, rel - a.win_window + 1);
+    w_last = (int32_t)min(min((int64_t)len, (int64_t)a.win_rows) - 1, rel);
+  } else {
+    w_last = min(len, a.win_rows) - 1;
+  }
+}
+
 template <int NT, int KIND>
 __device__ __forceinline__ void attend_split(const AttendArgs &a, AttShared &sh, int r, int b, int split,
                                              int32_t p0, int32_t p1, int32_t nent, int32_t w_first,
@@ -141,19 +316,8 @@ __device__ __forceinline__ void attend_split(const AttendArgs &a, AttShared &sh,
   const int trow = wave * 16 + n;          // this lane's row inside a tile
 
   // ---- every global load of the split first: Q, then the rows level by level ----
-  const int qh = tid >> 4, qpart = tid & 15;
   float qv[32];
-  {
-    const float *src = a.q + ((int64_t)r * CSA2_H + qh) * CSA2_D + qpart * 32;
-#pragma unroll
-    for (int i = 0; i < 32; i += 4) {
-      const v4f x = *(const v4f *)(src + i);
-      qv[i] = x[0];
-      qv[i + 1] = x[1];
-      qv[i + 2] = x[2];
-      qv[i + 3] = x[3];
-    }
-  }
+  load_q(a, r, qv);
   Slice sl[NT];
   if constexpr (KIND == SPLIT_WINDOW) {
 #pragma unroll
@@ -190,147 +354,16 @@ __device__ __forceinline__ void attend_split(const AttendArgs &a, AttShared &sh,
       }
     }
   }
-
-  // ---- Q: per-head power-of-two normalisation, fp16 hi + lo, into LDS ----
-  {
-    const int h = qh, part = qpart;
-    const float *v = qv;
-    float mx = 0.f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) mx = fmaxf(mx, fabsf(v[i]));
-    mx = row16_max(mx);  // the 16 threads of head h are one row of lanes
-    int e = 0;
-    if (mx > 0.f) frexpf(mx, &e);  // mx = f * 2^e, f in [0.5, 1)
-    const float sc = ldexpf(1.f, -e);
-#pragma unroll
-    for (int i = 0; i < 32; i += 8) {
-      v8h hv, lv;
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        const float x = v[i + jj] * sc;
-        const _Float16 hi = (_Float16)x;
-        hv[jj] = hi;
-        lv[jj] = (_Float16)(x - (float)hi);
-      }
-      *(v8h *)&sh.q[h * AT_PITCH + part * 32 + i] = hv;
-      *(v8h *)&sh.qlo[h * AT_PITCH + part * 32 + i] = lv;
-    }
-    if (part == 0) {
-      sh.qexp[h] = (float)e;
-      sh.m[h] = -INFINITY;
-      sh.l[h] = 0.f;
-    }
-  }
-  __syncthreads();
-  const float kLog2e = 1.4426950408889634f;
-  const float zscale = a.sm_scale * kLog2e;
-  float qs[4];  // logit scale of heads 4g + i
-#pragma unroll
-  for (int i = 0; i < 4; ++i) qs[i] = ldexpf(zscale, (int)sh.qexp[4 * g + i]);
-  // Q operands are the same for every tile: into registers once (A of step
-  // ks: head n, channels 128 g + 8 ks + [0, 8))
-  v8h qa[16], ql[16];
-#pragma unroll
-  for (int ks = 0; ks < 16; ++ks) {
-    qa[ks] = *(const v8h *)&sh.q[n * AT_PITCH + g * 128 + 8 * ks];
-    ql[ks] = *(const v8h *)&sh.qlo[n * AT_PITCH + g * 128 + 8 * ks];
-  }
-  __syncthreads();  // the R tile overwrites the staged Q
+  QOps q;
+  prepare_q(a, sh, qv, q);
 
   v4f accO[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) accO[i] = (v4f){0.f, 0.f, 0.f, 0.f};
-
 #pragma unroll
   for (int ti = 0; ti < NT; ++ti) {
     if (p0 + ti * AT_ROWS >= p1) break;  // uniform
-    // ---- S = Q R^T for the wave's 16 rows; the same operands fill the R tile ----
-    v4f acc[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] = (v4f){0.f, 0.f, 0.f, 0.f};
-    _Float16 *rrow = &sh.r[trow * AT_PITCH + g * 128];
-#define CSA2_QK_STEP(KS)                                                                            \
-    {                                                                                               \
-      const v8h bop = slice_operand<KS, KIND>(sl[ti]);                                              \
-      *(v8h *)(rrow + 8 * (KS)) = bop;                                                              \
-      acc[(KS) & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[KS], bop, acc[(KS) & 1], 0, 0, 0);   \
-      acc[2 + ((KS) & 1)] =                                                                         \
-          __builtin_amdgcn_mfma_f32_16x16x32_f16(ql[KS], bop, acc[2 + ((KS) & 1)], 0, 0, 0);        \
-    }
-    CSA2_QK_STEP(0) CSA2_QK_STEP(1) CSA2_QK_STEP(2) CSA2_QK_STEP(3)
-    CSA2_QK_STEP(4) CSA2_QK_STEP(5) CSA2_QK_STEP(6) CSA2_QK_STEP(7)
-    CSA2_QK_STEP(8) CSA2_QK_STEP(9) CSA2_QK_STEP(10) CSA2_QK_STEP(11)
-    CSA2_QK_STEP(12) CSA2_QK_STEP(13) CSA2_QK_STEP(14) CSA2_QK_STEP(15)
-#undef CSA2_QK_STEP
-    // lane holds S[head 4g + i][row n]
-    const bool valid = sl[ti].kind != 0;
-    const float rs = sl[ti].rs;
-    float z[4], mx[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float sv = (acc[0][i] + acc[1][i]) + (acc[2][i] + acc[3][i]);
-      z[i] = valid ? sv * qs[i] * rs : -INFINITY;
-      mx[i] = row16_max(z[i]);  // over the wave's 16 rows
-    }
-    if (n == 0) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sh.wmax[wave][4 * g + i] = mx[i];
-    }
-    __syncthreads();  // R tile and the waves' maxima are in LDS
-    float alpha[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int h = 4 * g + i;
-      const float m_old = sh.m[h];
-      const float m_new =
-          fmaxf(fmaxf(m_old, fmaxf(sh.wmax[0][h], sh.wmax[1][h])), fmaxf(sh.wmax[2][h], sh.wmax[3][h]));
-      alpha[i] = (m_new == -INFINITY) ? 1.f : ((m_old == -INFINITY) ? 0.f : exp2f(m_old - m_new));
-      const float pv = (z[i] == -INFINITY) ? 0.f : exp2f(z[i] - m_new);
-      const float ps = row16_sum(pv);
-      if (n == 0) sh.wsum[wave][h] = ps;
-      sh.p[h * AT_PPITCH + trow] = (_Float16)(pv * rs);
-      z[i] = m_new;  // kept for the state update below
-    }
-    __syncthreads();  // P and the row sums are in LDS; every read of m is done
-    if (tid < CSA2_H) {
-      const float m_old = sh.m[tid];
-      const float m_new =
-          fmaxf(fmaxf(m_old, fmaxf(sh.wmax[0][tid], sh.wmax[1][tid])), fmaxf(sh.wmax[2][tid], sh.wmax[3][tid]));
-      const float al = (m_new == -INFINITY) ? 1.f : ((m_old == -INFINITY) ? 0.f : exp2f(m_old - m_new));
-      sh.l[tid] = sh.l[tid] * al + ((sh.wsum[0][tid] + sh.wsum[1][tid]) + (sh.wsum[2][tid] + sh.wsum[3][tid]));
-      sh.m[tid] = m_new;
-    }
-    // ---- O = O * alpha + P R  (wave owns channels 128 wave .. +127) ----
-    {
-      const int c = n >> 2, rq = n & 3;
-#pragma unroll
-      for (int nt = 0; nt < 8; ++nt) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) accO[nt][i] *= alpha[i];
-      }
-#pragma unroll
-      for (int kstep = 0; kstep < 2; ++kstep) {
-        const v8h pa = *(const v8h *)&sh.p[n * AT_PPITCH + 32 * kstep + 8 * g];
-        v4s t0v[8], t1v[8];
-#pragma unroll
-        for (int nt = 0; nt < 8; ++nt) {
-          const int n0 = wave * 128 + nt * 16;
-          const _Float16 *base0 = &sh.r[(32 * kstep + 8 * g + c) * AT_PITCH + n0 + 4 * rq];
-          const _Float16 *base1 = &sh.r[(32 * kstep + 8 * g + 4 + c) * AT_PITCH + n0 + 4 * rq];
-          t0v[nt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(base0));
-          t1v[nt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(base1));
-        }
-#pragma unroll
-        for (int nt = 0; nt < 8; ++nt) {
-          // whole-vector bit casts only: this clang mistranslates a bit cast of
-          // a single vector element (it reads element 0)
-          const v4h h0 = __builtin_bit_cast(v4h, t0v[nt]), h1 = __builtin_bit_cast(v4h, t1v[nt]);
-          const v8h rb = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
-          accO[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, rb, accO[nt], 0, 0, 0);
-        }
-      }
-    }
-    __syncthreads();  // the R tile and P are free for the next tile
+    attend_tile<KIND>(sh, sl[ti], q, accO);
   }
 
   // ---- write this split's partial state ----
@@ -356,20 +389,8 @@ __global__ __launch_bounds__(256) void k_attend(AttendArgs a) {
   const int32_t p0 = split * (NT * AT_ROWS);
   const int32_t p1 = min(p0 + NT * AT_ROWS, total_pos);
   const int32_t nent = a.c.n_entries[b];
-  // window geometry for this query
-  int32_t w_first = 0, w_last = -1;
-  if (a.win_codes) {
-    const int32_t len = a.win_len[b];
-    if (a.win_pos0) {
-      const int32_t pq = a.q_pos ? a.q_pos[r] : 0x7FFFFFFF;
-      const int64_t rel = (int64_t)pq - a.win_pos0[b];
-      w_first = (int32_t)max((int64_t)0, rel - a.win_window + 1);
-      w_last = (int32_t)min(min((int64_t)len, (int64_t)a.win_rows) - 1, rel);
-    } else {
-      w_first = 0;
-      w_last = min(len, a.win_rows) - 1;
-    }
-  }
+  int32_t w_first, w_last;
+  window_range(a, r, b, w_first, w_last);
   // a split holds only selected entries, only window rows, or both
   if (p1 <= a.k)
     attend_split<NT, SPLIT_ENTRIES>(a, sh, r, b, split, p0, p1, nent, w_first, w_last);
@@ -377,6 +398,120 @@ __global__ __launch_bounds__(256) void k_attend(AttendArgs a) {
     attend_split<NT, SPLIT_WINDOW>(a, sh, r, b, split, p0, p1, nent, w_first, w_last);
   else
     attend_split<NT, SPLIT_MIXED>(a, sh, r, b, split, p0, p1, nent, w_first, w_last);
+}
+
+// ---- one workgroup per query row, all tiles in turn ----------------------------------
+// For calls with many query rows (a prefill chunk): no split partials and no
+// merge; the row's tiles run in sequence, each tile's rows loaded while the
+// previous tile computes (ids three tiles ahead, block-table words two
+// ahead), and the workgroup writes out and lse itself.
+struct TileFetch {
+  int32_t id, page;
+};
+
+__device__ __forceinline__ int tile_kind(const AttendArgs &a, int t) {
+  const int32_t t0 = t * AT_ROWS;
+  return (t0 + AT_ROWS <= a.k) ? SPLIT_ENTRIES : (t0 >= a.k ? SPLIT_WINDOW : SPLIT_MIXED);
+}
+
+__device__ __forceinline__ int32_t fetch_id(const AttendArgs &a, int r, int t, int T, int trow) {
+  if (t >= T || t * AT_ROWS >= a.k) return 0;  // uniform: no entries in this tile
+  const int32_t pos = min(t * AT_ROWS + trow, a.k - 1);
+  return a.idx[(int64_t)r * a.k + pos];
+}
+
+__device__ __forceinline__ int32_t fetch_page(const AttendArgs &a, int b, int32_t id, int32_t nent) {
+  const int32_t pg = min(min(max(id, 0), max(nent, 1) - 1) >> a.c.page_shift, a.c.max_pages - 1);
+  return a.c.block_table[(int64_t)b * a.c.max_pages + pg];
+}
+
+__device__ __forceinline__ void fetch_rows(const AttendArgs &a, int b, int t, int T, int trow, int g,
+                                           const TileFetch &tf, int32_t nent, int32_t total_pos,
+                                           int32_t w_first, int32_t w_last, Slice &sl) {
+  if (t >= T) return;  // uniform
+  const int32_t pos = t * AT_ROWS + trow;
+  const int kind = tile_kind(a, t);
+  if (kind == SPLIT_ENTRIES) {
+    load_entry(a, tf.id, tf.page, pos < total_pos, nent, g, sl);
+  } else if (kind == SPLIT_WINDOW) {
+    const int32_t j = w_first + (pos - a.k);
+    load_window(a, b, j, pos < total_pos && j <= w_last, g, sl);
+  } else {
+    Slice e, wr;
+    load_entry(a, tf.id, tf.page, pos < a.k, nent, g, e);
+    const int32_t j = w_first + (pos - a.k);
+    load_window(a, b, j, pos < total_pos && pos >= a.k && j <= w_last, g, wr);
+    sl = (pos < a.k) ? e : wr;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_attend_row(AttendArgs a, float *out, float *lse) {
+  __shared__ __attribute__((aligned(16))) AttShared sh;
+  const int r = blockIdx.x;
+  const int b = r / a.nq;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int trow = wave * 16 + n;
+  const int32_t total_pos = a.k + a.win_cap;
+  const int T = (total_pos + AT_ROWS - 1) / AT_ROWS;
+  const int32_t nent = a.c.n_entries[b];
+  int32_t w_first, w_last;
+  window_range(a, r, b, w_first, w_last);
+
+  float qv[32];
+  load_q(a, r, qv);
+  // ids three tiles ahead, block-table words two ahead, rows one ahead
+  TileFetch f0, f1, f2;
+  f0.id = fetch_id(a, r, 0, T, trow);
+  f1.id = fetch_id(a, r, 1, T, trow);
+  f2.id = fetch_id(a, r, 2, T, trow);
+  f0.page = fetch_page(a, b, f0.id, nent);
+  f1.page = fetch_page(a, b, f1.id, nent);
+  Slice cur, nxt;
+  cur.kind = 0;
+  cur.rs = 1.f;
+  fetch_rows(a, b, 0, T, trow, g, f0, nent, total_pos, w_first, w_last, cur);
+  QOps q;
+  prepare_q(a, sh, qv, q);
+
+  v4f accO[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) accO[i] = (v4f){0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < T; ++t) {
+    nxt.kind = 0;
+    nxt.rs = 1.f;
+    fetch_rows(a, b, t + 1, T, trow, g, f1, nent, total_pos, w_first, w_last, nxt);
+    f2.page = fetch_page(a, b, f2.id, nent);
+    const int32_t id3 = fetch_id(a, r, t + 3, T, trow);
+    const int kind = tile_kind(a, t);  // uniform
+    if (kind == SPLIT_ENTRIES)
+      attend_tile<SPLIT_ENTRIES>(sh, cur, q, accO);
+    else if (kind == SPLIT_WINDOW)
+      attend_tile<SPLIT_WINDOW>(sh, cur, q, accO);
+    else
+      attend_tile<SPLIT_MIXED>(sh, cur, q, accO);
+    cur = nxt;
+    f1 = f2;
+    f2.id = id3;
+  }
+
+  // ---- normalise and write the row's output ----
+  float inv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float l = sh.l[4 * g + i];
+    inv[i] = (l > 0.f) ? 1.f / l : 0.f;
+  }
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt) {
+    const int ch = wave * 128 + nt * 16 + n;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[((int64_t)r * CSA2_H + 4 * g + i) * CSA2_D + ch] = accO[nt][i] * inv[i];
+  }
+  if (tid < CSA2_H) {
+    const float l = sh.l[tid];
+    lse[(int64_t)r * CSA2_H + tid] = (l > 0.f) ? (sh.m[tid] + log2f(l)) * 0.6931471805599453f : -INFINITY;
+  }
 }
 
 // Combine split partials of one (row, head): out = sum_s 2^(m_s - M) O_s /
@@ -419,6 +554,11 @@ __global__ __launch_bounds__(512) void k_merge(MergeArgs a) {
   a.out[((int64_t)r * CSA2_H + h) * CSA2_D + c] = (L > 0.f) ? o / L : 0.f;
   if (c == 0)
     a.lse[(int64_t)r * CSA2_H + h] = (L > 0.f) ? (M + log2f(L)) * 0.6931471805599453f : -INFINITY;
+}
+
+hipError_t launch_attend_rows(const AttendArgs &a, int rows, float *out, float *lse, hipStream_t st) {
+  hipLaunchKernelGGL(k_attend_row, dim3((unsigned)rows), dim3(256), 0, st, a, out, lse);
+  return hipGetLastError();
 }
 
 hipError_t launch_attend(const AttendArgs &a, int rows, hipStream_t st) {

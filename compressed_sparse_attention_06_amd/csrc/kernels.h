@@ -103,7 +103,7 @@ struct AttendArgs {
   const int32_t *q_pos;
   int32_t nq;
   float sm_scale;
-  int32_t rows_per_split;
+  int32_t rows_per_split;  // 0: one workgroup per query row, no partials
   int32_t n_split;
   float *part;   // [rows][n_split][16][512 + 2]
 };
@@ -123,6 +123,7 @@ hipError_t launch_final(const FinalArgs &a, int rows, int ntarget, hipStream_t s
 hipError_t launch_select_direct(const DirectArgs &a, int rows, int ntarget, hipStream_t st);
 hipError_t launch_sort_rows(int32_t *ids, int32_t stride, int32_t T, int rows, hipStream_t st);
 hipError_t launch_attend(const AttendArgs &a, int rows, hipStream_t st);
+hipError_t launch_attend_rows(const AttendArgs &a, int rows, float *out, float *lse, hipStream_t st);
 hipError_t launch_merge(const MergeArgs &a, int rows, hipStream_t st);
 hipError_t launch_dequant_fp4(const uint8_t *codes, const uint8_t *scales, int64_t n_rows,
                               int32_t channels, uint16_t *out, hipStream_t st);

@@ -238,11 +238,13 @@ LAYER_CASES = [
     # Reindex over a pool long enough for the chunked selection; request 1 has
     # fewer entries than the pool, so its pool ends in -1 pads
     dict(contexts=[4 * 60000, 4 * 9000], layers="FRU", k=1024, pool=12000, page_size=64, shuffle=True),
+    # 520 query rows of a prefill chunk: attention runs one workgroup per query row
+    dict(contexts=[4 * 3000], layers="FRU", k=256, pool=1024, nq=520, prefill=True, page_size=32),
 ]
 
 
 @pytest.mark.parametrize("case", LAYER_CASES, ids=["tiny_full", "full_reuse", "full_reindex_reuse",
-                                                   "rowscale", "short_ctx", "long_pool"])
+                                                   "rowscale", "short_ctx", "long_pool", "prefill_rows"])
 def test_layer_step_chain(case):
     _log(f"layer chain {case}")
     wl = make_small_decode(**case)
