@@ -6,6 +6,10 @@ tokens of context per request (262,144 compressed entries), layers
 128-token FP8 window per layer. Inputs are seeded and synthetic and resident
 in HBM before timing; the step's inputs are rotated over several device
 copies so the 256 MB Infinity Cache cannot hold one step's data for the next.
+The 128K-context workload (batch 32, [Full, Reuse x5]) is timed beside it.
+--workload selects another workload for the JSON line: the 128K one, the
+ragged 64-request 20-layer stack, or the 4096-query prefill chunk (whose
+roofline kernel is the matrix-core scoring, against the fp16 MFMA peak).
 
 Printed: one JSON line (metric, value = queries/s, roofline of the dominant
 kernel measured live with HIP events, CPU-oracle baseline).
@@ -20,10 +24,13 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0
 WORKLOAD = "b8_1m_full_reindex_reuse4"
 WORKLOAD_128K = "b32_128k_full_reuse5"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_index_score_b8_1m.json")
@@ -46,6 +53,9 @@ def parse():
     p.add_argument("--no-graph", action="store_true")
     p.add_argument("--copy-probe-mb", type=int, default=0,
                    help="also run a plain device copy of this size (counter calibration)")
+    p.add_argument("--workload", default=WORKLOAD,
+                   choices=[WORKLOAD, WORKLOAD_128K, "ragged64_paged_20layer", "prefill_4096q_128k"],
+                   help="the workload of the JSON line (default: the 1M-context decode step)")
     p.add_argument("--no-secondary", action="store_true",
                    help="skip the 128K-context (batch 32) workload reported beside the main one")
     return p.parse_args()
@@ -64,6 +74,8 @@ def step_bytes(wl) -> int:
     row + 4 B id per selected entry, window rows, 32 KB fp32 query, 32 KB
     output + 64 B lse.)
     """
+    if wl.q_pos is not None:
+        return prefill_bytes(wl)
     total = 0
     for li, L in enumerate(wl.layers):
         c = wl.caches[L.cache_id]
@@ -79,6 +91,32 @@ def step_bytes(wl) -> int:
             else:
                 total += A
     return total * wl.nq
+
+
+def prefill_bytes(wl) -> int:
+    """Algorithmic bytes of a prefill chunk: each request's indexer keys once
+    (36 B per entry), and per query 160 B of indexer query and weights plus
+    A(K) (its own gathered rows, window rows, q and out), per layer."""
+    total = 0
+    for L in wl.layers:
+        c = wl.caches[L.cache_id]
+        for b in range(wl.batch):
+            N = int(c.n_entries[b])
+            K = min(wl.k, N)
+            A = 292 * K + wl.window * 512 + 32768 + 32832
+            total += (36 * N if L.mode == "F" else 0) + wl.nq * (160 * (L.mode != "U") + A)
+    return total
+
+
+def prefill_score_flops(wl) -> int:
+    """Useful flops of one prefill scoring launch: 4 heads x 64 channels x 2 per
+    visible (query, entry) pair (entry s visible at position p iff 4(s+1) <= p+1)."""
+    c = wl.caches[0]
+    vis = 0
+    for b in range(wl.batch):
+        v = np.minimum((wl.q_pos[b].astype(np.int64) + 1) // 4, int(c.n_entries[b]))
+        vis += int(np.maximum(v, 0).sum())
+    return vis * 4 * 64 * 2
 
 
 def score_kernel_bytes(wl) -> int:
@@ -107,7 +145,9 @@ def upload_chains(wl, n_copies, dev):
                                    block_table=up(c.block_table), n_entries=up(c.n_entries)))
     for L in wl.layers:
         host["layers"].append(dict(q=up(L.q), win_codes=up(L.win.codes), win_len=up(L.win.length),
+                                   win_pos0=up(L.win.pos0), win_rs=up(L.win.row_scale),
                                    qix_codes=up(L.qix_codes), qix_scales=up(L.qix_scales), w=up(L.w)))
+    q_pos = up(wl.q_pos)
     copies = []
     for ci in range(n_copies):
         cl = (lambda x: x) if ci == 0 else (lambda x: None if x is None else x.clone())
@@ -122,18 +162,20 @@ def upload_chains(wl, n_copies, dev):
         for li, Lh in enumerate(wl.layers):
             L = layers[li]
             cache = caches[Lh.cache_id]
-            win = csa2.Window(codes=L["win_codes"], length=L["win_len"])
+            win = csa2.Window(codes=L["win_codes"], length=L["win_len"], pos0=L["win_pos0"],
+                              row_scale=L["win_rs"], window=wl.window)
             if Lh.mode == "F":
                 c = csa2.LayerCall("F", cache, win, L["q"], k, pool=pool, qix_codes=L["qix_codes"],
-                                   qix_scales=L["qix_scales"], w=L["w"], sm_scale=wl.sm_scale)
+                                   qix_scales=L["qix_scales"], w=L["w"], q_pos=q_pos, sm_scale=wl.sm_scale)
                 last_idx, last_pool = c.idx_out, c.pool_out
             elif Lh.mode == "R":
                 c = csa2.LayerCall("R", cache, win, L["q"], k, pool=pool, qix_codes=L["qix_codes"],
-                                   qix_scales=L["qix_scales"], w=L["w"], idx_in=last_pool,
+                                   qix_scales=L["qix_scales"], w=L["w"], idx_in=last_pool, q_pos=q_pos,
                                    sm_scale=wl.sm_scale)
                 last_idx = c.idx_out
             else:
-                c = csa2.LayerCall("U", cache, win, L["q"], k, idx_in=last_idx, sm_scale=wl.sm_scale)
+                c = csa2.LayerCall("U", cache, win, L["q"], k, idx_in=last_idx, q_pos=q_pos,
+                                   sm_scale=wl.sm_scale)
             calls.append(c)
         return calls
 
@@ -197,15 +239,17 @@ def main():
     import torch
 
     import compressed_sparse_attention_06_amd as csa2
-    from synth import make_decode_workload
+    from synth import make_decode_workload, make_prefill_workload, take_queries, take_requests
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     csa2.lib()
+    name = args.workload
+    prefill = name == "prefill_4096q_128k"
     t0 = time.time()
-    wl = make_decode_workload(WORKLOAD)
-    log(f"workload {WORKLOAD} generated in {time.time() - t0:.1f}s; modes {wl.modes}, "
-        f"N/request {int(wl.caches[0].n_entries[0])}")
+    wl = make_prefill_workload() if prefill else make_decode_workload(name)
+    log(f"workload {name} generated in {time.time() - t0:.1f}s; modes {wl.modes}, "
+        f"batch {wl.batch}, queries/request {wl.nq}, N/request {int(wl.caches[0].n_entries[0])}")
     copies, chains = upload_chains(wl, args.copies, dev)
     log(f"inputs on device: {args.copies} copies, "
         f"{torch.cuda.memory_allocated() / 2**30:.2f} GiB allocated")
@@ -220,35 +264,43 @@ def main():
     sbytes = step_bytes(wl)
     gbps = sbytes / (best_s / args.steps) / 1e9
 
-    # ---- dominant kernel: Full-layer index scoring, timed live with HIP events ----
-    kb = score_kernel_bytes(wl)
+    # ---- dominant kernel: the Full layer's indexer scoring, timed live with HIP events ----
     scores = torch.empty(B, nq, copies[0][0][0].capacity, dtype=torch.float32, device=dev)
-    hist = torch.zeros(B, nq, 4096, dtype=torch.int32, device=dev)
-    for i in range(5):
+    hist = None if prefill else torch.zeros(B, nq, 4096, dtype=torch.int32, device=dev)
+    qp = None if wl.q_pos is None else torch.from_numpy(wl.q_pos).to(dev)
+
+    def score_once(i):
         caches, layers = copies[i % len(copies)]
         csa2.index_score(caches[0], layers[0]["qix_codes"], layers[0]["qix_scales"], layers[0]["w"],
-                         out=scores, hist=hist)
+                         q_pos=qp, out=scores, hist=hist)
+
+    for i in range(5):
+        score_once(i)
     torch.cuda.synchronize()
     # back-to-back launches on the stream they run on (torch's current stream,
     # which the binding passes to the library), bracketed by two HIP events
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record()
     for i in range(args.kernel_iters):
-        caches, layers = copies[i % len(copies)]
-        csa2.index_score(caches[0], layers[0]["qix_codes"], layers[0]["qix_scales"], layers[0]["w"],
-                         out=scores, hist=hist)
+        score_once(i)
     ev1.record()
     torch.cuda.synchronize()
     k_ms = ev0.elapsed_time(ev1) / args.kernel_iters
-    k_gbps = kb / (k_ms * 1e-3) / 1e9
-    log(f"index_score kernel: {k_ms * 1e3:.2f} us/launch, {k_gbps:.0f} GB/s algorithmic")
+    if prefill:
+        kflops = prefill_score_flops(wl)
+        k_tflops = kflops / (k_ms * 1e-3) / 1e12
+        log(f"prefill scoring kernel: {k_ms * 1e3:.2f} us/launch, {k_tflops:.1f} TFLOP/s")
+    else:
+        kb = score_kernel_bytes(wl)
+        k_gbps = kb / (k_ms * 1e-3) / 1e9
+        log(f"index_score kernel: {k_ms * 1e3:.2f} us/launch, {k_gbps:.0f} GB/s algorithmic")
 
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         try:
             rec = json.load(open(TRAFFIC_FILE))
             src_hash = hashlib.sha256(open(SCORE_SRC, "rb").read()).hexdigest()
-            if rec.get("kernel_source_sha256") == src_hash and rec.get("workload") == WORKLOAD:
+            if rec.get("kernel_source_sha256") == src_hash and rec.get("workload") == name:
                 traffic = rec.get("bytes_per_launch")
         except Exception:
             traffic = None
@@ -270,7 +322,7 @@ def main():
 
     # ---- the 128K-context workload (batch 32, [Full, Reuse x5]) beside it ----
     secondary = None
-    if not args.no_secondary:
+    if not args.no_secondary and name == WORKLOAD:
         del chains, copies
         torch.cuda.empty_cache()
         wl2 = make_decode_workload(WORKLOAD_128K)
@@ -293,16 +345,25 @@ def main():
     cpu = None
     if not args.skip_cpu:
         import oracle
+        # a bounded sample of the same workload: all requests (decode), a few
+        # requests of the ragged stack, or a few query rows of the prefill chunk
+        if prefill:
+            sample_wl, what = take_queries(wl, range(16)), "16 of the 4096 query rows of the prefill chunk"
+        elif wl.batch > 8:
+            sample_wl, what = take_requests(wl, range(8)), f"8 of the {wl.batch} requests"
+        else:
+            sample_wl, what = wl, f"all {wl.batch} requests"
+        sq = sample_wl.batch * sample_wl.nq
         reps, t_cpu = 0, 0.0
         w0 = time.perf_counter()
         while reps == 0 or (time.perf_counter() - w0) < args.cpu_seconds:
-            oracle.run_workload(wl)
+            oracle.run_workload(sample_wl)
             reps += 1
         t_cpu = time.perf_counter() - w0
-        cores = min(oracle.num_threads(), len(os.sched_getaffinity(0)), B * nq)
-        cpu = dict(value=round(B * nq * reps / t_cpu, 3), unit="queries/s", cores=cores, kind="oracle",
-                   sample=f"the whole 6-layer step of all {B} requests, repeated {reps}x "
-                          f"({t_cpu:.1f}s); fp64 C oracle, OpenMP over requests")
+        cores = min(oracle.num_threads(), len(os.sched_getaffinity(0)))
+        cpu = dict(value=round(sq * reps / t_cpu, 3), unit="queries/s", cores=cores, kind="oracle",
+                   sample=f"the whole {len(wl.layers)}-layer step of {what}, repeated {reps}x "
+                          f"({t_cpu:.1f}s); fp64 C oracle, OpenMP over query rows")
         log(f"cpu oracle: {cpu['value']} queries/s on {cores} threads")
 
     line = {
@@ -318,7 +379,8 @@ def main():
         "vs_baseline": None,
         "dtype": "fp4/fp8 inputs; fp4 and f16 MFMA, f32 accumulate",
         "data": "synthetic",
-        "config": {"workload": WORKLOAD, "batch": B, "context_tokens": int(wl.contexts[0]),
+        "config": {"workload": name, "batch": B, "queries_per_request": nq,
+                   "context_tokens": int(wl.contexts[0]),
                    "entries_per_request": int(wl.caches[0].n_entries[0]), "layers": wl.modes,
                    "top_k": k, "pool": pool, "window": 128, "input_copies": args.copies,
                    "timing": "graph" if (graph_s is not None and graph_s <= eager_s) else "eager"},
@@ -327,10 +389,15 @@ def main():
         "step_algorithmic_bytes": sbytes,
         "eager_ms_per_step": round(eager_s / args.steps * 1e3, 4),
         "graph_ms_per_step": None if graph_s is None else round(graph_s / args.steps * 1e3, 4),
-        "roofline": {"kernel": "k_index_score (Full-layer lightning-indexer scoring)", "bound": "hbm",
-                     "achieved": round(k_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(k_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                     "bytes_per_launch": kb, "us_per_launch": round(k_ms * 1e3, 3)},
+        "roofline": (
+            {"kernel": "k_prefill_score (indexer scoring of a prefill chunk, fp16 MFMA)", "bound": "mfma",
+             "achieved": round(k_tflops, 1), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+             "frac": round(k_tflops / MFMA_F16_PEAK_TFLOPS, 4), "traffic": traffic,
+             "flops_per_launch": kflops, "us_per_launch": round(k_ms * 1e3, 3)} if prefill else
+            {"kernel": "k_index_score (Full-layer lightning-indexer scoring)", "bound": "hbm",
+             "achieved": round(k_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+             "frac": round(k_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
+             "bytes_per_launch": kb, "us_per_launch": round(k_ms * 1e3, 3)}),
         "cpu_baseline": cpu,
         "secondary": secondary,
     }

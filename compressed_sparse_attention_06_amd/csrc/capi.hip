@@ -30,24 +30,31 @@ constexpr int kFinItems = 4096;        // rows up to this length select in LDS d
 constexpr int kScoreChunk = 2048;      // scoring columns per workgroup (contiguous entries)
 constexpr int kScoreChunkCand = 512;   // ... when gathering a candidate list
 constexpr int64_t kRowAttendMin = 512;  // query rows from which attention runs one workgroup per row
+constexpr int32_t kPrefillQueries = 64;  // queries per request from which scoring is a matrix-core contraction
+
+// Scoring as a dense queries x entries contraction (many queries of one
+// request, every visible entry, pages of at least 16 entries).
+bool use_prefill_scoring(int32_t nq, const int32_t *cand, int32_t page_size) {
+  return nq >= kPrefillQueries && !cand && page_size >= 16;
+}
 constexpr int64_t kMaxSelectCols = CSA2_MAX_SELECT_COLS;
 static_assert(CSA2_MAX_SELECT_COLS <= SEL_MAX_WG * 8192, "the chunked selection takes SEL_MAX_WG chunks of 8192");
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Columns per selection chunk: the smallest of 2048, 4096, 8192 that cuts
-// the row into at most SEL_MAX_WG chunks and, where possible, keeps the
-// final pass (one workgroup per chunk, row and target) within two
-// workgroups per compute unit.
+// the row into at most SEL_MAX_WG chunks and keeps the final pass (one
+// workgroup per chunk, row and target) within two workgroups per compute
+// unit; when no size does (many rows), the size with the fewest workgroups.
 int32_t select_chunk(int64_t n_cols, int64_t rows, int ntarget) {
-  int32_t fallback = 0;
+  int32_t largest = 0;
   for (int32_t c = 2048; c <= 8192; c <<= 1) {
     const int64_t nwg = (n_cols + c - 1) / c;
     if (nwg > SEL_MAX_WG) continue;
-    if (!fallback) fallback = c;
     if (nwg * rows * ntarget <= 512) return c;
+    largest = c;
   }
-  return fallback ? fallback : 8192;
+  return largest ? largest : 8192;
 }
 
 struct WsLayout {
@@ -330,6 +337,13 @@ csa2_status csa2_index_score(const csa2_cache *cache, const uint8_t *qix_codes,
   a.hist = hist;
   a.write_masked = 1;
   a.chunk = kScoreChunk;
+  if (use_prefill_scoring(nq, cand, cache->page_size)) {
+    a.hist = nullptr;
+    s = hip_check(csa2::launch_prefill_score(a, batch, (hipStream_t)stream), "index_score");
+    if (s || !hist) return s;
+    return hip_check(csa2::launch_hist(scores, a.n_cols, batch * nq, hist, (hipStream_t)stream,
+                                       cache->n_entries, q_pos, nq), "hist");
+  }
   return hip_check(csa2::launch_index_score(a, batch * nq, (hipStream_t)stream), "index_score");
 }
 
@@ -433,7 +447,16 @@ csa2_status csa2_layer_step(const csa2_layer_args *p, void *stream) {
     const SelTarget tgr{p->k, p->idx_out, p->k};
     const SelTarget *tg = p->mode == CSA2_FULL ? tgf : &tgr;
     const int ntarget = (p->mode == CSA2_FULL && p->pool > 0) ? 2 : 1;
-    if ((s = hip_check(csa2::launch_index_score(a, rows, st), "index_score"))) return s;
+    if (p->mode == CSA2_FULL && use_prefill_scoring(p->nq, nullptr, p->cache->page_size)) {
+      a.hist = nullptr;
+      if ((s = hip_check(csa2::launch_prefill_score(a, p->batch, st), "index_score"))) return s;
+      if (L.compact &&
+          (s = hip_check(csa2::launch_hist(scores, n_cols, rows, (uint32_t *)(ws + L.hist), st,
+                                           p->cache->n_entries, p->q_pos, p->nq), "hist")))
+        return s;
+    } else if ((s = hip_check(csa2::launch_index_score(a, rows, st), "index_score"))) {
+      return s;
+    }
     if (p->mode == CSA2_FULL)
       s = run_select(L, ws, rows, n_cols, nullptr, p->cache->n_entries, p->q_pos, p->nq, tg, ntarget, true,
                      scores, st);

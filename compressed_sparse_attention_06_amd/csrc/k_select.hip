@@ -67,18 +67,30 @@ __device__ __forceinline__ int32_t row_limit(const int32_t *n_entries, const int
 }
 
 // ---- standalone histogram ------------------------------------------------------
+// Columns past a row's limit (visible entries, when n_entries is given) are
+// not counted: they may hold nothing.
 __global__ __launch_bounds__(256) void k_hist(const float *scores, int32_t n_cols, int32_t chunk,
-                                              uint32_t *hist) {
+                                              uint32_t *hist, const int32_t *n_entries,
+                                              const int32_t *q_pos, int32_t nq) {
   __shared__ uint32_t lh[HIST_BINS];
   const int r = blockIdx.y;
+  const int32_t lim = row_limit(n_entries, q_pos, nq, r, n_cols);
   const int64_t c0 = (int64_t)blockIdx.x * chunk;
-  const int64_t c1 = min(c0 + (int64_t)chunk, (int64_t)n_cols);
+  if (c0 >= lim) return;  // uniform
+  const int64_t c1 = min(c0 + (int64_t)chunk, (int64_t)lim);
   for (int i = threadIdx.x; i < HIST_BINS; i += 256) lh[i] = 0;
   __syncthreads();
   const float *row = scores + (int64_t)r * n_cols;
-  for (int64_t j = c0 + threadIdx.x; j < c1; j += 256) {
-    const uint32_t k = score_key(row[j]);
-    if (k > KEY_NEG_INF) atomicAdd(&lh[k >> HIST_SHIFT], 1u);
+  constexpr int U = 8;
+  for (int64_t j0 = c0 + threadIdx.x; j0 < c1; j0 += 256 * U) {
+    float v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = row[min(j0 + 256 * u, c1 - 1)];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t k = score_key(v[u]);
+      if (j0 + 256 * u < c1 && k > KEY_NEG_INF) atomicAdd(&lh[k >> HIST_SHIFT], 1u);
+    }
   }
   __syncthreads();
   for (int i = threadIdx.x; i < HIST_BINS; i += 256)
@@ -86,10 +98,10 @@ __global__ __launch_bounds__(256) void k_hist(const float *scores, int32_t n_col
 }
 
 hipError_t launch_hist(const float *scores, int32_t n_cols, int rows, uint32_t *hist,
-                       hipStream_t st) {
+                       hipStream_t st, const int32_t *n_entries, const int32_t *q_pos, int32_t nq) {
   const int32_t chunk = 8192;
   dim3 grid((unsigned)((n_cols + chunk - 1) / chunk), (unsigned)rows);
-  hipLaunchKernelGGL(k_hist, grid, dim3(256), 0, st, scores, n_cols, chunk, hist);
+  hipLaunchKernelGGL(k_hist, grid, dim3(256), 0, st, scores, n_cols, chunk, hist, n_entries, q_pos, nq);
   return hipGetLastError();
 }
 

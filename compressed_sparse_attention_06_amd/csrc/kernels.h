@@ -117,7 +117,9 @@ struct MergeArgs {
 hipError_t launch_fill_u32(uint32_t *p, int64_t n, uint32_t v, hipStream_t st);
 hipError_t launch_index_score(const ScoreArgs &a, int rows, hipStream_t st);
 hipError_t launch_hist(const float *scores, int32_t n_cols, int rows, uint32_t *hist,
-                       hipStream_t st);
+                       hipStream_t st, const int32_t *n_entries = nullptr,
+                       const int32_t *q_pos = nullptr, int32_t nq = 1);
+hipError_t launch_prefill_score(const ScoreArgs &a, int batch, hipStream_t st);
 hipError_t launch_compact(const CompactArgs &a, int rows, hipStream_t st);
 hipError_t launch_final(const FinalArgs &a, int rows, int ntarget, hipStream_t st);
 hipError_t launch_select_direct(const DirectArgs &a, int rows, int ntarget, hipStream_t st);

@@ -17,5 +17,7 @@ from .workloads import (  # noqa: F401
     Window,
     make_decode_workload,
     make_prefill_workload,
+    take_queries,
+    take_requests,
     make_small_decode,
 )

@@ -327,3 +327,46 @@ def make_small_decode(contexts, layers="F", k=16, pool=0, page_size=64, shuffle=
                           page_size=page_size, shuffle=shuffle, nq=nq, prefill=prefill,
                           seed=seed, stream=stream, row_scale=row_scale,
                           bias_frac=bias_frac, window=window)
+
+
+# ---- subsets (array slicing only) ---------------------------------------------
+
+def take_requests(wl: DecodeWorkload, reqs) -> DecodeWorkload:
+    """The same workload restricted to some requests (caches keep every page)."""
+    reqs = list(reqs)
+
+    def cs(c: Cache):
+        return Cache(kv_codes=c.kv_codes, kv_scales=c.kv_scales, ix_codes=c.ix_codes,
+                         ix_scales=c.ix_scales, block_table=c.block_table[reqs],
+                         n_entries=c.n_entries[reqs], page_size=c.page_size)
+
+    def ws(w: Window):
+        return Window(codes=w.codes[reqs], row_scale=None if w.row_scale is None else w.row_scale[reqs],
+                          length=w.length[reqs], pos0=None if w.pos0 is None else w.pos0[reqs],
+                          window=w.window)
+
+    layers = []
+    for L in wl.layers:
+        layers.append(LayerInputs(mode=L.mode, cache_id=L.cache_id, q=L.q[reqs], win=ws(L.win),
+                                  qix_codes=None if L.qix_codes is None else L.qix_codes[reqs],
+                                  qix_scales=None if L.qix_scales is None else L.qix_scales[reqs],
+                                  w=None if L.w is None else L.w[reqs]))
+    return DecodeWorkload(name=wl.name + "_slice", contexts=wl.contexts[reqs], nq=wl.nq, k=wl.k,
+                          pool=wl.pool, caches=[cs(c) for c in wl.caches], layers=layers,
+                          q_pos=None if wl.q_pos is None else wl.q_pos[reqs], sm_scale=wl.sm_scale,
+                          window=wl.window, meta=dict(wl.meta))
+
+
+def take_queries(wl: DecodeWorkload, qs) -> DecodeWorkload:
+    """The same (single-request) workload restricted to some query rows."""
+    qs = list(qs)
+    layers = []
+    for L in wl.layers:
+        layers.append(LayerInputs(mode=L.mode, cache_id=L.cache_id, q=L.q[:, qs], win=L.win,
+                                  qix_codes=None if L.qix_codes is None else L.qix_codes[:, qs],
+                                  qix_scales=None if L.qix_scales is None else L.qix_scales[:, qs],
+                                  w=None if L.w is None else L.w[:, qs]))
+    return DecodeWorkload(name=wl.name + "_qslice", contexts=wl.contexts, nq=len(qs), k=wl.k,
+                          pool=wl.pool, caches=wl.caches, layers=layers,
+                          q_pos=None if wl.q_pos is None else wl.q_pos[:, qs], sm_scale=wl.sm_scale,
+                          window=wl.window, meta=dict(wl.meta))

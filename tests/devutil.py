@@ -8,7 +8,7 @@ import torch
 
 import compressed_sparse_attention_06_amd as csa2
 from synth.workloads import Cache as HostCache
-from synth.workloads import DecodeWorkload, LayerInputs, Window as HostWindow
+from synth.workloads import DecodeWorkload, LayerInputs, Window as HostWindow, take_queries, take_requests
 
 
 def t(a, dtype=None, device="cuda"):
@@ -88,45 +88,8 @@ def run_gpu(wl: DecodeWorkload, layers=None):
     return res
 
 
-def slice_requests(wl: DecodeWorkload, reqs) -> DecodeWorkload:
-    """The same workload restricted to some requests (caches keep every page)."""
-    reqs = list(reqs)
-
-    def cs(c: HostCache):
-        return HostCache(kv_codes=c.kv_codes, kv_scales=c.kv_scales, ix_codes=c.ix_codes,
-                         ix_scales=c.ix_scales, block_table=c.block_table[reqs],
-                         n_entries=c.n_entries[reqs], page_size=c.page_size)
-
-    def ws(w: HostWindow):
-        return HostWindow(codes=w.codes[reqs], row_scale=None if w.row_scale is None else w.row_scale[reqs],
-                          length=w.length[reqs], pos0=None if w.pos0 is None else w.pos0[reqs],
-                          window=w.window)
-
-    layers = []
-    for L in wl.layers:
-        layers.append(LayerInputs(mode=L.mode, cache_id=L.cache_id, q=L.q[reqs], win=ws(L.win),
-                                  qix_codes=None if L.qix_codes is None else L.qix_codes[reqs],
-                                  qix_scales=None if L.qix_scales is None else L.qix_scales[reqs],
-                                  w=None if L.w is None else L.w[reqs]))
-    return DecodeWorkload(name=wl.name + "_slice", contexts=wl.contexts[reqs], nq=wl.nq, k=wl.k,
-                          pool=wl.pool, caches=[cs(c) for c in wl.caches], layers=layers,
-                          q_pos=None if wl.q_pos is None else wl.q_pos[reqs], sm_scale=wl.sm_scale,
-                          window=wl.window, meta=dict(wl.meta))
-
-
-def slice_queries(wl: DecodeWorkload, qs) -> DecodeWorkload:
-    """The same (single-request) workload restricted to some query rows."""
-    qs = list(qs)
-    layers = []
-    for L in wl.layers:
-        layers.append(LayerInputs(mode=L.mode, cache_id=L.cache_id, q=L.q[:, qs], win=L.win,
-                                  qix_codes=None if L.qix_codes is None else L.qix_codes[:, qs],
-                                  qix_scales=None if L.qix_scales is None else L.qix_scales[:, qs],
-                                  w=None if L.w is None else L.w[:, qs]))
-    return DecodeWorkload(name=wl.name + "_qslice", contexts=wl.contexts, nq=len(qs), k=wl.k,
-                          pool=wl.pool, caches=wl.caches, layers=layers,
-                          q_pos=None if wl.q_pos is None else wl.q_pos[:, qs], sm_scale=wl.sm_scale,
-                          window=wl.window, meta=dict(wl.meta))
+slice_requests = take_requests
+slice_queries = take_queries
 
 
 # ---- comparisons -------------------------------------------------------------------

@@ -126,6 +126,29 @@ def test_index_score_causal_and_candidates():
     _check_scores(g, o, "candidates")
 
 
+@pytest.mark.parametrize("page_size", [16, 64])
+def test_index_score_prefill_chunk(page_size):
+    """Many queries per request (the matrix-core contraction path): 2 requests x 130
+    queries at ragged positions, block-causal, with the score histogram."""
+    _log(f"index_score prefill chunk page {page_size}")
+    wl = make_small_decode([4 * 2500, 4 * 700], layers="F", k=16, nq=130, prefill=True,
+                           page_size=page_size, shuffle=True)
+    L, c = wl.layers[0], wl.caches[0]
+    rng = np.random.default_rng(page_size)
+    qp = np.stack([np.sort(rng.integers(0, 4 * 2500 + 40, size=130)),
+                   np.sort(rng.integers(0, 4 * 700 + 40, size=130))]).astype(np.int32)
+    qp[0, :3] = [0, 2, 3]  # nothing, nothing, entry 0 visible
+    hist = torch.zeros(2, 130, 4096, dtype=torch.int32, device="cuda")
+    g = csa2.index_score(dev_cache(c), t(L.qix_codes), t(L.qix_scales), t(L.w), q_pos=t(qp),
+                         hist=hist).cpu().numpy()
+    o = oracle.index_score(c, L.qix_codes, L.qix_scales, L.w, q_pos=qp)
+    _check_scores(g, o, "prefill chunk")
+    h = hist.cpu().numpy()
+    fin = np.isfinite(g)
+    assert (h.sum(axis=-1) == fin.sum(axis=-1)).all()
+    assert h[0, 0].sum() == 0 and h[0, 2].sum() == 1
+
+
 # ------------------------------------------------------------------ top-K
 
 @pytest.mark.parametrize("n,k", [(100, 7), (2048 + 37, 256), (16384, 2048), (16385, 2048),
