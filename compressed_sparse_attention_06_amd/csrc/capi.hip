@@ -6,6 +6,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "csa2_dev.h"
 #include "kernels.h"
 
@@ -29,7 +31,6 @@ csa2_status hip_check(hipError_t e, const char *what) {
 constexpr int kFinItems = 4096;        // rows up to this length select in LDS directly
 constexpr int kScoreChunk = 2048;      // scoring columns per workgroup (contiguous entries)
 constexpr int kScoreChunkCand = 512;   // ... when gathering a candidate list
-constexpr int64_t kRowAttendMin = 512;  // query rows from which attention runs one workgroup per row
 constexpr int32_t kPrefillQueries = 64;  // queries per request from which scoring is a matrix-core contraction
 
 // Scoring as a dense queries x entries contraction (many queries of one
@@ -62,19 +63,28 @@ struct WsLayout {
          eq1 = 0, part = 0,
          total = 0;
   bool compact = false;
-  int max_wg = 0, chunk = 0, n_split = 0, rows_per_split = 256;
+  int max_wg = 0, chunk = 0;
   int64_t seg_stride = 0;
+  // attention: units of 128 positions, U per row, T in all, over G workgroups
+  int32_t att_U = 0, att_G = 0;
+  int64_t att_T = 0;
+  int32_t att_slots = 1;  // most workgroups sharing one row (2+: merge pass)
 };
 
-// Attention rows per workgroup. Many query rows (a prefill chunk): 0, one
-// workgroup per row walking all its tiles, no partials and no merge. Few rows
-// (decode): split-K, 64 rows per split when 64-row splits still fit the GPU
-// in one round of one workgroup per compute unit, else 128 (fewer partials
-// to merge; measured faster on the 8 x 1M-context step).
-int rows_per_split(int64_t rows, int64_t span) {
-  if (rows >= kRowAttendMin) return 0;
-  const int64_t wg64 = rows * ((span + 63) / 64);
-  return wg64 <= 256 ? 64 : 128;
+// Attention work split: each row's attention set (k entries, then the window
+// from k rounded up to 16) in units of 128 positions, shared out evenly over
+// at most one workgroup per compute unit.
+void attend_geometry(WsLayout &L, int64_t rows, int32_t k, int32_t win_cap) {
+  const int64_t span = (((int64_t)k + 15) & ~(int64_t)15) + (win_cap > 0 ? win_cap : 0);
+  L.att_U = (int32_t)((span + 127) / 128);
+  L.att_T = rows * L.att_U;
+  L.att_G = (int32_t)std::min<int64_t>(L.att_T, csa2::kSegMaxWg);
+  const int64_t rows_n = L.att_T / L.att_U;
+  auto owner = [&](int64_t u) { return ((u + 1) * L.att_G + L.att_T - 1) / L.att_T - 1; };
+  L.att_slots = 1;
+  for (int64_t r = 0; r < rows_n; ++r)
+    L.att_slots = std::max<int32_t>(L.att_slots,
+                                    (int32_t)(owner(r * L.att_U + L.att_U - 1) - owner(r * L.att_U) + 1));
 }
 
 WsLayout ws_layout(csa2_mode mode, int64_t rows, int64_t n_cols, int32_t k, int32_t win_cap, int ntarget) {
@@ -108,12 +118,9 @@ WsLayout ws_layout(csa2_mode mode, int64_t rows, int64_t n_cols, int32_t k, int3
       off = align256(off + (size_t)rows * L.seg_stride * 8);
     }
   }
-  const int64_t span = (int64_t)k + (win_cap > 0 ? win_cap : 0);
-  L.rows_per_split = rows_per_split(rows, span);
-  L.n_split = L.rows_per_split ? (int)((span + L.rows_per_split - 1) / L.rows_per_split) : 1;
-  if (L.n_split < 1) L.n_split = 1;
-  L.part = off;
-  if (L.rows_per_split) off = align256(off + (size_t)rows * L.n_split * CSA2_H * csa2::kPartStride * 4);
+  attend_geometry(L, rows, k, win_cap);
+  L.part = off;  // two partials per workgroup
+  if (L.att_slots > 1) off = align256(off + (size_t)L.att_G * 2 * CSA2_H * csa2::kPartStride * 4);
   L.total = off;
   return L;
 }
@@ -273,18 +280,14 @@ csa2_status run_attend(const WsLayout &L, char *ws, const csa2_cache *cache, con
   a.q_pos = q_pos;
   a.nq = nq;
   a.sm_scale = sm_scale;
-  a.rows_per_split = L.rows_per_split;
-  a.n_split = L.n_split;
   a.part = (float *)(ws + L.part);
-  if (L.rows_per_split == 0) return hip_check(csa2::launch_attend_rows(a, rows, out, lse, st), "attend");
-  csa2_status s = hip_check(csa2::launch_attend(a, rows, st), "attend");
-  if (s) return s;
-  csa2::MergeArgs m{};
-  m.part = a.part;
-  m.n_split = L.n_split;
-  m.out = out;
-  m.lse = lse;
-  return hip_check(csa2::launch_merge(m, rows, st), "merge");
+  csa2::SegArgs sg{};
+  sg.T = L.att_T;
+  sg.U = L.att_U;
+  sg.G = L.att_G;
+  sg.out = out;
+  sg.lse = lse;
+  return hip_check(csa2::launch_attend_seg(a, sg, L.att_slots, st), "attend");
 }
 
 }  // namespace

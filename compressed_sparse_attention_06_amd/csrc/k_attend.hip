@@ -4,154 +4,318 @@
 // global Q and its own SWA KV; all heads share one compressed latent, so the
 // latent row is both key and value).
 //
-// One workgroup (4 waves) owns a (query row, split) pair: a contiguous slice of
-// the attention set, processed in tiles of 64 rows, 16 per wave.
-//  * each lane holds one quarter (128 channels) of one row of its wave's 16:
-//    the FP4 codes (64 bytes + 8 scale bytes) of a selected entry, or the E4M3
-//    bytes of a window row, all loaded before any compute;
+// Layout of the work: see the segmented attention section below. Inside one
+// unit of 128 positions, each of eight waves owns 16 rows:
+//  * each lane holds one quarter (128 channels) of one row: the FP4 codes (64
+//    bytes + 8 scale bytes) of a selected entry, or the E4M3 bytes of a window
+//    row, loaded one unit ahead;
 //  * S = Q R^T with v_mfma_f32_16x16x32_f16 (M = the 16 heads, N = the wave's
 //    16 rows, K = 512 channels in 16 steps). The channel order inside a step
 //    is free as long as both operands share it: step ks, lane quarter kq and
 //    element j stand for channel 128 kq + 8 ks + j, so each lane dequantises
 //    its own B operand straight from registers (E2M1 x E4M3 and E4M3 are exact
 //    in fp16). Q is carried as an fp16 hi + lo pair after a per-head
-//    power-of-two normalisation (about 22 significant bits);
-//  * the dequantised rows also go to an LDS tile [64][512] fp16 for O += P R,
-//    where each wave owns 128 output channels and reads R with rows along K
-//    through ds_read_b64_tr_b16;
-//  * online softmax in fp32 (base-2) across tiles; three workgroup barriers
-//    per tile.
-// The partial (unnormalised O, running max, running sum) of each split goes to
-// the workspace; k_merge combines the splits.
+//    power-of-two normalisation (about 22 significant bits); the hi halves
+//    stay in registers, the lo halves are read from LDS at each step;
+//  * the dequantised rows also go to an LDS tile [128][512] fp16 for
+//    O += P R, where wave w owns output channels 64 w .. 64 w + 63 and reads R
+//    with rows along K through ds_read_b64_tr_b16;
+//  * online softmax in fp32 (base-2) across units; three workgroup barriers
+//    per unit.
 #include "csa2_dev.h"
 #include "kernels.h"
 
 namespace csa2 {
 
-#define AT_ROWS 64     // rows per tile (4 waves x 16)
-#define AT_PITCH 520   // halfs per LDS row of Q and of the R tile (512 + 8)
-#define AT_PPITCH 72   // halfs per LDS row of P (64 + 8)
+#define AT_PITCH 520   // halfs per LDS row of the staged Q (512 + 8)
 
 typedef __attribute__((address_space(3))) v4s *lds_v4s_ptr;
 
-// One lane's quarter of one tile row. FP4 entry: c[0..3] hold the 64 code
-// bytes, c[4].x and c[4].y the 8 group scales; window row: c[0..7] hold the
-// 128 E4M3 bytes.
-struct Slice {
-  v4i c[8];
-  float rs;   // window row scale (1 for entries)
-  int kind;   // 0 no row, 1 entry, 2 window row
-};
+enum { SPLIT_ENTRIES = 0, SPLIT_WINDOW = 1 };
 
-enum { SPLIT_ENTRIES = 0, SPLIT_WINDOW = 1, SPLIT_MIXED = 2 };
-
-// Reductions over each row of 16 lanes with DPP moves (no LDS round trip):
-// swap neighbours, swap pairs, mirror within 8 lanes, mirror within 16.
+// DPP move within rows of 16 lanes (quad_perm / mirror controls only)
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
-__device__ __forceinline__ float row16_max(float v) {
-  v = fmaxf(v, dpp_f32<0xB1>(v));   // quad_perm [1,0,3,2]
-  v = fmaxf(v, dpp_f32<0x4E>(v));   // quad_perm [2,3,0,1]
-  v = fmaxf(v, dpp_f32<0x141>(v));  // row_half_mirror
-  v = fmaxf(v, dpp_f32<0x140>(v));  // row_mirror
-  return v;
+
+// Q of query row r: this thread's 32 fp32 values (head tid / 16, channels
+// 32 (tid % 16) + [0, 32)).
+__device__ __forceinline__ void load_q(const AttendArgs &a, int r, float *qv) {
+  const int tid = threadIdx.x;
+  const float *src = a.q + ((int64_t)r * CSA2_H + (tid >> 4)) * CSA2_D + (tid & 15) * 32;
+#pragma unroll
+  for (int i = 0; i < 32; i += 4) {
+    const v4f x = *(const v4f *)(src + i);
+    qv[i] = x[0];
+    qv[i + 1] = x[1];
+    qv[i + 2] = x[2];
+    qv[i + 3] = x[3];
+  }
 }
-__device__ __forceinline__ float row16_sum(float v) {
-  v += dpp_f32<0xB1>(v);
-  v += dpp_f32<0x4E>(v);
-  v += dpp_f32<0x141>(v);
-  v += dpp_f32<0x140>(v);
+
+// Window geometry of query row r: rows w_first..w_last of its request's window.
+__device__ __forceinline__ void window_range(const AttendArgs &a, int r, int b, int32_t &w_first,
+                                             int32_t &w_last) {
+  w_first = 0;
+  w_last = -1;
+  if (!a.win_codes) return;
+  const int32_t len = a.win_len[b];
+  if (a.win_pos0) {
+    const int32_t pq = a.q_pos ? a.q_pos[r] : 0x7FFFFFFF;
+    const int64_t rel = (int64_t)pq - a.win_pos0[b];
+    w_first = (int32_t)max((int64_t)0, rel - a.win_window + 1);
+    w_last = (int32_t)min(min((int64_t)len, (int64_t)a.win_rows) - 1, rel);
+  } else {
+    w_last = min(len, a.win_rows) - 1;
+  }
+}
+
+// ---- segmented attention: eight waves, 128 positions per step -----------------------
+// The attention set of every query row (k selected entries, then from k
+// rounded up to 16 up to win_cap window rows) is cut into units of 128 positions, and the units of all rows,
+// row after row, are shared out evenly over G workgroups (G <= 256, one per
+// compute unit: the 128-row R tile takes most of the LDS). A workgroup walks
+// its units in order with one online-softmax state per row, loading the next
+// unit's rows while it computes the current one (ids two units ahead,
+// block-table words one ahead). Each of the eight waves takes 16 positions of a
+// unit, so two waves share each SIMD and cover each other's latencies. A row
+// whose units all fall to one workgroup is normalised and written there; a row
+// cut between workgroups leaves one partial per workgroup (slot 0 for the
+// workgroup's first row, slot 1 for its last), which k_merge_seg combines.
+#define AS_UNIT 128   // positions per unit (8 waves x 16)
+#define AS_PPITCH 136 // halfs per LDS row of P (128 + 8)
+#define AS_RPITCH 512 // halfs per LDS row of the R tile (unpadded; 16-byte chunks are swizzled)
+#ifndef SEG_QLO_LDS
+#define SEG_QLO_LDS 1 // the low halves of Q are read from LDS at each step
+#endif
+
+// R tile swizzle: in row r, the 16-byte chunk c of each 256-byte block is
+// stored at chunk c ^ seg_rswz(r). Sixteen consecutive rows then fill every
+// bank for the QK stores (same chunk, 16 rows) and eight rows x two chunks do
+// the same for the PV transposed loads, with 32 or 64 banks.
+__device__ __forceinline__ int seg_rswz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1) | (r & 8); }
+
+struct SegShared {
+  union {
+    struct {
+      _Float16 q[CSA2_H * AT_PITCH];
+#if !SEG_QLO_LDS
+      _Float16 qlo[CSA2_H * AT_PITCH];
+#endif
+    };
+    _Float16 r[AS_UNIT * AS_RPITCH];
+  };
+#if SEG_QLO_LDS
+  _Float16 qlo[CSA2_H * AT_PITCH];
+#endif
+  _Float16 p[CSA2_H * AS_PPITCH];
+  float wmax[CSA2_H][8], wsum[CSA2_H][8];  // [head][wave]
+  float m[CSA2_H], l[CSA2_H], qexp[CSA2_H];
+};
+
+struct SegQ {
+  v8h qa[16];
+#if !SEG_QLO_LDS
+  v8h ql[16];
+#endif
+  float qs[4];  // logit scale (sm_scale * log2 e * 2^e) of heads 4g + i
+};
+
+// One lane's share of a unit row: the 64 code bytes and 8 scale bytes of a
+// selected entry, or the first 64 E4M3 bytes of a window row (the other 64
+// are loaded when the unit is computed, which keeps the prefetch buffer small).
+struct SegSlice {
+  v4i c[4];
+  uint32_t s0, s1;
+  float rs;     // window row scale (1 for entries)
+  int32_t tag;  // entry id (checked against the request's entry count), or window row
+  int kind;     // 0 no row, 1 entry, 2 window row
+};
+
+struct SegFetch {
+  int32_t id, page;
+};
+
+// max of two non-NaN floats in one instruction: median of (a, b, +inf)
+__device__ __forceinline__ float fmax_nc(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, INFINITY); }
+
+// maximum over each row of 16 lanes: swap neighbours, swap pairs, mirror
+// within 8 lanes, mirror within 16
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmax_nc(v, dpp_f32<0xB1>(v));
+  v = fmax_nc(v, dpp_f32<0x4E>(v));
+  v = fmax_nc(v, dpp_f32<0x141>(v));
+  v = fmax_nc(v, dpp_f32<0x140>(v));
   return v;
 }
 
-// Loads are unconditional from clamped, in-range addresses (row 0 stands in
-// for a missing row: its values are finite and get zero weight).
-__device__ __forceinline__ void load_entry(const AttendArgs &a, int32_t id, int32_t page, bool in_range,
-                                           int32_t nent, int kq, Slice &f) {
+// Positions of a row's attention set: entries at [0, k), window rows from
+// kw = k rounded up to 16, so that each wave's 16 positions are all entries
+// (those at k and beyond hold nothing) or all window rows.
+__device__ __forceinline__ int32_t seg_kw(int32_t k) { return (k + 15) & ~15; }
+
+// id of the lane's position in unit y (0 past the range or for window waves)
+__device__ __forceinline__ int32_t seg_fetch_id(const AttendArgs &a, int64_t y, int64_t u_end, int32_t U,
+                                                int prow) {
+  if (y >= u_end) return 0;
+  const int32_t r = (int32_t)(y / U), j = (int32_t)(y % U);
+  if (j * AS_UNIT + (prow & ~15) >= seg_kw(a.k)) return 0;  // uniform per wave
+  const int32_t pos = min(j * AS_UNIT + prow, a.k - 1);
+  return a.idx[(int64_t)r * a.k + pos];
+}
+
+__device__ __forceinline__ int32_t seg_fetch_page(const AttendArgs &a, int64_t y, int64_t u_end, int32_t U,
+                                                  int prow, int32_t id) {
+  if (y >= u_end) return 0;
+  const int32_t r = (int32_t)(y / U), j = (int32_t)(y % U);
+  if (j * AS_UNIT + (prow & ~15) >= seg_kw(a.k)) return 0;
+  const int b = r / a.nq;
+  const int32_t pg = min(max(id, 0) >> a.c.page_shift, a.c.max_pages - 1);
+  return a.c.block_table[(int64_t)b * a.c.max_pages + pg];
+}
+
+// The address depends only on the id and the page word; whether the id is
+// below the request's entry count is decided when the unit is computed.
+__device__ __forceinline__ void seg_load_entry(const AttendArgs &a, int32_t id, int32_t page, int kq,
+                                               SegSlice &f) {
   const int sh = a.c.page_shift;
-  const bool ok = in_range && id >= 0 && id < nent && (id >> sh) < a.c.max_pages && page >= 0 &&
-                  page < a.c.num_pages;
+  const bool ok = id >= 0 && (id >> sh) < a.c.max_pages && page >= 0 && page < a.c.num_pages;
   const int64_t crow = ok ? ((int64_t)page << sh) + (id & ((1 << sh) - 1)) : 0;
   const uint8_t *cp = a.c.kv_codes + crow * 256 + kq * 64;
 #pragma unroll
   for (int i = 0; i < 4; ++i) f.c[i] = *(const v4i *)(cp + 16 * i);
   const v2f sc = *(const v2f *)(a.c.kv_scales + crow * 32 + kq * 8);
-  f.c[4][0] = __float_as_int(sc[0]);
-  f.c[4][1] = __float_as_int(sc[1]);
+  f.s0 = (uint32_t)__float_as_int(sc[0]);
+  f.s1 = (uint32_t)__float_as_int(sc[1]);
   f.rs = 1.f;
+  f.tag = id;
   f.kind = ok ? 1 : 0;
 }
 
-__device__ __forceinline__ void load_window(const AttendArgs &a, int b, int32_t j, bool ok, int kq, Slice &f) {
-  const int64_t wr = (int64_t)b * a.win_rows + (ok ? j : 0);
-  const uint8_t *src = a.win_codes + wr * CSA2_D + kq * 128;
+__device__ __forceinline__ void seg_load_window(const AttendArgs &a, int b, int32_t j, bool ok, int kq,
+                                                SegSlice &f) {
+  const int32_t wr = b * a.win_rows + (ok ? j : 0);
+  const uint8_t *src = a.win_codes + (int64_t)wr * CSA2_D + kq * 128;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) f.c[i] = *(const v4i *)(src + 16 * i);
+  for (int i = 0; i < 4; ++i) f.c[i] = *(const v4i *)(src + 16 * i);
+  f.s0 = f.s1 = 0u;
   f.rs = a.win_row_scale ? a.win_row_scale[wr] : 1.f;
+  f.tag = wr;
   f.kind = ok ? 2 : 0;
 }
 
-// B operand of step ks: channels 128 kq + 8 ks + [0, 8) of the lane's row.
+__device__ __forceinline__ void seg_fetch_rows(const AttendArgs &a, int64_t y, int64_t u_end, int32_t U,
+                                               int prow, int kq, const SegFetch &fe, SegSlice &s) {
+  // a position with no row still feeds the R tile: zeros, never stale registers
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s.c[i] = (v4i){0, 0, 0, 0};
+  s.s0 = s.s1 = 0u;
+  s.kind = 0;
+  s.rs = 1.f;
+  s.tag = 0;
+  if (y >= u_end) return;
+  const int32_t r = (int32_t)(y / U), j = (int32_t)(y % U);
+  const int32_t pos = j * AS_UNIT + prow;
+  const int32_t kw = seg_kw(a.k);
+  if (j * AS_UNIT + (prow & ~15) < kw) {  // entry wave
+    seg_load_entry(a, fe.id, fe.page, kq, s);
+    if (pos >= a.k) s.kind = 0;
+    return;
+  }
+  if (!a.win_codes) return;  // no window
+  const int b = r / a.nq;
+  int32_t wf, wl;
+  window_range(a, r, b, wf, wl);
+  const int32_t jw = wf + (pos - kw);
+  seg_load_window(a, b, jw, pos < kw + a.win_cap && jw <= wl, kq, s);
+}
+
+// B operand of step KS from an entry: code word KS, scale of group KS / 2
+// (the eight group scales of the lane's quarter, converted to fp16 in pairs)
 template <int KS>
-__device__ __forceinline__ v8h entry_operand(const Slice &f) {
-  const uint32_t word = (uint32_t)f.c[KS / 4][KS % 4];
-  const uint32_t sw = (uint32_t)f.c[4][KS / 8];
-  const _Float16 s = (_Float16)e4m3_to_f32((sw >> (8 * ((KS / 2) % 4))) & 0xFFu);
-  return fp4x8_dequant(word, s);
+__device__ __forceinline__ v8h seg_entry_operand(const SegSlice &f, const v2h *sc) {
+  return fp4x8_dequant((uint32_t)f.c[KS / 4][KS % 4], sc[KS / 4][(KS / 2) % 2]);
 }
 
 template <int KS>
-__device__ __forceinline__ v8h window_operand(const Slice &f) {
-  const v4h h0 = e4m3x4_to_f16((uint32_t)f.c[(2 * KS) / 4][(2 * KS) % 4]);
-  const v4h h1 = e4m3x4_to_f16((uint32_t)f.c[(2 * KS + 1) / 4][(2 * KS + 1) % 4]);
+__device__ __forceinline__ v8h seg_window_operand(const SegSlice &f, const v4i *h2) {
+  uint32_t w0, w1;
+  if constexpr (KS < 8) {
+    w0 = (uint32_t)f.c[(2 * KS) / 4][(2 * KS) % 4];
+    w1 = (uint32_t)f.c[(2 * KS + 1) / 4][(2 * KS + 1) % 4];
+  } else {
+    w0 = (uint32_t)h2[(2 * KS - 16) / 4][(2 * KS - 16) % 4];
+    w1 = (uint32_t)h2[(2 * KS - 15) / 4][(2 * KS - 15) % 4];
+  }
+  const v4h h0 = e4m3x4_to_f16(w0), h1 = e4m3x4_to_f16(w1);
   const v8h r = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
   return r;
 }
 
-template <int KS, int KIND>
-__device__ __forceinline__ v8h slice_operand(const Slice &f) {
-  if constexpr (KIND == SPLIT_ENTRIES) return entry_operand<KS>(f);
-  if constexpr (KIND == SPLIT_WINDOW) return window_operand<KS>(f);
-  return (f.kind == 2) ? window_operand<KS>(f) : entry_operand<KS>(f);
+// S = Q R^T for the wave's 16 rows of the unit; the dequantised rows also go
+// to the R tile. No barrier inside: entry or window is uniform per wave.
+template <int KIND>
+__device__ __forceinline__ void seg_qk(const AttendArgs &a, const SegShared &sh, const SegSlice &f, const SegQ &q,
+                                       _Float16 *rtile, int prow, int n, int kq, v4f *acc) {
+  v4i h2[4];
+  if constexpr (KIND == SPLIT_WINDOW) {
+    if (a.win_codes) {
+      const int32_t wr = (f.kind == 2) ? f.tag : 0;
+      const uint8_t *src = a.win_codes + (int64_t)wr * CSA2_D + kq * 128 + 64;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) h2[i] = *(const v4i *)(src + 16 * i);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) h2[i] = (v4i){0, 0, 0, 0};
+    }
+  }
+  // byte offset of the lane's chunk 0 in the R tile (row prow, block kq), swizzled
+  const uint32_t rbase = (uint32_t)(prow * AS_RPITCH * 2 + kq * 256 + 16 * seg_rswz(prow));
+#if SEG_QLO_LDS
+  const _Float16 *qlo = &sh.qlo[n * AT_PITCH + kq * 128];
+#define CSA2_QLO(KS) (*(const v8h *)(qlo + 8 * (KS)))
+#else
+#define CSA2_QLO(KS) (q.ql[KS])
+#endif
+  v2h sc[4];
+  if constexpr (KIND == SPLIT_ENTRIES) {
+    sc[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(f.s0, 1.0f, false);
+    sc[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(f.s0, 1.0f, true);
+    sc[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(f.s1, 1.0f, false);
+    sc[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(f.s1, 1.0f, true);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = (v4f){0.f, 0.f, 0.f, 0.f};
+#define CSA2_SEG_STEP(KS)                                                                              \
+  {                                                                                                    \
+    v8h bop;                                                                                           \
+    if constexpr (KIND == SPLIT_ENTRIES) bop = seg_entry_operand<KS>(f, sc);                           \
+    else bop = seg_window_operand<KS>(f, h2);                                                          \
+    *(v8h *)(rtile + ((rbase ^ (16 * (KS))) >> 1)) = bop;                                              \
+    acc[(KS) & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(q.qa[KS], bop, acc[(KS) & 1], 0, 0, 0);      \
+    acc[2 + ((KS) & 1)] = __builtin_amdgcn_mfma_f32_16x16x32_f16(CSA2_QLO(KS), bop, acc[2 + ((KS) & 1)], 0, 0, 0); \
+  }
+  CSA2_SEG_STEP(0) CSA2_SEG_STEP(1) CSA2_SEG_STEP(2) CSA2_SEG_STEP(3)
+  CSA2_SEG_STEP(4) CSA2_SEG_STEP(5) CSA2_SEG_STEP(6) CSA2_SEG_STEP(7)
+  CSA2_SEG_STEP(8) CSA2_SEG_STEP(9) CSA2_SEG_STEP(10) CSA2_SEG_STEP(11)
+  CSA2_SEG_STEP(12) CSA2_SEG_STEP(13) CSA2_SEG_STEP(14) CSA2_SEG_STEP(15)
+#undef CSA2_SEG_STEP
+#undef CSA2_QLO
 }
 
-// Q (hi, lo) is staged in LDS only until every lane holds its operands in
-// registers; the R tile then reuses that space.
-struct AttShared {
-  union {
-    struct {
-      _Float16 q[CSA2_H * AT_PITCH];
-      _Float16 qlo[CSA2_H * AT_PITCH];
-    };
-    _Float16 r[AT_ROWS * AT_PITCH];
-  };
-  _Float16 p[CSA2_H * AT_PPITCH];
-  float wmax[4][CSA2_H], wsum[4][CSA2_H];
-  float m[CSA2_H], l[CSA2_H], qexp[CSA2_H];
-};
-
-// Q of one query row: per-head power-of-two normalisation, fp16 hi + lo,
-// staged in LDS and then held in registers as the A operands of every step
-// (step ks: head n, channels 128 g + 8 ks + [0, 8)). qv: this thread's 32
-// fp32 values (head tid / 16, channels 32 (tid % 16) + [0, 32)).
-struct QOps {
-  v8h qa[16], ql[16];
-  float qs[4];  // logit scale (sm_scale * log2 e * 2^e) of heads 4g + i
-};
-
-__device__ __forceinline__ void prepare_q(const AttendArgs &a, AttShared &sh, const float *qv, QOps &q) {
+// Q of row r into the A operands (threads of waves 0-3 convert, all read).
+__device__ __forceinline__ void seg_prepare_q(const AttendArgs &a, SegShared &sh, const float *qv, SegQ &q) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int n = lane & 15, g = lane >> 4;
-  {
+  if (tid < 256) {  // waves 0-3
     const int h = tid >> 4, part = tid & 15;
     float mx = 0.f;
 #pragma unroll
     for (int i = 0; i < 32; ++i) mx = fmaxf(mx, fabsf(qv[i]));
-    mx = row16_max(mx);  // the 16 threads of head h are one row of lanes
+    mx = row16_max(mx);
     int e = 0;
-    if (mx > 0.f) frexpf(mx, &e);  // mx = f * 2^e, f in [0.5, 1)
+    if (mx > 0.f) frexpf(mx, &e);
     const float sc = ldexpf(1.f, -e);
 #pragma unroll
     for (int i = 0; i < 32; i += 8) {
@@ -179,401 +343,299 @@ __device__ __forceinline__ void prepare_q(const AttendArgs &a, AttShared &sh, co
 #pragma unroll
   for (int ks = 0; ks < 16; ++ks) {
     q.qa[ks] = *(const v8h *)&sh.q[n * AT_PITCH + g * 128 + 8 * ks];
+#if !SEG_QLO_LDS
     q.ql[ks] = *(const v8h *)&sh.qlo[n * AT_PITCH + g * 128 + 8 * ks];
+#endif
   }
   __syncthreads();  // the R tile overwrites the staged Q
 }
 
-__device__ __forceinline__ void load_q(const AttendArgs &a, int r, float *qv) {
+__device__ __forceinline__ void seg_load_q(const AttendArgs &a, int r, float *qv) {
   const int tid = threadIdx.x;
-  const float *src = a.q + ((int64_t)r * CSA2_H + (tid >> 4)) * CSA2_D + (tid & 15) * 32;
-#pragma unroll
-  for (int i = 0; i < 32; i += 4) {
-    const v4f x = *(const v4f *)(src + i);
-    qv[i] = x[0];
-    qv[i + 1] = x[1];
-    qv[i + 2] = x[2];
-    qv[i + 3] = x[3];
-  }
+  if (tid >= 256) return;  // uniform per wave
+  load_q(a, r, qv);
 }
 
-// One 64-row tile: S = Q R^T for the wave's 16 rows (the same operands fill
-// the R tile), the online-softmax update, and O = O * alpha + P R with the
-// wave owning output channels 128 wave .. +127.
-template <int KIND>
-__device__ __forceinline__ void attend_tile(AttShared &sh, const Slice &sl, const QOps &q, v4f *accO) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// One unit: QK for the waves' 16 rows each, online softmax over the 128 rows,
+// O = O * alpha + P R with wave w owning output channels 64 w .. 64 w + 63.
+__device__ __forceinline__ void seg_unit(const AttendArgs &a, SegShared &sh, int32_t pos0, int32_t nent,
+                                         const SegSlice &f, const SegQ &q, v4f *accO) {
+  // lane indices and LDS addresses are recomputed per unit from an opaque copy
+  // of the thread id instead of being kept live across the loop
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
-  const int trow = wave * 16 + n;
+  const int prow = wave * 16 + n;
   v4f acc[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) acc[i] = (v4f){0.f, 0.f, 0.f, 0.f};
-  _Float16 *rrow = &sh.r[trow * AT_PITCH + g * 128];
-#define CSA2_QK_STEP(KS)                                                                              \
-  {                                                                                                   \
-    const v8h bop = slice_operand<KS, KIND>(sl);                                                      \
-    *(v8h *)(rrow + 8 * (KS)) = bop;                                                                  \
-    acc[(KS) & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(q.qa[KS], bop, acc[(KS) & 1], 0, 0, 0);     \
-    acc[2 + ((KS) & 1)] = __builtin_amdgcn_mfma_f32_16x16x32_f16(q.ql[KS], bop, acc[2 + ((KS) & 1)], 0, 0, 0); \
-  }
-  CSA2_QK_STEP(0) CSA2_QK_STEP(1) CSA2_QK_STEP(2) CSA2_QK_STEP(3)
-  CSA2_QK_STEP(4) CSA2_QK_STEP(5) CSA2_QK_STEP(6) CSA2_QK_STEP(7)
-  CSA2_QK_STEP(8) CSA2_QK_STEP(9) CSA2_QK_STEP(10) CSA2_QK_STEP(11)
-  CSA2_QK_STEP(12) CSA2_QK_STEP(13) CSA2_QK_STEP(14) CSA2_QK_STEP(15)
-#undef CSA2_QK_STEP
-  // lane holds S[head 4g + i][row n]
-  const bool valid = sl.kind != 0;
-  const float rs = sl.rs;
+  if (pos0 + wave * 16 < seg_kw(a.k))  // uniform per wave
+    seg_qk<SPLIT_ENTRIES>(a, sh, f, q, sh.r, prow, n, g, acc);
+  else
+    seg_qk<SPLIT_WINDOW>(a, sh, f, q, sh.r, prow, n, g, acc);
+  // lane holds S[head 4g + i][row prow]
+  const bool valid = (f.kind == 2) || (f.kind == 1 && f.tag < nent);
+  const float rs = f.rs;
   float z[4], mx[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const float sv = (acc[0][i] + acc[1][i]) + (acc[2][i] + acc[3][i]);
     z[i] = valid ? sv * q.qs[i] * rs : -INFINITY;
-    mx[i] = row16_max(z[i]);  // over the wave's 16 rows
+    mx[i] = z[i];
   }
+  // maxima over the wave's 16 rows, the four heads' reductions interleaved
+#pragma unroll
+  for (int i = 0; i < 4; ++i) mx[i] = fmax_nc(mx[i], dpp_f32<0xB1>(mx[i]));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) mx[i] = fmax_nc(mx[i], dpp_f32<0x4E>(mx[i]));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) mx[i] = fmax_nc(mx[i], dpp_f32<0x141>(mx[i]));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) mx[i] = fmax_nc(mx[i], dpp_f32<0x140>(mx[i]));
   if (n == 0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sh.wmax[wave][4 * g + i] = mx[i];
+    for (int i = 0; i < 4; ++i) sh.wmax[4 * g + i][wave] = mx[i];
   }
   __syncthreads();  // R tile and the waves' maxima are in LDS
-  float alpha[4];
+  // running maximum after this unit; a head with no finite logit yet keeps
+  // reference 0 (its exponentials are all 0 and its state is empty)
+  float alpha[4], mref[4], pv[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int h = 4 * g + i;
+    const v4f w0 = *(const v4f *)&sh.wmax[h][0], w1 = *(const v4f *)&sh.wmax[h][4];
     const float m_old = sh.m[h];
-    const float m_new =
-        fmaxf(fmaxf(m_old, fmaxf(sh.wmax[0][h], sh.wmax[1][h])), fmaxf(sh.wmax[2][h], sh.wmax[3][h]));
-    alpha[i] = (m_new == -INFINITY) ? 1.f : ((m_old == -INFINITY) ? 0.f : exp2f(m_old - m_new));
-    const float pv = (z[i] == -INFINITY) ? 0.f : exp2f(z[i] - m_new);
-    const float ps = row16_sum(pv);
-    if (n == 0) sh.wsum[wave][h] = ps;
-    sh.p[h * AT_PPITCH + trow] = (_Float16)(pv * rs);
+    const float m_new = fmax_nc(fmax_nc(fmax_nc(m_old, fmax_nc(w0[0], w0[1])), fmax_nc(fmax_nc(w0[2], w0[3]), fmax_nc(w1[0], w1[1]))),
+                                fmax_nc(w1[2], w1[3]));
+    mref[i] = (m_new == -INFINITY) ? 0.f : m_new;
+    alpha[i] = __builtin_amdgcn_exp2f(m_old - mref[i]);  // 0 while m_old is -inf
+    pv[i] = __builtin_amdgcn_exp2f(z[i] - mref[i]);      // 0 for an invalid row
+  }
+  float ps[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) ps[i] = pv[i] + dpp_f32<0xB1>(pv[i]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) ps[i] += dpp_f32<0x4E>(ps[i]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) ps[i] += dpp_f32<0x141>(ps[i]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) ps[i] += dpp_f32<0x140>(ps[i]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int h = 4 * g + i;
+    if (n == 0) sh.wsum[h][wave] = ps[i];
+    sh.p[h * AS_PPITCH + prow] = (_Float16)(pv[i] * rs);
   }
   __syncthreads();  // P and the row sums are in LDS; every read of m is done
   if (tid < CSA2_H) {
+    const v4f w0 = *(const v4f *)&sh.wmax[tid][0], w1 = *(const v4f *)&sh.wmax[tid][4];
+    const v4f s0 = *(const v4f *)&sh.wsum[tid][0], s1 = *(const v4f *)&sh.wsum[tid][4];
     const float m_old = sh.m[tid];
-    const float m_new =
-        fmaxf(fmaxf(m_old, fmaxf(sh.wmax[0][tid], sh.wmax[1][tid])), fmaxf(sh.wmax[2][tid], sh.wmax[3][tid]));
-    const float al = (m_new == -INFINITY) ? 1.f : ((m_old == -INFINITY) ? 0.f : exp2f(m_old - m_new));
-    sh.l[tid] = sh.l[tid] * al + ((sh.wsum[0][tid] + sh.wsum[1][tid]) + (sh.wsum[2][tid] + sh.wsum[3][tid]));
+    const float m_new = fmax_nc(fmax_nc(fmax_nc(m_old, fmax_nc(w0[0], w0[1])), fmax_nc(fmax_nc(w0[2], w0[3]), fmax_nc(w1[0], w1[1]))),
+                                fmax_nc(w1[2], w1[3]));
+    const float mr = (m_new == -INFINITY) ? 0.f : m_new;
+    const float sum = ((s0[0] + s0[1]) + (s0[2] + s0[3])) + ((s1[0] + s1[1]) + (s1[2] + s1[3]));
+    sh.l[tid] = sh.l[tid] * __builtin_amdgcn_exp2f(m_old - mr) + sum;
     sh.m[tid] = m_new;
   }
   {
     const int c = n >> 2, rq = n & 3;
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
+    for (int nt = 0; nt < 4; ++nt) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) accO[nt][i] *= alpha[i];
     }
+    // lane reads channels n0 + 4 rq .. + 3 of rows 32 kstep + 8 g + c (+ 4):
+    // chunk (8 wave + 2 nt + rq / 2) of the row, swizzled, half rq % 2
+    const uint32_t cb = (uint32_t)((8 * wave) | (rq >> 1));
+    const uint32_t a0 = (uint32_t)((8 * g + c) * AS_RPITCH * 2 + 8 * (rq & 1)) + 16 * (cb ^ seg_rswz(8 * g + c));
+    const uint32_t a1 = (uint32_t)((8 * g + 4 + c) * AS_RPITCH * 2 + 8 * (rq & 1)) + 16 * (cb ^ seg_rswz(8 * g + 4 + c));
 #pragma unroll
-    for (int kstep = 0; kstep < 2; ++kstep) {
-      const v8h pa = *(const v8h *)&sh.p[n * AT_PPITCH + 32 * kstep + 8 * g];
-      v4s t0v[8], t1v[8];
+    for (int kstep = 0; kstep < 4; ++kstep) {
+      const v8h pa = *(const v8h *)&sh.p[n * AS_PPITCH + 32 * kstep + 8 * g];
+      v4s t0v[4], t1v[4];
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt) {
-        const int n0 = wave * 128 + nt * 16;
-        const _Float16 *base0 = &sh.r[(32 * kstep + 8 * g + c) * AT_PITCH + n0 + 4 * rq];
-        const _Float16 *base1 = &sh.r[(32 * kstep + 8 * g + 4 + c) * AT_PITCH + n0 + 4 * rq];
-        t0v[nt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(base0));
-        t1v[nt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(base1));
+      for (int nt = 0; nt < 4; ++nt) {
+        const uint32_t o0 = (a0 ^ (32u * nt)) + 32u * AS_RPITCH * 2 * kstep;
+        const uint32_t o1 = (a1 ^ (32u * nt)) + 32u * AS_RPITCH * 2 * kstep;
+        t0v[nt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(sh.r + (o0 >> 1)));
+        t1v[nt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(sh.r + (o1 >> 1)));
       }
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt) {
-        // whole-vector bit casts only: this clang mistranslates a bit cast of
-        // a single vector element (it reads element 0)
+      for (int nt = 0; nt < 4; ++nt) {
         const v4h h0 = __builtin_bit_cast(v4h, t0v[nt]), h1 = __builtin_bit_cast(v4h, t1v[nt]);
         const v8h rb = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
         accO[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, rb, accO[nt], 0, 0, 0);
       }
     }
   }
-  __syncthreads();  // the R tile and P are free for the next tile
+  __syncthreads();  // the R tile and P are free for the next unit
 }
 
-// Window geometry of query row r: rows w_first..w_last of its request's window.
-__device__ __forceinline__ void window_range(const AttendArgs &a, int r, int b, int32_t &w_first,
-                                             int32_t &w_last) {
-  w_first = 0;
-  w_last = -1;
-  if (!a.win_codes) return;
-  const int32_t len = a.win_len[b];
-  if (a.win_pos0) {
-    const int32_t pq = a.q_pos ? a.q_pos[r] : 0x7FFFFFFF;
-    const int64_t rel = (int64_t)pq - a.win_pos0[b];
-    w_first = (int32_t)max((int64_t)0, rel - a.win_window + 1);
-    w_last = (int32_t)min(min((int64_t)len, (int64_t)a.win_rows) - 1, rel);
-  } else {
-    w_last = min(len, a.win_rows) - 1;
-  }
-}
-
-template <int NT, int KIND>
-__device__ __forceinline__ void attend_split(const AttendArgs &a, AttShared &sh, int r, int b, int split,
-                                             int32_t p0, int32_t p1, int32_t nent, int32_t w_first,
-                                             int32_t w_last) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n = lane & 15, g = lane >> 4;  // row of the wave's 16 / channel quarter; head group in C
-  const int trow = wave * 16 + n;          // this lane's row inside a tile
-
-  // ---- every global load of the split first: Q, then the rows level by level ----
-  float qv[32];
-  load_q(a, r, qv);
-  Slice sl[NT];
-  if constexpr (KIND == SPLIT_WINDOW) {
-#pragma unroll
-    for (int ti = 0; ti < NT; ++ti) {
-      const int32_t pos = p0 + ti * AT_ROWS + trow;
-      const int32_t j = w_first + (pos - a.k);
-      load_window(a, b, j, pos < p1 && j <= w_last, g, sl[ti]);
-    }
-  } else {
-    int32_t idv[NT], pgv[NT];
-    const int32_t nent_c = max(nent, 1);
-#pragma unroll
-    for (int ti = 0; ti < NT; ++ti) {
-      const int32_t pos = min(p0 + ti * AT_ROWS + trow, min(p1, a.k) - 1);
-      idv[ti] = a.idx[(int64_t)r * a.k + pos];
-    }
-#pragma unroll
-    for (int ti = 0; ti < NT; ++ti) {
-      const int32_t pg = min(min(max(idv[ti], 0), nent_c - 1) >> a.c.page_shift, a.c.max_pages - 1);
-      pgv[ti] = a.c.block_table[(int64_t)b * a.c.max_pages + pg];
-    }
-#pragma unroll
-    for (int ti = 0; ti < NT; ++ti) {
-      const int32_t pos = p0 + ti * AT_ROWS + trow;
-      if constexpr (KIND == SPLIT_ENTRIES) {
-        load_entry(a, idv[ti], pgv[ti], pos < p1, nent, g, sl[ti]);
-      } else {
-        // a lane reads an entry or a window row; both paths are issued
-        Slice e, wr;
-        load_entry(a, idv[ti], pgv[ti], pos < p1 && pos < a.k, nent, g, e);
-        const int32_t j = w_first + (pos - a.k);
-        load_window(a, b, j, pos < p1 && pos >= a.k && j <= w_last, g, wr);
-        sl[ti] = (pos < a.k) ? e : wr;
-      }
-    }
-  }
-  QOps q;
-  prepare_q(a, sh, qv, q);
-
-  v4f accO[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) accO[i] = (v4f){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int ti = 0; ti < NT; ++ti) {
-    if (p0 + ti * AT_ROWS >= p1) break;  // uniform
-    attend_tile<KIND>(sh, sl[ti], q, accO);
-  }
-
-  // ---- write this split's partial state ----
-  float *part = a.part + ((int64_t)r * a.n_split + split) * CSA2_H * kPartStride;
-#pragma unroll
-  for (int nt = 0; nt < 8; ++nt) {
-    const int ch = wave * 128 + nt * 16 + n;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) part[(4 * g + i) * kPartStride + ch] = accO[nt][i];
-  }
-  if (tid < CSA2_H) {
-    part[tid * kPartStride + CSA2_D] = sh.m[tid];
-    part[tid * kPartStride + CSA2_D + 1] = sh.l[tid];
-  }
-}
-
-template <int NT>
-__global__ __launch_bounds__(256) void k_attend(AttendArgs a) {
-  __shared__ __attribute__((aligned(16))) AttShared sh;
-  const int r = blockIdx.y, split = blockIdx.x;
-  const int b = r / a.nq;
-  const int32_t total_pos = a.k + a.win_cap;
-  const int32_t p0 = split * (NT * AT_ROWS);
-  const int32_t p1 = min(p0 + NT * AT_ROWS, total_pos);
-  const int32_t nent = a.c.n_entries[b];
-  int32_t w_first, w_last;
-  window_range(a, r, b, w_first, w_last);
-  // a split holds only selected entries, only window rows, or both
-  if (p1 <= a.k)
-    attend_split<NT, SPLIT_ENTRIES>(a, sh, r, b, split, p0, p1, nent, w_first, w_last);
-  else if (p0 >= a.k)
-    attend_split<NT, SPLIT_WINDOW>(a, sh, r, b, split, p0, p1, nent, w_first, w_last);
-  else
-    attend_split<NT, SPLIT_MIXED>(a, sh, r, b, split, p0, p1, nent, w_first, w_last);
-}
-
-// ---- one workgroup per query row, all tiles in turn ----------------------------------
-// For calls with many query rows (a prefill chunk): no split partials and no
-// merge; the row's tiles run in sequence, each tile's rows loaded while the
-// previous tile computes (ids three tiles ahead, block-table words two
-// ahead), and the workgroup writes out and lse itself.
-struct TileFetch {
-  int32_t id, page;
-};
-
-__device__ __forceinline__ int tile_kind(const AttendArgs &a, int t) {
-  const int32_t t0 = t * AT_ROWS;
-  return (t0 + AT_ROWS <= a.k) ? SPLIT_ENTRIES : (t0 >= a.k ? SPLIT_WINDOW : SPLIT_MIXED);
-}
-
-__device__ __forceinline__ int32_t fetch_id(const AttendArgs &a, int r, int t, int T, int trow) {
-  if (t >= T || t * AT_ROWS >= a.k) return 0;  // uniform: no entries in this tile
-  const int32_t pos = min(t * AT_ROWS + trow, a.k - 1);
-  return a.idx[(int64_t)r * a.k + pos];
-}
-
-__device__ __forceinline__ int32_t fetch_page(const AttendArgs &a, int b, int32_t id, int32_t nent) {
-  const int32_t pg = min(min(max(id, 0), max(nent, 1) - 1) >> a.c.page_shift, a.c.max_pages - 1);
-  return a.c.block_table[(int64_t)b * a.c.max_pages + pg];
-}
-
-__device__ __forceinline__ void fetch_rows(const AttendArgs &a, int b, int t, int T, int trow, int g,
-                                           const TileFetch &tf, int32_t nent, int32_t total_pos,
-                                           int32_t w_first, int32_t w_last, Slice &sl) {
-  if (t >= T) return;  // uniform
-  const int32_t pos = t * AT_ROWS + trow;
-  const int kind = tile_kind(a, t);
-  if (kind == SPLIT_ENTRIES) {
-    load_entry(a, tf.id, tf.page, pos < total_pos, nent, g, sl);
-  } else if (kind == SPLIT_WINDOW) {
-    const int32_t j = w_first + (pos - a.k);
-    load_window(a, b, j, pos < total_pos && j <= w_last, g, sl);
-  } else {
-    Slice e, wr;
-    load_entry(a, tf.id, tf.page, pos < a.k, nent, g, e);
-    const int32_t j = w_first + (pos - a.k);
-    load_window(a, b, j, pos < total_pos && pos >= a.k && j <= w_last, g, wr);
-    sl = (pos < a.k) ? e : wr;
-  }
-}
-
-__global__ __launch_bounds__(256) void k_attend_row(AttendArgs a, float *out, float *lse) {
-  __shared__ __attribute__((aligned(16))) AttShared sh;
-  const int r = blockIdx.x;
-  const int b = r / a.nq;
+// Row `row` is done in this workgroup: write it whole (normalised, with its
+// lse), or leave its partial (unnormalised O, running max, running sum). The
+// state goes through LDS (the R tile is free after the unit's last barrier) so
+// that the stores are whole 16-byte vectors along each head's row.
+__device__ __forceinline__ void seg_finish(const AttendArgs &a, const SegArgs &s, SegShared &sh, int w,
+                                           int32_t row, int32_t first_row, int64_t u_begin, int64_t u_end,
+                                           const v4f *accO) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
-  const int trow = wave * 16 + n;
-  const int32_t total_pos = a.k + a.win_cap;
-  const int T = (total_pos + AT_ROWS - 1) / AT_ROWS;
-  const int32_t nent = a.c.n_entries[b];
-  int32_t w_first, w_last;
-  window_range(a, r, b, w_first, w_last);
-
-  float qv[32];
-  load_q(a, r, qv);
-  // ids three tiles ahead, block-table words two ahead, rows one ahead
-  TileFetch f0, f1, f2;
-  f0.id = fetch_id(a, r, 0, T, trow);
-  f1.id = fetch_id(a, r, 1, T, trow);
-  f2.id = fetch_id(a, r, 2, T, trow);
-  f0.page = fetch_page(a, b, f0.id, nent);
-  f1.page = fetch_page(a, b, f1.id, nent);
-  Slice cur, nxt;
-  cur.kind = 0;
-  cur.rs = 1.f;
-  fetch_rows(a, b, 0, T, trow, g, f0, nent, total_pos, w_first, w_last, cur);
-  QOps q;
-  prepare_q(a, sh, qv, q);
-
-  v4f accO[8];
+  float *stage = (float *)sh.r;  // [16][kPartStride]
 #pragma unroll
-  for (int i = 0; i < 8; ++i) accO[i] = (v4f){0.f, 0.f, 0.f, 0.f};
-  for (int t = 0; t < T; ++t) {
-    nxt.kind = 0;
-    nxt.rs = 1.f;
-    fetch_rows(a, b, t + 1, T, trow, g, f1, nent, total_pos, w_first, w_last, nxt);
-    f2.page = fetch_page(a, b, f2.id, nent);
-    const int32_t id3 = fetch_id(a, r, t + 3, T, trow);
-    const int kind = tile_kind(a, t);  // uniform
-    if (kind == SPLIT_ENTRIES)
-      attend_tile<SPLIT_ENTRIES>(sh, cur, q, accO);
-    else if (kind == SPLIT_WINDOW)
-      attend_tile<SPLIT_WINDOW>(sh, cur, q, accO);
-    else
-      attend_tile<SPLIT_MIXED>(sh, cur, q, accO);
-    cur = nxt;
-    f1 = f2;
-    f2.id = id3;
-  }
-
-  // ---- normalise and write the row's output ----
-  float inv[4];
+  for (int nt = 0; nt < 4; ++nt) {
+    const int ch = wave * 64 + nt * 16 + n;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float l = sh.l[4 * g + i];
-    inv[i] = (l > 0.f) ? 1.f / l : 0.f;
-  }
-#pragma unroll
-  for (int nt = 0; nt < 8; ++nt) {
-    const int ch = wave * 128 + nt * 16 + n;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) out[((int64_t)r * CSA2_H + 4 * g + i) * CSA2_D + ch] = accO[nt][i] * inv[i];
+    for (int i = 0; i < 4; ++i) stage[(4 * g + i) * kPartStride + ch] = accO[nt][i];
   }
   if (tid < CSA2_H) {
-    const float l = sh.l[tid];
-    lse[(int64_t)r * CSA2_H + tid] = (l > 0.f) ? (sh.m[tid] + log2f(l)) * 0.6931471805599453f : -INFINITY;
+    stage[tid * kPartStride + CSA2_D] = sh.m[tid];
+    stage[tid * kPartStride + CSA2_D + 1] = sh.l[tid];
+  }
+  __syncthreads();
+  const int64_t r0 = (int64_t)row * s.U;
+  if (r0 >= u_begin && r0 + s.U <= u_end) {
+    // 16 x 512 outputs as 2048 float4, four per thread
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int v = tid + 512 * j, h = v >> 7, c = (v & 127) * 4;
+      const float l = stage[h * kPartStride + CSA2_D + 1];
+      const float inv = (l > 0.f) ? 1.f / l : 0.f;
+      const v4f o = *(const v4f *)&stage[h * kPartStride + c];
+      *(v4f *)&s.out[((int64_t)row * CSA2_H + h) * CSA2_D + c] = o * inv;
+    }
+    if (tid < CSA2_H) {
+      const float l = stage[tid * kPartStride + CSA2_D + 1];
+      s.lse[(int64_t)row * CSA2_H + tid] =
+          (l > 0.f) ? (stage[tid * kPartStride + CSA2_D] + log2f(l)) * 0.6931471805599453f : -INFINITY;
+    }
+  } else {
+    const int slot = (row == first_row) ? 0 : 1;
+    float *part = a.part + ((int64_t)w * 2 + slot) * CSA2_H * kPartStride;
+    // 16 x 516 floats as 2064 float4
+    for (int v = tid; v < CSA2_H * kPartStride / 4; v += 512)
+      *(v4f *)&part[4 * v] = *(const v4f *)&stage[4 * v];
   }
 }
 
-// Combine split partials of one (row, head): out = sum_s 2^(m_s - M) O_s /
-// sum_s 2^(m_s - M) l_s, one thread per channel. Splits are read 32 at a time
-// (all loads in flight together) and folded into a running maximum.
-__global__ __launch_bounds__(512) void k_merge(MergeArgs a) {
-  constexpr int BATCH = 32;
-  const int h = blockIdx.x, r = blockIdx.y, c = threadIdx.x;
-  const float *base = a.part + (int64_t)r * a.n_split * CSA2_H * kPartStride + (int64_t)h * kPartStride;
-  const int64_t sstride = (int64_t)CSA2_H * kPartStride;
-  float M = -INFINITY, L = 0.f, o = 0.f;
-  for (int s0 = 0; s0 < a.n_split; s0 += BATCH) {
-    const int cnt = min(BATCH, a.n_split - s0);
-    float mv[BATCH], lv[BATCH], ov[BATCH];
+__global__ __launch_bounds__(512) void k_attend_seg(AttendArgs a, SegArgs s) {
+  __shared__ __attribute__((aligned(16))) SegShared sh;
+  const int w = blockIdx.x;
+  const int32_t U = s.U;
+  const int64_t u_begin = (int64_t)w * s.T / s.G, u_end = (int64_t)(w + 1) * s.T / s.G;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, prow = wave * 16 + (lane & 15);
+  const int32_t first_row = (int32_t)(u_begin / U);
+
+  for (int64_t x = u_begin; x < u_end;) {
+    // one row's units [x, xe): Q first, then the pipeline's prologue
+    const int32_t row = (int32_t)(x / U);
+    const int64_t xe = min(u_end, (int64_t)(row + 1) * U);
+    // Q loads first, then the ids of the first three units; Q is converted
+    // while the ids are in flight (loads complete in issue order)
+    SegQ q;
+    SegFetch fc, fn;
+    int32_t id2;
+    {
+      float qv[32];
+      seg_load_q(a, row, qv);
+      fc.id = seg_fetch_id(a, x, xe, U, prow);
+      fn.id = seg_fetch_id(a, x + 1, xe, U, prow);
+      id2 = seg_fetch_id(a, x + 2, xe, U, prow);
+      seg_prepare_q(a, sh, qv, q);
+    }
+    // pipeline: rows of unit x in sc, id and page word of x + 1 in fn, id of x + 2 in id2
+    fc.page = seg_fetch_page(a, x, xe, U, prow, fc.id);
+    fn.page = seg_fetch_page(a, x + 1, xe, U, prow, fn.id);
+    SegSlice sc;
+    seg_fetch_rows(a, x, xe, U, prow, g, fc, sc);
+    const int32_t nent = a.c.n_entries[row / a.nq];
+    v4f accO[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) accO[i] = (v4f){0.f, 0.f, 0.f, 0.f};
+    for (; x < xe; ++x) {
+      // rows of x + 1, page word of x + 2 and id of x + 3 load while unit x computes
+      SegSlice sn;
+      seg_fetch_rows(a, x + 1, xe, U, prow, g, fn, sn);
+      const int32_t pg2 = seg_fetch_page(a, x + 2, xe, U, prow, id2);
+      const int32_t id3 = seg_fetch_id(a, x + 3, xe, U, prow);
+      seg_unit(a, sh, (int32_t)(x % U) * AS_UNIT, nent, sc, q, accO);
+      sc = sn;
+      fn.id = id2;
+      fn.page = pg2;
+      id2 = id3;
+    }
+    seg_finish(a, s, sh, w, row, first_row, u_begin, u_end, accO);
+    __syncthreads();  // m and l are read before the next row resets them
+  }
+}
+
+// Combine the partials of rows cut between workgroups of k_attend_seg (rows
+// written whole are skipped). Workgroup w's partial for row r sits in slot 0
+// when r is the first row of w's range, else in slot 1. One workgroup per
+// (head, row), four channels per thread; BATCH partials are loaded together.
+template <int BATCH>
+__global__ __launch_bounds__(128) void k_merge_seg(MergeArgs a, SegArgs s) {
+  const int h = blockIdx.x, r = blockIdx.y, t = threadIdx.x;
+  const int64_t u0 = (int64_t)r * s.U, u1 = u0 + s.U - 1;
+  const int32_t first = (int32_t)(((u0 + 1) * s.G + s.T - 1) / s.T - 1);
+  const int32_t last = (int32_t)(((u1 + 1) * s.G + s.T - 1) / s.T - 1);
+  if (first == last) return;  // written whole by its workgroup
+  const int n = last - first + 1;
+  // the first workgroup holds this row in slot 0 only when its range starts in it
+  const int first_slot = ((int64_t)first * s.T / s.G / s.U == r) ? 0 : 1;
+  float M = -INFINITY, L = 0.f;
+  v4f o = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < n; s0 += BATCH) {
+    const int cnt = min(BATCH, n - s0);
+    float mv[BATCH], lv[BATCH];
+    v4f ov[BATCH];
 #pragma unroll
     for (int u = 0; u < BATCH; ++u) {
-      const float *ps = base + (s0 + min(u, cnt - 1)) * sstride;
+      const int wi = s0 + min(u, cnt - 1);
+      const int slot = (wi == 0) ? first_slot : 0;
+      const float *ps = a.part + (((int64_t)(first + wi) * 2 + slot) * CSA2_H + h) * kPartStride;
       mv[u] = ps[CSA2_D];
       lv[u] = ps[CSA2_D + 1];
-      ov[u] = ps[c];
+      ov[u] = *(const v4f *)&ps[4 * t];
     }
-    // repeats of the batch's last split weigh nothing: their max is -inf
+    // repeats of the batch's last partial weigh nothing
 #pragma unroll
     for (int u = 1; u < BATCH; ++u) mv[u] = (u < cnt) ? mv[u] : -INFINITY;
     float bm = M;
 #pragma unroll
     for (int u = 0; u < BATCH; ++u) bm = fmaxf(bm, mv[u]);
     if (bm == -INFINITY) continue;
-    const float f = exp2f(M - bm);  // 0 while M is -inf
+    const float f = __builtin_amdgcn_exp2f(M - bm);  // 0 while M is -inf
     L *= f;
     o *= f;
 #pragma unroll
     for (int u = 0; u < BATCH; ++u) {
-      const float wgt = exp2f(mv[u] - bm);  // 0 for an empty split (m = -inf)
+      const float wgt = __builtin_amdgcn_exp2f(mv[u] - bm);  // 0 for an empty partial
       L += wgt * lv[u];
       o += wgt * ov[u];
     }
     M = bm;
   }
-  a.out[((int64_t)r * CSA2_H + h) * CSA2_D + c] = (L > 0.f) ? o / L : 0.f;
-  if (c == 0)
-    a.lse[(int64_t)r * CSA2_H + h] = (L > 0.f) ? (M + log2f(L)) * 0.6931471805599453f : -INFINITY;
+  const float inv = (L > 0.f) ? 1.f / L : 0.f;
+  *(v4f *)&s.out[((int64_t)r * CSA2_H + h) * CSA2_D + 4 * t] = o * inv;
+  if (t == 0)
+    s.lse[(int64_t)r * CSA2_H + h] = (L > 0.f) ? (M + log2f(L)) * 0.6931471805599453f : -INFINITY;
 }
 
-hipError_t launch_attend_rows(const AttendArgs &a, int rows, float *out, float *lse, hipStream_t st) {
-  hipLaunchKernelGGL(k_attend_row, dim3((unsigned)rows), dim3(256), 0, st, a, out, lse);
-  return hipGetLastError();
-}
-
-hipError_t launch_attend(const AttendArgs &a, int rows, hipStream_t st) {
-  dim3 grid((unsigned)a.n_split, (unsigned)rows);
-  if (a.rows_per_split == 64)
-    hipLaunchKernelGGL(k_attend<1>, grid, dim3(256), 0, st, a);
-  else if (a.rows_per_split == 128)
-    hipLaunchKernelGGL(k_attend<2>, grid, dim3(256), 0, st, a);
+hipError_t launch_attend_seg(const AttendArgs &a, const SegArgs &s, int max_slots, hipStream_t st) {
+  if (s.G < 1 || s.G > kSegMaxWg || s.T < s.G || s.U < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_attend_seg, dim3((unsigned)s.G), dim3(512), 0, st, a, s);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || max_slots < 2) return e;
+  MergeArgs m{};
+  m.part = a.part;
+  const dim3 grid(CSA2_H, (unsigned)(s.T / s.U));
+  if (max_slots <= 8)
+    hipLaunchKernelGGL(k_merge_seg<8>, grid, dim3(128), 0, st, m, s);
+  else if (max_slots <= 16)
+    hipLaunchKernelGGL(k_merge_seg<16>, grid, dim3(128), 0, st, m, s);
   else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
-}
-
-hipError_t launch_merge(const MergeArgs &a, int rows, hipStream_t st) {
-  hipLaunchKernelGGL(k_merge, dim3(CSA2_H, (unsigned)rows), dim3(512), 0, st, a);
+    hipLaunchKernelGGL(k_merge_seg<32>, grid, dim3(128), 0, st, m, s);
   return hipGetLastError();
 }
 

@@ -103,15 +103,20 @@ struct AttendArgs {
   const int32_t *q_pos;
   int32_t nq;
   float sm_scale;
-  int32_t rows_per_split;  // 0: one workgroup per query row, no partials
-  int32_t n_split;
-  float *part;   // [rows][n_split][16][512 + 2]
+  float *part;   // [G][2][16][kPartStride]: partials of rows cut between workgroups
+};
+
+// Attention work split: units of 128 positions (U per row, T = rows * U in
+// all) shared out over G workgroups; out/lse receive the rows.
+constexpr int kSegMaxWg = 256;
+struct SegArgs {
+  int64_t T;
+  int32_t U, G;
+  float *out, *lse;
 };
 
 struct MergeArgs {
   const float *part;
-  int32_t n_split;
-  float *out, *lse;
 };
 
 hipError_t launch_fill_u32(uint32_t *p, int64_t n, uint32_t v, hipStream_t st);
@@ -124,13 +129,13 @@ hipError_t launch_compact(const CompactArgs &a, int rows, hipStream_t st);
 hipError_t launch_final(const FinalArgs &a, int rows, int ntarget, hipStream_t st);
 hipError_t launch_select_direct(const DirectArgs &a, int rows, int ntarget, hipStream_t st);
 hipError_t launch_sort_rows(int32_t *ids, int32_t stride, int32_t T, int rows, hipStream_t st);
-hipError_t launch_attend(const AttendArgs &a, int rows, hipStream_t st);
-hipError_t launch_attend_rows(const AttendArgs &a, int rows, float *out, float *lse, hipStream_t st);
-hipError_t launch_merge(const MergeArgs &a, int rows, hipStream_t st);
+// max_slots: most workgroups sharing one row (2 or more: rows cut between
+// workgroups are combined by a merge pass)
+hipError_t launch_attend_seg(const AttendArgs &a, const SegArgs &s, int max_slots, hipStream_t st);
 hipError_t launch_dequant_fp4(const uint8_t *codes, const uint8_t *scales, int64_t n_rows,
                               int32_t channels, uint16_t *out, hipStream_t st);
 hipError_t launch_dequant_e4m3(const uint8_t *bytes, int64_t n, float *out, hipStream_t st);
 
-constexpr int kPartStride = CSA2_D + 2;  // per head: 512 unnormalised outputs, max, sum
+constexpr int kPartStride = CSA2_D + 4;  // per head: 512 unnormalised outputs, max, sum, 2 pad
 
 }  // namespace csa2
