@@ -8,11 +8,13 @@ in HBM before timing; the step's inputs are rotated over several device
 copies so the 256 MB Infinity Cache cannot hold one step's data for the next.
 The 128K-context workload (batch 32, [Full, Reuse x5]) is timed beside it.
 --workload selects another workload for the JSON line: the 128K one, the
-ragged 64-request 20-layer stack, or the 4096-query prefill chunk (whose
-roofline kernel is the matrix-core scoring, against the fp16 MFMA peak).
+ragged 64-request 20-layer stack, or the 4096-query prefill chunk.
 
-Printed: one JSON line (metric, value = queries/s, roofline of the dominant
-kernel measured live with HIP events, CPU-oracle baseline).
+Printed: one JSON line (metric, value = queries/s, CPU-oracle baseline, and
+rooflines measured live with HIP events: `roofline` for the kernel that takes
+the most step time, the attention call (k_attend_seg and its merge), and
+`roofline_scoring` for the indexer scoring kernel (HBM-bound in decode,
+matrix-core bound in the prefill chunk)).
 """
 
 from __future__ import annotations
@@ -35,6 +37,8 @@ WORKLOAD = "b8_1m_full_reindex_reuse4"
 WORKLOAD_128K = "b32_128k_full_reuse5"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_index_score_b8_1m.json")
 SCORE_SRC = os.path.join(ROOT, "compressed_sparse_attention_06_amd", "csrc", "k_score.hip")
+ATT_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attend_b8_1m.json")
+ATT_SRC = os.path.join(ROOT, "compressed_sparse_attention_06_amd", "csrc", "k_attend.hip")
 
 
 def log(*a):
@@ -105,6 +109,23 @@ def prefill_bytes(wl) -> int:
             K = min(wl.k, N)
             A = 292 * K + wl.window * 512 + 32768 + 32832
             total += (36 * N if L.mode == "F" else 0) + wl.nq * (160 * (L.mode != "U") + A)
+    return total
+
+
+def attend_bytes(wl, li) -> int:
+    """Algorithmic bytes of one attention call of layer li: A(K) per query row
+    (292 B per selected entry incl. its id, the window rows it scans, 32 KB fp32
+    query, 32 KB output + 64 B lse)."""
+    L = wl.layers[li]
+    c = wl.caches[L.cache_id]
+    total = 0
+    for b in range(wl.batch):
+        K = min(wl.k, int(c.n_entries[b]))
+        if wl.q_pos is not None:
+            win = wl.window * (512 + (4 if L.win.row_scale is not None else 0))
+        else:
+            win = int(L.win.length[b]) * (512 + (4 if L.win.row_scale is not None else 0))
+        total += wl.nq * (292 * K + win + 32768 + 32832)
     return total
 
 
@@ -295,6 +316,48 @@ def main():
         k_gbps = kb / (k_ms * 1e-3) / 1e9
         log(f"index_score kernel: {k_ms * 1e3:.2f} us/launch, {k_gbps:.0f} GB/s algorithmic")
 
+    # ---- the dominant kernel by step time: attention (k_attend_seg + its merge) of
+    # the first layer, called with that layer's selection, timed live the same way ----
+    li0 = 0
+    att_args = []
+    for ci, (caches, layers) in enumerate(copies):
+        Lh, L = wl.layers[li0], layers[li0]
+        win = csa2.Window(codes=L["win_codes"], length=L["win_len"], pos0=L["win_pos0"],
+                          row_scale=L["win_rs"], window=wl.window)
+        idx = chains[ci][li0].idx_out
+        out = torch.empty_like(L["q"])
+        lse = torch.empty(L["q"].shape[:3], dtype=torch.float32, device=dev)
+        wcap = win.span(qp)
+        ws = csa2.alloc_workspace(csa2.workspace_bytes("U", B, nq, 0, k, 0, wcap), dev)
+        att_args.append((caches[Lh.cache_id], idx, L["q"], win, out, lse, ws))
+
+    def attend_once(i):
+        cache, idx, q, win, out, lse, ws = att_args[i % len(att_args)]
+        csa2.sparse_attend(cache, idx, q, win, q_pos=qp, sm_scale=wl.sm_scale, out=out, lse=lse, ws=ws)
+
+    for i in range(5):
+        attend_once(i)
+    torch.cuda.synchronize()
+    ev0.record()
+    for i in range(args.kernel_iters):
+        attend_once(i)
+    ev1.record()
+    torch.cuda.synchronize()
+    att_ms = ev0.elapsed_time(ev1) / args.kernel_iters
+    att_b = attend_bytes(wl, li0)
+    att_gbps = att_b / (att_ms * 1e-3) / 1e9
+    log(f"attention call: {att_ms * 1e3:.2f} us/launch, {att_gbps:.0f} GB/s algorithmic")
+
+    att_traffic = None
+    if os.path.exists(ATT_TRAFFIC_FILE):
+        try:
+            rec = json.load(open(ATT_TRAFFIC_FILE))
+            src_hash = hashlib.sha256(open(ATT_SRC, "rb").read()).hexdigest()
+            if rec.get("kernel_source_sha256") == src_hash and rec.get("workload") == name:
+                att_traffic = rec.get("bytes_per_launch")
+        except Exception:
+            att_traffic = None
+
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         try:
@@ -389,10 +452,14 @@ def main():
         "step_algorithmic_bytes": sbytes,
         "eager_ms_per_step": round(eager_s / args.steps * 1e3, 4),
         "graph_ms_per_step": None if graph_s is None else round(graph_s / args.steps * 1e3, 4),
-        "roofline": (
+        "roofline": {"kernel": "csa2_sparse_attend: k_attend_seg + k_merge_seg (first layer's selection)",
+                     "bound": "hbm", "achieved": round(att_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(att_gbps / HBM_PEAK_GBPS, 4), "traffic": att_traffic,
+                     "bytes_per_launch": att_b, "us_per_launch": round(att_ms * 1e3, 3)},
+        "roofline_scoring": (
             {"kernel": "k_prefill_score (indexer scoring of a prefill chunk, fp16 MFMA)", "bound": "mfma",
              "achieved": round(k_tflops, 1), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-             "frac": round(k_tflops / MFMA_F16_PEAK_TFLOPS, 4), "traffic": traffic,
+             "frac": round(k_tflops / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
              "flops_per_launch": kflops, "us_per_launch": round(k_ms * 1e3, 3)} if prefill else
             {"kernel": "k_index_score (Full-layer lightning-indexer scoring)", "bound": "hbm",
              "achieved": round(k_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
