@@ -29,6 +29,7 @@ csa2_status hip_check(hipError_t e, const char *what) {
 }
 
 constexpr int kFinItems = 4096;        // rows up to this length select in LDS directly
+constexpr int64_t kRowSelectMinRows = 32;  // rows from which rows up to 16384 select one workgroup per row
 constexpr int kScoreChunk = 2048;      // scoring columns per workgroup (contiguous entries)
 constexpr int kScoreChunkCand = 512;   // ... when gathering a candidate list
 constexpr int32_t kPrefillQueries = 64;  // queries per request from which scoring is a matrix-core contraction
@@ -62,7 +63,8 @@ struct WsLayout {
   size_t scores = 0, hist = 0, zero_end = 0, info = 0, counts = 0, suf = 0, list0 = 0, list1 = 0, eq0 = 0,
          eq1 = 0, part = 0,
          total = 0;
-  bool compact = false;
+  bool compact = false;   // chunked compaction + final selection (long rows)
+  bool row_sel = false;   // one workgroup per row, keys in registers (rows up to kSelectRowMax)
   int max_wg = 0, chunk = 0;
   int64_t seg_stride = 0;
   // attention: units of 128 positions, U per row, T in all, over G workgroups
@@ -91,7 +93,11 @@ WsLayout ws_layout(csa2_mode mode, int64_t rows, int64_t n_cols, int32_t k, int3
   WsLayout L;
   size_t off = 0;
   if (mode == CSA2_FULL || mode == CSA2_REINDEX) {
-    L.compact = n_cols > kFinItems;
+    // one workgroup per row pays off once there are enough rows to fill the
+    // GPU; few long rows go through the chunked path, which spreads each row
+    // over many workgroups
+    L.row_sel = n_cols > kFinItems && n_cols <= csa2::kSelectRowMax && rows >= kRowSelectMinRows;
+    L.compact = n_cols > kFinItems && !L.row_sel;
     L.scores = off;
     off = align256(off + (size_t)rows * n_cols * 4);
     L.hist = off;  // zeroed by a fill before the scoring kernel adds to it
@@ -191,7 +197,7 @@ struct SelTarget {
 csa2_status run_select(const WsLayout &L, char *ws, int rows, int32_t n_cols, const int32_t *cand_map,
                        const int32_t *n_entries, const int32_t *q_pos, int32_t nq, const SelTarget *tg,
                        int ntarget, bool hist_ready, const float *scores, hipStream_t st) {
-  if (!L.compact) {
+  if (!L.compact) {  // the row fits one workgroup
     csa2::DirectArgs d{};
     d.scores = scores;
     d.n_cols = n_cols;
@@ -204,7 +210,9 @@ csa2_status run_select(const WsLayout &L, char *ws, int rows, int32_t n_cols, co
       d.out[i] = tg[i].out;
       d.out_stride[i] = tg[i].stride;
     }
-    return hip_check(csa2::launch_select_direct(d, rows, ntarget, st), "select");
+    return hip_check(L.row_sel ? csa2::launch_select_row(d, rows, ntarget, st)
+                               : csa2::launch_select_direct(d, rows, ntarget, st),
+                     "select");
   }
   csa2_status s;
   if (!hist_ready) {
@@ -363,8 +371,8 @@ csa2_status csa2_topk(const float *scores, const int32_t *cand, int32_t batch, i
   const SelTarget tg{k, idx_out, k};
   s = run_select(L, (char *)ws, batch * nq, n, cand, nullptr, nullptr, nq, &tg, 1, false, scores,
                  (hipStream_t)stream);
-  if (s || !cand || !L.compact) return s;
-  // the chunked path writes ids in column order: sort them when ids are a map
+  if (s || !cand || !(L.compact || L.row_sel)) return s;
+  // these paths write ids in column order: sort them when ids are a map
   return hip_check(csa2::launch_sort_rows(idx_out, k, k, batch * nq, (hipStream_t)stream), "sort");
 }
 

@@ -793,6 +793,169 @@ hipError_t launch_select_direct(const DirectArgs &a, int rows, int ntarget, hipS
   return hipGetLastError();
 }
 
+// ---- one workgroup per row, every key in registers ----------------------------------
+// Rows of up to 1024 * PER columns (16 per thread: 32 would spill at 1024
+// threads). Thread t holds columns t * PER + [0, PER),
+// so (thread, item) is column order. The threshold key (the T-th largest) is
+// found exactly by radix levels over the row's own key range: level 1 bins
+// key - kmin by its top 12 significant bits, the next levels refine the
+// boundary bin 12 bits at a time. Every key above the threshold is taken, and
+// of the keys equal to it the first ones in column order (the lower entry ids
+// when ids grow with the column). Ids are written in column order, then -1.
+#define ROW_NT 1024
+
+// min and max over the workgroup (s: ROW_NT / 64 x 2 words)
+__device__ __forceinline__ void block_minmax(uint32_t lo, uint32_t hi, uint32_t *s, uint32_t &mn, uint32_t &mx) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    lo = min(lo, (uint32_t)__shfl_xor((int)lo, off));
+    hi = max(hi, (uint32_t)__shfl_xor((int)hi, off));
+  }
+  const int t = threadIdx.x, nw = blockDim.x >> 6;
+  if ((t & 63) == 0) {
+    s[2 * (t >> 6)] = lo;
+    s[2 * (t >> 6) + 1] = hi;
+  }
+  __syncthreads();
+  mn = 0xFFFFFFFFu;
+  mx = 0u;
+  for (int i = 0; i < nw; ++i) {
+    mn = min(mn, s[2 * i]);
+    mx = max(mx, s[2 * i + 1]);
+  }
+  __syncthreads();
+}
+
+template <int PER, bool VEC>
+__global__ __launch_bounds__(ROW_NT) void k_select_row(DirectArgs a) {
+  __shared__ uint32_t hist[DIG_BINS];
+  __shared__ uint32_t scan[ROW_NT / 64 * 2];
+  __shared__ int hout[4];
+  const int r = blockIdx.x, tg = blockIdx.y, t = threadIdx.x;
+  const float *row = a.scores + (int64_t)r * a.n_cols;
+  const int32_t lim = row_limit(a.n_entries, a.q_pos, a.nq, r, a.n_cols);
+  const int T = a.T[tg];
+  int32_t *gout = a.out[tg] + (int64_t)r * a.out_stride[tg];
+  const int32_t c0 = t * PER;
+
+  // ---- keys: columns past the row's limit count as absent (key 0) ----
+  uint32_t key[PER];
+  if constexpr (VEC) {
+#pragma unroll
+    for (int j = 0; j < PER / 4; ++j) {
+      const int32_t c = min(c0 + 4 * j, a.n_cols - 4);  // in the row even past its end
+      const v4f v = *(const v4f *)(row + c);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) key[4 * j + e] = score_key(v[e]);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) key[j] = score_key(row[min(c0 + j, a.n_cols - 1)]);
+  }
+  uint32_t nv = 0, lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const bool ok = c0 + j < lim && key[j] > KEY_NEG_INF;
+    key[j] = ok ? key[j] : 0u;
+    nv += ok ? 1u : 0u;
+    lo = ok ? min(lo, key[j]) : lo;
+    hi = max(hi, key[j]);
+  }
+  const uint32_t n_valid = block_sum(nv, scan);
+  const int n_sel = min((uint32_t)T, n_valid);
+
+  // ---- threshold key and how many keys equal to it are taken ----
+  uint32_t thr = KEY_NEG_INF + 1u;  // every valid key passes
+  int take_eq = 1 << 30;
+  if ((uint32_t)T < n_valid) {
+    uint32_t kmin, kmax;
+    block_minmax(lo, hi, scan, kmin, kmax);
+    // level shifts: the range's significant bits, 12 per level
+    const uint32_t range = kmax - kmin;
+    const int bits = range ? 32 - __builtin_clz(range) : 0;
+    int shift = bits > 12 ? bits - 12 : 0;
+    uint32_t prefix = 0;  // bits [pshift, 32) of key - kmin in the boundary bin so far
+    int need = T;         // keys still to take at or below the current prefix
+    int pshift = 32;      // bits above the current level are fixed to `prefix`
+    bool all_in_set = false;
+    for (int level = 0; level < 3; ++level) {
+      for (int i = t; i < DIG_BINS; i += ROW_NT) hist[i] = 0;
+      __syncthreads();
+      // this level's digit: bits [shift, pshift) of key - kmin (at most 12)
+      const uint32_t mask = pshift >= 32 ? (uint32_t)(DIG_BINS - 1) : ((1u << (pshift - shift)) - 1u);
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const uint32_t d = key[j] - kmin;
+        const bool in = key[j] != 0u && (pshift >= 32 || (d >> pshift) == prefix);
+        if (in) atomicAdd(&hist[(d >> shift) & mask], 1u);
+      }
+      __syncthreads();
+      hist_threshold_n<DIG_BINS, ROW_NT, true>(hist, (uint32_t)need, scan, hout);
+      const int bin = hout[0];
+      const int before = hout[1];
+      __syncthreads();  // hout is read before the next level rewrites it
+      if (bin < 0) {
+        // the set holds exactly `need` keys: all of them are taken, and the
+        // threshold is the set's smallest key
+        uint32_t lo2 = 0xFFFFFFFFu;
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+          const uint32_t d = key[j] - kmin;
+          const bool in = key[j] != 0u && (pshift >= 32 || (d >> pshift) == prefix);
+          lo2 = in ? min(lo2, key[j]) : lo2;
+        }
+        uint32_t mn, mx;
+        block_minmax(lo2, 0u, scan, mn, mx);
+        thr = mn;
+        all_in_set = true;
+        break;
+      }
+      need -= before;  // keys in higher bins are all taken
+      prefix = (pshift >= 32 ? 0u : (prefix << (pshift - shift))) | (uint32_t)bin;
+      pshift = shift;
+      if (shift == 0) break;
+      shift = shift > 12 ? shift - 12 : 0;
+    }
+    if (!all_in_set) {
+      thr = kmin + (prefix << pshift);
+      take_eq = need;
+    }
+  }
+
+  // ---- emission in column order ----
+  uint32_t na = 0, ne = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    na += key[j] > thr ? 1u : 0u;
+    ne += key[j] == thr ? 1u : 0u;
+  }
+  uint32_t tot;
+  const uint32_t eb = block_exclusive_scan(ne, scan, &tot);  // equal keys in earlier threads
+  const int eq_take = max(0, min((int)ne, take_eq - (int)eb));
+  const uint32_t off = block_exclusive_scan(na + (uint32_t)eq_take, scan, &tot);
+  const int32_t *map = a.cand_map ? a.cand_map + (int64_t)r * a.n_cols : nullptr;
+  int o = (int)off, e = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const bool take = key[j] > thr || (key[j] == thr && e++ < eq_take);
+    if (take) {
+      gout[o++] = map ? map[c0 + j] : c0 + j;
+    }
+  }
+  for (int i = n_sel + t; i < T; i += ROW_NT) gout[i] = -1;
+}
+
+hipError_t launch_select_row(const DirectArgs &a, int rows, int ntarget, hipStream_t st) {
+  const bool vec = (a.n_cols & 3) == 0 && (((uintptr_t)a.scores) & 15) == 0;
+  const dim3 grid((unsigned)rows, (unsigned)ntarget);
+  if (a.n_cols > kSelectRowMax) return hipErrorInvalidValue;
+  if (vec)
+    hipLaunchKernelGGL((k_select_row<kSelectRowMax / ROW_NT, true>), grid, dim3(ROW_NT), 0, st, a);
+  else
+    hipLaunchKernelGGL((k_select_row<kSelectRowMax / ROW_NT, false>), grid, dim3(ROW_NT), 0, st, a);
+  return hipGetLastError();
+}
+
 // ---- ascending order for ids that did not come in column order ----------------------
 // Row r of `ids` holds its selected ids first, then -1 up to T.
 __global__ __launch_bounds__(FIN_NT) void k_sort_rows(int32_t *ids, int32_t stride, int32_t T) {

@@ -176,6 +176,35 @@ def test_topk_random_scores(n, k):
     assert (g == o).all()
 
 
+@pytest.mark.parametrize("dist", ["ties", "normal", "outliers"])
+def test_topk_many_rows_one_workgroup_each(dist):
+    """40 rows of 4097..16384 columns (the one-workgroup-per-row path): ties,
+    plain normal scores, and a few large outliers that squeeze most keys into
+    a narrow part of the row's range; -inf holes and a short last row."""
+    _log(f"topk many rows {dist}")
+    rng = np.random.default_rng({"ties": 11, "normal": 12, "outliers": 13}[dist])
+    rows, n, k = 40, 12000, 2048
+    if dist == "ties":
+        s = rng.integers(0, 40, size=(rows, 1, n)).astype(np.float64)
+    elif dist == "normal":
+        s = rng.standard_normal((rows, 1, n))
+    else:
+        s = np.abs(rng.standard_normal((rows, 1, n))) + 1.0
+        s[:, :, :5] = 1e6
+    s[rng.random(s.shape) < 0.05] = -np.inf
+    s[-1, 0, 3000:] = -np.inf  # fewer finite scores than k
+    s32 = s.astype(np.float32)
+    g = csa2.topk(t(s32), k).cpu().numpy()
+    o = oracle.topk(s32.astype(np.float64), k)
+    assert (g == o).all()
+    # a candidate map in ascending order keeps ascending ids
+    cand = np.sort(np.stack([rng.choice(10 ** 6, size=n, replace=False) for _ in range(rows)]), axis=1)
+    cand = cand[:, None, :].astype(np.int32)
+    g = csa2.topk(t(s32), k, cand=t(cand)).cpu().numpy()
+    o = oracle.topk(s32.astype(np.float64), k, cand=cand)
+    assert (g == o).all()
+
+
 def test_topk_candidate_map():
     rng = np.random.default_rng(9)
     n, k = 20000, 300
