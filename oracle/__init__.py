@@ -176,6 +176,74 @@ def dequant_e4m3(b: np.ndarray, row_scale: Optional[np.ndarray] = None) -> np.nd
     return out
 
 
+# ---- encoding: the write side of the cache (readings in csa2_oracle.h) ----
+
+def e4m3_encode(x) -> np.ndarray:
+    """E4M3 bytes of fp32 values: nearest finite value, ties to even, saturating."""
+    x = np.ascontiguousarray(x, np.float32)
+    out = np.empty(x.shape, np.uint8)
+    lib().orc_e4m3_encode_n(C.c_void_p(x.ctypes.data), C.c_int64(x.size), C.c_void_p(out.ctypes.data))
+    return out
+
+
+def e2m1_encode(y: float) -> int:
+    """E2M1 code (sign in bit 3) of a value already divided by its block scale."""
+    L = lib()
+    L.orc_e2m1_encode.argtypes = [C.c_float]
+    return int(L.orc_e2m1_encode(C.c_float(y)))
+
+
+def quantize_fp4(x: np.ndarray):
+    """Rows [..., C] (C a multiple of 16) -> (codes [..., C/2], scales [..., C/16])."""
+    x = np.ascontiguousarray(x, np.float32)
+    ch = x.shape[-1]
+    n = x.size // ch
+    codes = np.empty(x.shape[:-1] + (ch // 2,), np.uint8)
+    scales = np.empty(x.shape[:-1] + (ch // 16,), np.uint8)
+    lib().orc_quantize_fp4(C.c_void_p(x.ctypes.data), C.c_int64(n), C.c_int32(ch),
+                           C.c_void_p(codes.ctypes.data), C.c_void_p(scales.ctypes.data))
+    return codes, scales
+
+
+class _CacheW(C.Structure):
+    _fields_ = [("kv_codes", C.c_void_p), ("kv_scales", C.c_void_p), ("ix_codes", C.c_void_p),
+                ("ix_scales", C.c_void_p), ("block_table", C.c_void_p), ("page_size", C.c_int32),
+                ("max_pages", C.c_int32), ("num_pages", C.c_int32)]
+
+
+def kv_append(kv_codes, kv_scales, ix_codes, ix_scales, block_table, page_size, kv, ix, entry):
+    """Quantise and write new entries into the (numpy) cache arrays in place.
+    kv [B][n_new][512], ix [B][n_new][64] or None, entry [B][n_new] (< 0: none)."""
+    for a in (kv_codes, kv_scales, ix_codes, ix_scales):
+        assert a.flags["C_CONTIGUOUS"] and a.dtype == np.uint8
+    bt = np.ascontiguousarray(block_table, np.int32)
+    kv = np.ascontiguousarray(kv, np.float32)
+    ixa = None if ix is None else np.ascontiguousarray(ix, np.float32)
+    en = np.ascontiguousarray(entry, np.int32)
+    B, n_new = en.shape
+    num_pages = kv_codes.shape[0] // page_size if kv_codes.ndim == 2 else kv_codes.shape[0]
+    cw = _CacheW(kv_codes.ctypes.data, kv_scales.ctypes.data, ix_codes.ctypes.data, ix_scales.ctypes.data,
+                 bt.ctypes.data, page_size, bt.shape[-1], num_pages)
+    lib().orc_kv_append(C.byref(cw), C.c_void_p(kv.ctypes.data),
+                        None if ixa is None else C.c_void_p(ixa.ctypes.data),
+                        C.c_void_p(en.ctypes.data), C.c_int32(B), C.c_int32(n_new))
+
+
+def window_append(codes, row_scale, x, row):
+    """Encode window rows into codes [B][rows][512] (and row_scale [B][rows]) in place.
+    x [B][n_new][512], row [B][n_new] (< 0: none)."""
+    assert codes.flags["C_CONTIGUOUS"] and codes.dtype == np.uint8
+    if row_scale is not None:
+        assert row_scale.flags["C_CONTIGUOUS"] and row_scale.dtype == np.float32
+    x = np.ascontiguousarray(x, np.float32)
+    rw = np.ascontiguousarray(row, np.int32)
+    B, n_new = rw.shape
+    lib().orc_window_append(C.c_void_p(codes.ctypes.data),
+                            None if row_scale is None else C.c_void_p(row_scale.ctypes.data),
+                            C.c_int32(codes.shape[1]), C.c_void_p(x.ctypes.data),
+                            C.c_void_p(rw.ctypes.data), C.c_int32(B), C.c_int32(n_new))
+
+
 def index_score(cache, qix_codes, qix_scales, w, q_pos=None, cand=None, n_cols=None):
     keep = _Keep()
     cs = _cache_struct(cache, keep)

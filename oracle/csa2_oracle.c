@@ -88,6 +88,105 @@ void orc_dequant_e4m3(const uint8_t *bytes, const float *row_scale, int64_t n_ro
   }
 }
 
+/* ---- Encoding (the write side of the cache) -------------------------------
+ * Nearest representable value by exhaustive search over the format's
+ * magnitudes in increasing order; a tie goes to the even mantissa (the even
+ * code, since consecutive codes differ in the mantissa's last bit).
+ * Readings are listed in csa2_oracle.h. */
+static int nearest_even(const double *mag, int n, double a) {
+  int best = 0;
+  double bd = fabs(a - mag[0]);
+  for (int i = 1; i < n; ++i) {
+    double d = fabs(a - mag[i]);
+    if (d < bd || (d == bd && (i & 1) == 0 && (best & 1) == 1)) {
+      best = i;
+      bd = d;
+    }
+  }
+  return best;
+}
+
+int orc_e4m3_encode(float x) {
+  build_tables();
+  /* finite magnitudes: bytes 0x00..0x7E (0x7F is NaN) */
+  int b = nearest_even(T_E4M3, 0x7F, fabs((double)x));
+  return b | (x < 0.0f ? 0x80 : 0);
+}
+
+void orc_e4m3_encode_n(const float *x, int64_t n, uint8_t *out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = (uint8_t)orc_e4m3_encode(x[i]);
+}
+
+int orc_e2m1_encode(float y) {
+  build_tables();
+  int c = nearest_even(T_E2M1, 8, fabs((double)y));
+  return c | (y < 0.0f ? 8 : 0);
+}
+
+void orc_quantize_fp4(const float *x, int64_t n_rows, int32_t channels, uint8_t *codes,
+                      uint8_t *scales) {
+  build_tables();
+  for (int64_t r = 0; r < n_rows; ++r) {
+    const float *xr = x + r * channels;
+    uint8_t *cr = codes + r * (channels / 2);
+    for (int c = 0; c < channels / 2; ++c) cr[c] = 0;
+    for (int g = 0; g < channels / ORC_G; ++g) {
+      float amax = 0.0f;
+      for (int i = 0; i < ORC_G; ++i) {
+        float a = fabsf(xr[g * ORC_G + i]);
+        if (a > amax) amax = a;
+      }
+      int sb = orc_e4m3_encode(amax / 6.0f);
+      scales[r * (channels / ORC_G) + g] = (uint8_t)sb;
+      float s = (float)T_E4M3[sb];
+      for (int i = 0; i < ORC_G; ++i) {
+        int ch = g * ORC_G + i;
+        float v = xr[ch];
+        int code = (s == 0.0f) ? (v < 0.0f ? 8 : 0) : orc_e2m1_encode(v / s);
+        cr[ch >> 1] |= (uint8_t)(code << ((ch & 1) * 4));
+      }
+    }
+  }
+}
+
+void orc_kv_append(const orc_cache_w *c, const float *kv, const float *ix, const int32_t *entry,
+                   int32_t B, int32_t n_new) {
+  for (int b = 0; b < B; ++b)
+    for (int j = 0; j < n_new; ++j) {
+      int32_t s = entry[(int64_t)b * n_new + j];
+      if (s < 0 || s / c->page_size >= c->max_pages) continue;
+      int32_t page = c->block_table[(int64_t)b * c->max_pages + s / c->page_size];
+      if (page < 0 || page >= c->num_pages) continue;
+      int64_t row = (int64_t)page * c->page_size + s % c->page_size;
+      orc_quantize_fp4(kv + ((int64_t)b * n_new + j) * ORC_D, 1, ORC_D, c->kv_codes + row * (ORC_D / 2),
+                       c->kv_scales + row * (ORC_D / ORC_G));
+      if (ix)
+        orc_quantize_fp4(ix + ((int64_t)b * n_new + j) * ORC_DI, 1, ORC_DI,
+                         c->ix_codes + row * (ORC_DI / 2), c->ix_scales + row * (ORC_DI / ORC_G));
+    }
+}
+
+void orc_window_append(uint8_t *codes, float *row_scale, int32_t rows, const float *x,
+                       const int32_t *row, int32_t B, int32_t n_new) {
+  for (int b = 0; b < B; ++b)
+    for (int j = 0; j < n_new; ++j) {
+      int32_t w = row[(int64_t)b * n_new + j];
+      if (w < 0 || w >= rows) continue;
+      const float *xr = x + ((int64_t)b * n_new + j) * ORC_D;
+      uint8_t *dst = codes + ((int64_t)b * rows + w) * ORC_D;
+      float rs = 1.0f;
+      if (row_scale) {
+        float amax = 0.0f;
+        for (int c = 0; c < ORC_D; ++c)
+          if (fabsf(xr[c]) > amax) amax = fabsf(xr[c]);
+        rs = amax > 0.0f ? amax / 448.0f : 1.0f;
+        row_scale[(int64_t)b * rows + w] = rs;
+      }
+      for (int c = 0; c < ORC_D; ++c)
+        dst[c] = (uint8_t)orc_e4m3_encode(row_scale ? xr[c] / rs : xr[c]);
+    }
+}
+
 /* Physical row of entry s of request b, or -1 if the page table has no page. */
 static int64_t entry_row(const orc_cache *c, int b, int64_t s) {
   int32_t page = c->block_table[(int64_t)b * c->max_pages + s / c->page_size];

@@ -90,6 +90,47 @@ int orc_layer_step(int mode, const orc_cache *c, const orc_window *win, const fl
                    const int32_t *idx_in, int32_t *idx_out, int32_t *pool_out,
                    double sm_scale, double *out, double *lse, double *scores_out);
 
+/* ---- Encoding: the write side of the cache ([P2-FP4]; [P2-FP4] also keeps
+ * the last 128 tokens of the window). The pages give the formats only; the
+ * rounding is a reading:
+ *  - E4M3 encode: the finite E4M3 value nearest to x, ties to the even
+ *    mantissa, saturating at +-448; the sign bit is x < 0.
+ *  - FP4 block of 16 channels: scale byte = E4M3 encode of amax/6 (amax the
+ *    group's largest |x|, 6 the largest E2M1 magnitude, the division in
+ *    fp32); s = its value; each channel's code is the E2M1 magnitude nearest
+ *    to |y|, y = x / s in fp32, ties to the even mantissa, saturating at 6,
+ *    with the sign bit for x < 0 (s = 0 gives magnitude 0).
+ *  - Window row: with a row scale, rs = amax/448 in fp32 (1 when amax is 0)
+ *    and each byte encodes x / rs in fp32; without, each byte encodes x. */
+int orc_e4m3_encode(float x);
+void orc_e4m3_encode_n(const float *x, int64_t n, uint8_t *out);
+int orc_e2m1_encode(float y);  /* y already divided by the block scale */
+
+/* Quantise rows [n_rows][channels] (channels a multiple of 16) to codes
+ * [n_rows][channels/2] (channel 2j in the low nibble of byte j) and scales
+ * [n_rows][channels/16]. */
+void orc_quantize_fp4(const float *x, int64_t n_rows, int32_t channels, uint8_t *codes,
+                      uint8_t *scales);
+
+/* Append new compressed entries: for request b and new entry j, when
+ * entry[b*n_new + j] >= 0 it is the entry index s written: main KV row
+ * kv[b][j][512] and (when ix != NULL) indexer key ix[b][j][64], quantised,
+ * at page block_table[b*max_pages + s/page_size], slot s%page_size. Entries
+ * whose page is missing are skipped. n_entries is left to the caller. */
+typedef struct {
+  uint8_t *kv_codes, *kv_scales, *ix_codes, *ix_scales;
+  const int32_t *block_table;
+  int32_t page_size, max_pages, num_pages;
+} orc_cache_w;
+void orc_kv_append(const orc_cache_w *c, const float *kv, const float *ix, const int32_t *entry,
+                   int32_t B, int32_t n_new);
+
+/* Window ring append: token j of request b, when row[b*n_new + j] >= 0, is
+ * written at codes[b][row][512] (and row_scale[b][row] when row_scale !=
+ * NULL). */
+void orc_window_append(uint8_t *codes, float *row_scale, int32_t rows, const float *x,
+                       const int32_t *row, int32_t B, int32_t n_new);
+
 int orc_num_threads(void);
 
 #ifdef __cplusplus

@@ -105,6 +105,144 @@ def pin_encoder_roundtrip():
     assert (oracle.dequant_e4m3(encode_e4m3(v)[None, :])[0] == v).all()
 
 
+def pin_encode_golden():
+    """Hand-derived E2M1 / E4M3 encodings (ties, saturation, signs) and one FP4 block."""
+    g = golden("encode_cases.json")
+    for y, code in g["e2m1"]["cases"]:
+        assert oracle.e2m1_encode(y) == code, (y, oracle.e2m1_encode(y), code)
+    xs = np.array([c[0] for c in g["e4m3"]["cases"]], np.float32)
+    assert [int(b) for b in oracle.e4m3_encode(xs)] == [c[1] for c in g["e4m3"]["cases"]]
+    blk = g["fp4_block"]
+    codes, scales = oracle.quantize_fp4(np.array(blk["x"], np.float32)[None, :])
+    assert int(scales[0, 0]) == blk["scale"] and [int(c) for c in codes[0]] == blk["codes"]
+
+
+def pin_e4m3_encode_vs_library():
+    """E4M3 encoding equals torch's float8_e4m3fn conversion (a library routine, round to
+    nearest even) on random values, every midpoint between neighbouring values, and
+    values past 448 (clamped first: the library maps them to NaN)."""
+    rng = np.random.default_rng(3)
+    v = torch.arange(0, 127, dtype=torch.uint8).view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    mids = (v[1:] + v[:-1]) / 2
+    x = np.concatenate([rng.standard_normal(4000) * 30, rng.standard_normal(2000) * 1e-2, mids, -mids,
+                        [500.0, -1e5, 449.0]]).astype(np.float32)
+    ref = torch.from_numpy(np.clip(x, -448, 448)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = oracle.e4m3_encode(x)
+    # the library keeps the sign of a negative value that rounds to zero; the reading sets it too
+    assert (got == ref).all(), np.nonzero(got != ref)[0][:5]
+
+
+def pin_fp4_encode_nearest():
+    """On random rows (zero groups, huge and tiny values included): the scale byte is the
+    library's E4M3 of fp32(amax/6), and every code is an E2M1 value nearest to x/s (fp32),
+    a tie going to the even code; dequantisation then errs by at most half a step."""
+    rng = np.random.default_rng(4)
+    x = (rng.standard_normal((40, 64)) * np.exp(rng.standard_normal((40, 1)) * 3)).astype(np.float32)
+    x[3, :16] = 0.0
+    x[5, 16:32] = 1e5
+    x[7, :] = rng.integers(-12, 13, 64) * 0.25  # many exact midpoints
+    codes, scales = oracle.quantize_fp4(x)
+    mags = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    for r in range(x.shape[0]):
+        for grp in range(4):
+            blk = x[r, 16 * grp:16 * grp + 16]
+            amax = np.float32(np.abs(blk).max())
+            sref = torch.tensor([min(float(amax / np.float32(6.0)), 448.0)], dtype=torch.float32)
+            sref = int(sref.to(torch.float8_e4m3fn).view(torch.uint8).item())
+            assert scales[r, grp] == sref, (r, grp)
+            s = np.float32(oracle.e4m3(int(scales[r, grp])))
+            for i in range(16):
+                ch = 16 * grp + i
+                nib = (int(codes[r, ch // 2]) >> (4 * (ch & 1))) & 15
+                if s == 0:
+                    assert nib & 7 == 0
+                    continue
+                y = np.float32(blk[i]) / s
+                d = np.abs(abs(float(y)) - mags)
+                best = np.flatnonzero(d == d.min())
+                want = best[0] if len(best) == 1 else [b for b in best if b % 2 == 0][0]
+                assert nib & 7 == want, (r, ch, float(y), nib)
+                assert (nib >> 3) == (1 if blk[i] < 0 else 0)
+
+
+def pin_fp4_grid_roundtrip():
+    """Rows built on the grid (E2M1 value x E4M3 scale, one channel at 6 s so that amax/6 = s)
+    encode back to the same codes and scale."""
+    rng = np.random.default_rng(5)
+    grid = np.array(golden("e2m1_values.json")["values"])
+    for sb in [0x08, 0x30, 0x38, 0x45, 0x6A, 0x7E]:
+        s = oracle.e4m3(sb)
+        nib = rng.integers(0, 16, 16)
+        nib[rng.integers(0, 16)] = 7
+        x = (grid[nib] * s).astype(np.float32)
+        codes, scales = oracle.quantize_fp4(x[None, :])
+        assert scales[0, 0] == sb
+        back = oracle.dequant_fp4(codes, scales)[0]
+        assert (back == grid[nib] * s).all()  # -0 comes back as +0, equal as a value
+
+
+def pin_window_append_rows():
+    """A window row with a row scale: rs = amax/448, the largest element encodes to +-448,
+    and every byte is the E4M3 nearest to x/rs; without a row scale the bytes encode x.
+    Rows not named are left alone."""
+    rng = np.random.default_rng(6)
+    B, rows = 2, 8
+    x = (rng.standard_normal((B, 2, 512)) * 3).astype(np.float32)
+    codes = np.full((B, rows, 512), 0x11, np.uint8)
+    rs = np.full((B, rows), 7.0, np.float32)
+    row = np.array([[3, -1], [0, 7]], np.int32)
+    oracle.window_append(codes, rs, x, row)
+    for b, j, w in [(0, 0, 3), (1, 0, 0), (1, 1, 7)]:
+        amax = np.float32(np.abs(x[b, j]).max())
+        assert rs[b, w] == amax / np.float32(448.0)
+        y = (x[b, j] / rs[b, w]).astype(np.float32)
+        ref = torch.from_numpy(np.clip(y, -448, 448)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert (codes[b, w] == ref).all()
+        assert (np.abs(oracle.dequant_e4m3(codes[b, w][None, :])[0]).max() == 448.0)
+    untouched = [(0, r) for r in range(rows) if r != 3] + [(1, r) for r in range(1, 7)]
+    for b, w in untouched:
+        assert (codes[b, w] == 0x11).all() and rs[b, w] == 7.0
+    c2 = np.zeros((1, 4, 512), np.uint8)
+    oracle.window_append(c2, None, x[:1, :1], np.array([[2]], np.int32))
+    ref = torch.from_numpy(np.clip(x[0, 0], -448, 448)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert (c2[0, 2] == ref).all() and (c2[0, [0, 1, 3]] == 0).all()
+
+
+def pin_kv_append_placement():
+    """New entries land at page block_table[b][s/page], slot s%page, main KV and indexer
+    key both; other rows are untouched; a missing page or a negative entry writes nothing."""
+    rng = np.random.default_rng(7)
+    B, page, max_pages, num_pages = 2, 4, 3, 6
+    bt = np.array([[5, 0, 2], [1, -1, 4]], np.int32)
+    kvc = np.full((num_pages * page, 256), 0xAA, np.uint8)
+    kvs = np.full((num_pages * page, 32), 0xAB, np.uint8)
+    ixc = np.full((num_pages * page, 32), 0xAC, np.uint8)
+    ixs = np.full((num_pages * page, 4), 0xAD, np.uint8)
+    kv = rng.standard_normal((B, 3, 512)).astype(np.float32)
+    ix = rng.standard_normal((B, 3, 64)).astype(np.float32)
+    entry = np.array([[9, 2, -1], [5, 0, 11]], np.int32)  # request 1 entry 5: page 1 missing
+    oracle.kv_append(kvc, kvs, ixc, ixs, bt, page, kv, ix, entry)
+    written = {}
+    for b in range(B):
+        for j in range(3):
+            s = int(entry[b, j])
+            if s < 0 or bt[b, s // page] < 0:
+                continue
+            r = int(bt[b, s // page]) * page + s % page
+            written[r] = (b, j)
+    assert sorted(written) == sorted([2 * page + 1, 5 * page + 2, 1 * page + 0, 4 * page + 3])
+    for r in range(num_pages * page):
+        if r in written:
+            b, j = written[r]
+            c, sc = oracle.quantize_fp4(kv[b, j][None, :])
+            assert (kvc[r] == c[0]).all() and (kvs[r] == sc[0]).all()
+            c, sc = oracle.quantize_fp4(ix[b, j][None, :])
+            assert (ixc[r] == c[0]).all() and (ixs[r] == sc[0]).all()
+        else:
+            assert (kvc[r] == 0xAA).all() and (kvs[r] == 0xAB).all()
+            assert (ixc[r] == 0xAC).all() and (ixs[r] == 0xAD).all()
+
+
 # ---------------------------------------------------------------- index score
 
 def _ix_query(q_nib, q_scales, w):
@@ -460,4 +598,6 @@ ALL_PINS = [
     pin_attend_dense_equals_sdpa, pin_attend_special_cases, pin_attend_large_logits,
     pin_attend_permutation_and_window_rows, pin_prefill_window_bounds,
     pin_reuse_equals_full_given_indices, pin_paged_equals_contiguous,
+    pin_encode_golden, pin_e4m3_encode_vs_library, pin_fp4_encode_nearest, pin_fp4_grid_roundtrip,
+    pin_window_append_rows, pin_kv_append_placement,
 ]

@@ -35,6 +35,17 @@ MUTATIONS = [
     ("lse without log", "lse[bt * ORC_H + h] = M + log(L);", "lse[bt * ORC_H + h] = M + L;"),
     ("query head stride", "const float *qh = q + (bt * ORC_H + h) * ORC_D;", "const float *qh = q + (bt * ORC_H + (h ^ 1)) * ORC_D;"),
     ("selected entry rows skipped", "if (s < 0 || s >= c->n_entries[b]) continue;", "if (s <= 0 || s >= c->n_entries[b]) continue;"),
+    ("encode ties to odd", "(d == bd && (i & 1) == 0 && (best & 1) == 1)", "(d == bd && (i & 1) == 1 && (best & 1) == 0)"),
+    ("encode ties upward", "(d == bd && (i & 1) == 0 && (best & 1) == 1)", "(d == bd)"),
+    ("block scale from amax/4", "int sb = orc_e4m3_encode(amax / 6.0f);", "int sb = orc_e4m3_encode(amax / 4.0f);"),
+    ("encode sign dropped", "return c | (y < 0.0f ? 8 : 0);", "return c;"),
+    ("encode nibble order", "cr[ch >> 1] |= (uint8_t)(code << ((ch & 1) * 4));", "cr[ch >> 1] |= (uint8_t)(code << ((1 - (ch & 1)) * 4));"),
+    ("encode NaN byte allowed", "int b = nearest_even(T_E4M3, 0x7F, fabs((double)x));", "int b = nearest_even(T_E4M3, 0x7E, fabs((double)x));"),
+    ("window row scale /240", "rs = amax > 0.0f ? amax / 448.0f : 1.0f;", "rs = amax > 0.0f ? amax / 240.0f : 1.0f;"),
+    ("append slot reversed", "int64_t row = (int64_t)page * c->page_size + s % c->page_size;",
+     "int64_t row = (int64_t)page * c->page_size + (c->page_size - 1 - s % c->page_size);"),
+    ("append indexer into main KV scales", "c->ix_codes + row * (ORC_DI / 2), c->ix_scales + row * (ORC_DI / ORC_G));",
+     "c->ix_codes + row * (ORC_DI / 2), c->kv_scales + row * (ORC_D / ORC_G));"),
 ]
 
 
