@@ -69,7 +69,8 @@ def lib():
         L.csa2_status_string.restype = C.c_char_p
         L.csa2_version.restype = C.c_char_p
         for name in ("csa2_index_score", "csa2_topk", "csa2_sparse_attend", "csa2_layer_step",
-                     "csa2_dequant_fp4", "csa2_dequant_e4m3"):
+                     "csa2_dequant_fp4", "csa2_dequant_e4m3", "csa2_quantize_fp4", "csa2_kv_append",
+                     "csa2_window_append"):
             getattr(L, name).restype = C.c_int
         _lib = L
     return _lib
@@ -77,6 +78,7 @@ def lib():
 
 EXPORTS = ["csa2_index_score", "csa2_topk", "csa2_sparse_attend", "csa2_layer_step",
            "csa2_workspace_bytes", "csa2_dequant_fp4", "csa2_dequant_e4m3",
+           "csa2_quantize_fp4", "csa2_kv_append", "csa2_window_append",
            "csa2_status_string", "csa2_last_error", "csa2_version"]
 
 
@@ -329,6 +331,59 @@ def dequant_e4m3(b):
     out = torch.empty(b.shape, dtype=torch.float32, device=b.device)
     _check(lib().csa2_dequant_e4m3(_ptr(b), C.c_int64(b.numel()), _ptr(out), _stream()))
     return out
+
+
+# ---- the write side of the cache ----
+
+def quantize_fp4(x, codes=None, scales=None):
+    """fp32 rows [..., C] (C a multiple of 16) -> (codes [..., C/2], scales [..., C/16]) uint8."""
+    _dev(x, torch.float32, "x")
+    ch = x.shape[-1]
+    n = x.numel() // ch if ch else 0
+    if codes is None:
+        codes = torch.empty(*x.shape[:-1], ch // 2, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(*x.shape[:-1], ch // 16, dtype=torch.uint8, device=x.device)
+    _dev(codes, torch.uint8, "codes", tuple(x.shape[:-1]) + (ch // 2,))
+    _dev(scales, torch.uint8, "scales", tuple(x.shape[:-1]) + (ch // 16,))
+    _check(lib().csa2_quantize_fp4(_ptr(x), C.c_int64(n), C.c_int32(ch), _ptr(codes), _ptr(scales),
+                                   _stream()))
+    return codes, scales
+
+
+class _CacheW(C.Structure):
+    _fields_ = [("kv_codes", C.c_void_p), ("kv_scales", C.c_void_p), ("ix_codes", C.c_void_p),
+                ("ix_scales", C.c_void_p), ("block_table", C.c_void_p), ("page_size", C.c_int32),
+                ("max_pages", C.c_int32), ("num_pages", C.c_int32)]
+
+
+def kv_append(cache: Cache, kv, entry, ix=None):
+    """Quantise new entries into the cache in place: kv [B, n_new, 512] fp32,
+    ix [B, n_new, 64] fp32 or None, entry [B, n_new] int32 (entry index, < 0: none).
+    The caller advances cache.n_entries."""
+    B, n_new = entry.shape
+    _dev(entry, torch.int32, "entry")
+    _dev(kv, torch.float32, "kv", (B, n_new, LATENT))
+    _dev(ix, torch.float32, "ix", (B, n_new, 64))
+    cw = _CacheW(cache.kv_codes.data_ptr(), cache.kv_scales.data_ptr(), cache.ix_codes.data_ptr(),
+                 cache.ix_scales.data_ptr(), cache.block_table.data_ptr(), cache.page_size,
+                 cache.max_pages, cache.kv_codes.shape[0])
+    _check(lib().csa2_kv_append(C.byref(cw), _ptr(kv), _ptr(ix), _ptr(entry), C.c_int32(B),
+                                C.c_int32(n_new), _stream()))
+
+
+def window_append(codes, x, row, row_scale=None):
+    """Encode window tokens into the ring in place: codes [B, rows, 512] uint8,
+    x [B, n_new, 512] fp32, row [B, n_new] int32 (ring row, < 0: none),
+    row_scale [B, rows] fp32 or None."""
+    B, rows = codes.shape[0], codes.shape[1]
+    n_new = row.shape[1]
+    _dev(codes, torch.uint8, "codes", (B, rows, LATENT))
+    _dev(x, torch.float32, "x", (B, n_new, LATENT))
+    _dev(row, torch.int32, "row", (B, n_new))
+    _dev(row_scale, torch.float32, "row_scale", (B, rows))
+    _check(lib().csa2_window_append(_ptr(codes), _ptr(row_scale), C.c_int32(rows), _ptr(x), _ptr(row),
+                                    C.c_int32(B), C.c_int32(n_new), _stream()))
 
 
 def version() -> str:

@@ -480,6 +480,54 @@ csa2_status csa2_layer_step(const csa2_layer_args *p, void *stream) {
                     p->nq, p->out, p->lse, st);
 }
 
+csa2_status csa2_quantize_fp4(const float *x, int64_t n_rows, int32_t channels, uint8_t *codes,
+                              uint8_t *scales, void *stream) {
+  if (!x || !codes || !scales) return fail(CSA2_EINVAL, "NULL pointer");
+  if (n_rows < 0 || channels <= 0 || channels % 16)
+    return fail(CSA2_EINVAL, "channels must be a positive multiple of 16 and n_rows >= 0");
+  if (((uintptr_t)x & 15) || ((uintptr_t)codes & 7))
+    return fail(CSA2_EINVAL, "x must be 16-byte and codes 8-byte aligned");
+  return hip_check(csa2::launch_quant_fp4(x, n_rows, channels, codes, scales, (hipStream_t)stream),
+                   "quantize_fp4");
+}
+
+csa2_status csa2_kv_append(const csa2_cache_w *cache, const float *kv, const float *ix,
+                           const int32_t *entry, int32_t batch, int32_t n_new, void *stream) {
+  if (!cache || !kv || !entry) return fail(CSA2_EINVAL, "NULL cache, kv or entry");
+  if (!cache->kv_codes || !cache->kv_scales || !cache->block_table)
+    return fail(CSA2_EINVAL, "cache kv_codes, kv_scales or block_table is NULL");
+  if (ix && (!cache->ix_codes || !cache->ix_scales))
+    return fail(CSA2_EINVAL, "ix given but the cache has no indexer arrays");
+  if (batch <= 0 || n_new < 0) return fail(CSA2_EINVAL, "batch must be positive, n_new >= 0");
+  if (!is_pow2(cache->page_size)) return fail(CSA2_EUNSUPPORTED, "page size %d is not a power of two", cache->page_size);
+  if (cache->max_pages <= 0 || cache->num_pages <= 0) return fail(CSA2_EINVAL, "empty page table");
+  if (((uintptr_t)kv & 15) || ((uintptr_t)ix & 15)) return fail(CSA2_EINVAL, "kv and ix must be 16-byte aligned");
+  csa2::AppendArgs a{};
+  a.kv_codes = cache->kv_codes;
+  a.kv_scales = cache->kv_scales;
+  a.ix_codes = cache->ix_codes;
+  a.ix_scales = cache->ix_scales;
+  a.block_table = cache->block_table;
+  a.page_shift = __builtin_ctz((unsigned)cache->page_size);
+  a.max_pages = cache->max_pages;
+  a.num_pages = cache->num_pages;
+  a.kv = kv;
+  a.ix = ix;
+  a.entry = entry;
+  a.batch = batch;
+  a.n_new = n_new;
+  return hip_check(csa2::launch_kv_append(a, (hipStream_t)stream), "kv_append");
+}
+
+csa2_status csa2_window_append(uint8_t *codes, float *row_scale, int32_t rows, const float *x,
+                               const int32_t *row, int32_t batch, int32_t n_new, void *stream) {
+  if (!codes || !x || !row) return fail(CSA2_EINVAL, "NULL codes, x or row");
+  if (rows <= 0 || batch <= 0 || n_new < 0) return fail(CSA2_EINVAL, "rows and batch must be positive, n_new >= 0");
+  if (((uintptr_t)x & 15) || ((uintptr_t)codes & 3)) return fail(CSA2_EINVAL, "x must be 16-byte and codes 4-byte aligned");
+  return hip_check(csa2::launch_window_append(codes, row_scale, rows, x, row, batch, n_new, (hipStream_t)stream),
+                   "window_append");
+}
+
 csa2_status csa2_dequant_fp4(const uint8_t *codes, const uint8_t *scales, int64_t n_rows,
                              int32_t channels, uint16_t *out_f16, void *stream) {
   if (!codes || !scales || !out_f16) return fail(CSA2_EINVAL, "NULL pointer");

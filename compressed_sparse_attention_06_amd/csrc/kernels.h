@@ -119,6 +119,22 @@ struct MergeArgs {
   const float *part;
 };
 
+// New compressed entries written into a paged cache (one FP4 row each).
+struct AppendArgs {
+  uint8_t *kv_codes, *kv_scales, *ix_codes, *ix_scales;
+  const int32_t *block_table;
+  int32_t page_shift, max_pages, num_pages;
+  const float *kv;       // [batch][n_new][512]
+  const float *ix;       // [batch][n_new][64] or null
+  const int32_t *entry;  // [batch][n_new] entry index, < 0: none
+  int32_t batch, n_new;
+};
+
+hipError_t launch_quant_fp4(const float *x, int64_t n_rows, int32_t channels, uint8_t *codes,
+                            uint8_t *scales, hipStream_t st);
+hipError_t launch_kv_append(const AppendArgs &a, hipStream_t st);
+hipError_t launch_window_append(uint8_t *codes, float *row_scale, int32_t rows, const float *x,
+                                const int32_t *row, int32_t batch, int32_t n_new, hipStream_t st);
 hipError_t launch_fill_u32(uint32_t *p, int64_t n, uint32_t v, hipStream_t st);
 hipError_t launch_index_score(const ScoreArgs &a, int rows, hipStream_t st);
 hipError_t launch_hist(const float *scores, int32_t n_cols, int rows, uint32_t *hist,

@@ -195,6 +195,53 @@ csa2_status csa2_dequant_fp4(const uint8_t *codes, const uint8_t *scales, int64_
                              int32_t channels, uint16_t *out_f16, void *stream);
 csa2_status csa2_dequant_e4m3(const uint8_t *bytes, int64_t n, float *out, void *stream);
 
+/* ---- The write side of the cache ([P2] "FP4 量化 + Bounded Replay": main KV
+ * and indexer Q/K in E2M1 with one E4M3 scale per 16 channels, no
+ * second-level scale; the window holds the last 128 tokens in 8 bits).
+ * The pages give the formats, not the rounding. Rounding used: nearest
+ * representable value, ties to the even mantissa, saturating (6 for E2M1,
+ * 448 for E4M3); the block scale byte encodes amax/6 of its 16 channels
+ * (division in fp32) and each channel encodes x / scale (fp32); the sign bit
+ * is x < 0. Bit-exact against the oracle. The learned compressor that makes
+ * the fp32 entries is not part of this library. */
+
+/* Quantise rows: x [n_rows][channels] fp32 (16-byte aligned; channels a
+ * positive multiple of 16) -> codes [n_rows][channels/2] (channel 2j in the
+ * low nibble of byte j; 8-byte aligned) and scales [n_rows][channels/16].
+ * Used for new entries and for the decode indexer query ([batch][nq][4][64]
+ * is 4*batch*nq rows of 64). */
+csa2_status csa2_quantize_fp4(const float *x, int64_t n_rows, int32_t channels, uint8_t *codes,
+                              uint8_t *scales, void *stream);
+
+/* Writable view of a paged cache (same layout as csa2_cache). */
+typedef struct {
+  uint8_t *kv_codes;        /* [num_pages][page][256] */
+  uint8_t *kv_scales;       /* [num_pages][page][32] */
+  uint8_t *ix_codes;        /* [num_pages][page][32]; may be NULL when ix is NULL */
+  uint8_t *ix_scales;       /* [num_pages][page][4] */
+  const int32_t *block_table; /* [batch][max_pages] */
+  int32_t page_size, max_pages, num_pages;
+} csa2_cache_w;
+
+/* Append new compressed entries (one every 4 tokens): for request b and new
+ * entry j, when entry[b][j] >= 0 it is the entry index s written; the main-KV
+ * row kv[b][j][512] (and, when ix != NULL, the indexer key ix[b][j][64]) is
+ * quantised into page block_table[b][s / page_size], slot s % page_size.
+ * Entries whose page is missing (out of the table or negative) are skipped.
+ * n_entries is the caller's to advance. kv, ix: fp32, 16-byte aligned. Two
+ * entries of one call must not name the same slot. */
+csa2_status csa2_kv_append(const csa2_cache_w *cache, const float *kv, const float *ix,
+                           const int32_t *entry, int32_t batch, int32_t n_new, void *stream);
+
+/* Append window tokens to each request's ring of `rows` rows: for token j of
+ * request b, when row[b][j] is in [0, rows), x[b][j][512] (fp32, 16-byte
+ * aligned) is encoded into codes[b][row][512]. With row_scale != NULL the row
+ * is scaled first: rs = amax/448 (1 when amax is 0), stored in
+ * row_scale[b][row], and each byte encodes x / rs. The caller keeps the
+ * ring's position and length (csa2_window.length / pos0). */
+csa2_status csa2_window_append(uint8_t *codes, float *row_scale, int32_t rows, const float *x,
+                               const int32_t *row, int32_t batch, int32_t n_new, void *stream);
+
 const char *csa2_status_string(csa2_status s);
 const char *csa2_last_error(void);
 const char *csa2_version(void);

@@ -122,6 +122,16 @@ def test_other_entry_points_validation():
                                 p, C.c_size_t(1 << 30), None) == EINVAL
     assert L.csa2_dequant_fp4(p, p, 4, 48, p, None) == EINVAL
     assert L.csa2_dequant_e4m3(None, 4, p, None) == EINVAL
+    # the write side: bad sizes, alignment and missing arrays are rejected on the host
+    assert L.csa2_quantize_fp4(p, C.c_int64(4), 40, p, p, None) == EINVAL
+    assert L.csa2_quantize_fp4(C.c_void_p(0x2004), C.c_int64(4), 64, p, p, None) == EINVAL
+    assert L.csa2_quantize_fp4(None, C.c_int64(4), 64, p, p, None) == EINVAL
+    cw = csa2._CacheW(0x2000, 0x2000, 0, 0, 0x2000, 64, 4, 4)
+    assert L.csa2_kv_append(C.byref(cw), p, p, p, 1, 1, None) == EINVAL  # ix without indexer arrays
+    cw = csa2._CacheW(0x2000, 0x2000, 0x2000, 0x2000, 0x2000, 48, 4, 4)
+    assert L.csa2_kv_append(C.byref(cw), p, None, p, 1, 1, None) == EUNSUPPORTED
+    assert L.csa2_window_append(p, None, 0, p, p, 1, 1, None) == EINVAL
+    assert L.csa2_window_append(p, None, 8, C.c_void_p(0x2008), p, 1, 1, None) == EINVAL
 
 
 @pytest.mark.parametrize("mode,n_cols,k,pool,win", [
