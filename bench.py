@@ -358,6 +358,56 @@ def main():
         except Exception:
             att_traffic = None
 
+    # ---- the cache's write side: what one decode step appends, and a prefill chunk's worth ----
+    def time_calls(fn, iters):
+        """us per call: `iters` calls captured in one HIP graph and replayed, so that
+        the binding's host-side overhead is not what is timed."""
+        for i in range(3):
+            fn(i)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        s_cap = torch.cuda.Stream()
+        s_cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s_cap):
+            with torch.cuda.graph(g, stream=s_cap):
+                for i in range(iters):
+                    fn(i)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ev0.record()
+        g.replay()
+        ev1.record()
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / iters * 1e3
+
+    gen = torch.Generator(device=dev).manual_seed(11)
+    cache0 = copies[0][0][0]
+    app = {}
+    for label, n_req, n_new in (("decode_step", B, 1), ("prefill_chunk", 1, 1024)):
+        kv_new = torch.randn(n_req, n_new, 512, device=dev, generator=gen)
+        ix_new = torch.randn(n_req, n_new, 64, device=dev, generator=gen)
+        # the last n_new entries of each request are rewritten (distinct slots; entries
+        # whose page does not exist are skipped by the kernel)
+        base = torch.clamp(cache0.n_entries[:n_req, None] - n_new, min=0)
+        ent = (base + torch.arange(n_new, device=dev, dtype=torch.int32)[None, :]).to(torch.int32).contiguous()
+        tok = torch.randn(n_req, 4 * n_new, 512, device=dev, generator=gen)
+        wcodes = torch.zeros(n_req, max(128, 4 * n_new), 512, dtype=torch.uint8, device=dev)
+        wrs = torch.ones(n_req, wcodes.shape[1], dtype=torch.float32, device=dev)
+        wrow = (torch.arange(4 * n_new, device=dev, dtype=torch.int32)[None, :] % wcodes.shape[1]).repeat(n_req, 1).contiguous()
+        qx = torch.randn(n_req, 1, 4, 64, device=dev, generator=gen)
+        qxc = torch.empty(n_req, 1, 4, 32, dtype=torch.uint8, device=dev)
+        qxs = torch.empty(n_req, 1, 4, 4, dtype=torch.uint8, device=dev)
+        us_kv = time_calls(lambda i: csa2.kv_append(cache0, kv_new, ent, ix=ix_new), 20)
+        us_win = time_calls(lambda i: csa2.window_append(wcodes, tok, wrow, row_scale=wrs), 20)
+        us_q = time_calls(lambda i: csa2.quantize_fp4(qx, qxc, qxs), 20)
+        nbytes = n_req * n_new * (576 * 4 + 324) + n_req * 4 * n_new * (512 * 4 + 516)
+        app[label] = dict(requests=n_req, entries_per_request=n_new, tokens_per_request=4 * n_new,
+                          kv_append_us=round(us_kv, 2), window_append_us=round(us_win, 2),
+                          qix_quantize_us=round(us_q, 2), algorithmic_bytes=nbytes,
+                          gbps=round(nbytes / ((us_kv + us_win) * 1e-6) / 1e9, 1))
+    log(f"append: {app}")
+
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         try:
@@ -465,6 +515,7 @@ def main():
              "achieved": round(k_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
              "frac": round(k_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
              "bytes_per_launch": kb, "us_per_launch": round(k_ms * 1e3, 3)}),
+        "append": app,
         "cpu_baseline": cpu,
         "secondary": secondary,
     }
