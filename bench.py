@@ -60,6 +60,8 @@ def parse():
     p.add_argument("--workload", default=WORKLOAD,
                    choices=[WORKLOAD, WORKLOAD_128K, "ragged64_paged_20layer", "prefill_4096q_128k"],
                    help="the workload of the JSON line (default: the 1M-context decode step)")
+    p.add_argument("--no-topk-compare", action="store_true",
+                   help="skip the standalone top-K comparison against torch.topk")
     p.add_argument("--no-secondary", action="store_true",
                    help="skip the 128K-context (batch 32) workload reported beside the main one")
     return p.parse_args()
@@ -408,6 +410,42 @@ def main():
                           gbps=round(nbytes / ((us_kv + us_win) * 1e-6) / 1e9, 1))
     log(f"append: {app}")
 
+    # ---- standalone top-K against torch.topk on the same scores (event-timed calls) ----
+    topk_cmp = []
+    if not args.no_topk_compare:
+        for rows, n, kk in ((8, 262144, 2048), (8, 16384, 2048), (32, 32768, 2048),
+                            (64, 16384, 2048), (4096, 32768, 2048)):
+            sc = torch.randn(rows, 1, n, device=dev, generator=gen)
+            out_i = torch.empty(rows, 1, kk, dtype=torch.int32, device=dev)
+            wsk = csa2.alloc_workspace(csa2.workspace_bytes("R", rows, 1, n, kk), dev)
+            tv = torch.empty(rows, 1, kk, device=dev)
+            ti = torch.empty(rows, 1, kk, dtype=torch.int64, device=dev)
+            iters = 10 if rows * n > 1e8 else 30
+
+            def ours(i):
+                csa2.topk(sc, kk, out=out_i, ws=wsk)
+
+            def theirs(i):
+                torch.topk(sc, kk, dim=-1, sorted=False, out=(tv, ti))
+
+            res = {}
+            for nm, fn in (("csa2_topk", ours), ("torch_topk", theirs)):
+                for i in range(3):
+                    fn(i)
+                torch.cuda.synchronize()
+                ev0.record()
+                for i in range(iters):
+                    fn(i)
+                ev1.record()
+                torch.cuda.synchronize()
+                res[nm] = ev0.elapsed_time(ev1) / iters * 1e3
+            same = bool((torch.sort(ti, dim=-1).values.to(torch.int32) == out_i).all().item())
+            topk_cmp.append(dict(rows=rows, n=n, k=kk, csa2_us=round(res["csa2_topk"], 1),
+                                 torch_us=round(res["torch_topk"], 1),
+                                 speedup=round(res["torch_topk"] / res["csa2_topk"], 2), same_ids=same))
+            del sc, out_i, wsk, tv, ti
+        log(f"topk vs torch.topk: {topk_cmp}")
+
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         try:
@@ -516,6 +554,7 @@ def main():
              "frac": round(k_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
              "bytes_per_launch": kb, "us_per_launch": round(k_ms * 1e3, 3)}),
         "append": app,
+        "topk_vs_torch": topk_cmp,
         "cpu_baseline": cpu,
         "secondary": secondary,
     }
