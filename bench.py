@@ -58,7 +58,8 @@ def parse():
     p.add_argument("--copy-probe-mb", type=int, default=0,
                    help="also run a plain device copy of this size (counter calibration)")
     p.add_argument("--workload", default=WORKLOAD,
-                   choices=[WORKLOAD, WORKLOAD_128K, "ragged64_paged_20layer", "prefill_4096q_128k"],
+                   choices=[WORKLOAD, WORKLOAD_128K, "ragged64_paged_20layer", "prefill_4096q_128k",
+                            "b8_1m_spec6"],
                    help="the workload of the JSON line (default: the 1M-context decode step)")
     p.add_argument("--no-topk-compare", action="store_true",
                    help="skip the standalone top-K comparison against torch.topk")
@@ -100,17 +101,24 @@ def step_bytes(wl) -> int:
 
 
 def prefill_bytes(wl) -> int:
-    """Algorithmic bytes of a prefill chunk: each request's indexer keys once
-    (36 B per entry), and per query 160 B of indexer query and weights plus
-    A(K) (its own gathered rows, window rows, q and out), per layer."""
+    """Algorithmic bytes when each request has several query rows with their own
+    positions (a prefill chunk, or the drafts of a speculative step): each
+    request's indexer keys once (36 B per entry, shared by its queries), and per
+    query row 160 B of indexer query and weights, 4 B per pool id written (Full)
+    or 40 B per pool entry rescored (Reindex), plus A(K), per layer."""
     total = 0
     for L in wl.layers:
         c = wl.caches[L.cache_id]
         for b in range(wl.batch):
             N = int(c.n_entries[b])
-            K = min(wl.k, N)
-            A = 292 * K + wl.window * 512 + 32768 + 32832
-            total += (36 * N if L.mode == "F" else 0) + wl.nq * (160 * (L.mode != "U") + A)
+            K, P = min(wl.k, N), min(wl.pool, N)
+            A = 292 * K + wl.window * (512 + (4 if L.win.row_scale is not None else 0)) + 32768 + 32832
+            if L.mode == "F":
+                total += 36 * N + wl.nq * (160 + 4 * P + A)
+            elif L.mode == "R":
+                total += wl.nq * (40 * P + 160 + A)
+            else:
+                total += wl.nq * A
     return total
 
 
@@ -143,10 +151,11 @@ def prefill_score_flops(wl) -> int:
 
 
 def score_kernel_bytes(wl) -> int:
-    """Algorithmic bytes of one launch of the Full-layer scoring kernel:
-    36 B per scored entry + 160 B of indexer query and weights per query."""
+    """Algorithmic bytes of one launch of the Full-layer scoring kernel: 36 B per
+    entry of each request (once, whatever its number of query rows) + 160 B of
+    indexer query and weights per query row."""
     c = wl.caches[0]
-    return int(sum(36 * int(n) + 160 for n in c.n_entries)) * wl.nq
+    return int(sum(36 * int(n) + 160 * wl.nq for n in c.n_entries))
 
 
 def upload_chains(wl, n_copies, dev):

@@ -348,9 +348,13 @@ csa2_status csa2_index_score(const csa2_cache *cache, const uint8_t *qix_codes,
   a.hist = hist;
   a.write_masked = 1;
   a.chunk = kScoreChunk;
-  if (use_prefill_scoring(nq, cand, cache->page_size)) {
+  if (use_prefill_scoring(nq, cand, cache->page_size) || (!cand && nq > 1)) {
+    // several query rows per request: one read of the keys serves all of them
     a.hist = nullptr;
-    s = hip_check(csa2::launch_prefill_score(a, batch, (hipStream_t)stream), "index_score");
+    s = hip_check(use_prefill_scoring(nq, cand, cache->page_size)
+                      ? csa2::launch_prefill_score(a, batch, (hipStream_t)stream)
+                      : csa2::launch_index_score_mq(a, batch, (hipStream_t)stream),
+                  "index_score");
     if (s || !hist) return s;
     return hip_check(csa2::launch_hist(scores, a.n_cols, batch * nq, hist, (hipStream_t)stream,
                                        cache->n_entries, q_pos, nq), "hist");
@@ -458,9 +462,15 @@ csa2_status csa2_layer_step(const csa2_layer_args *p, void *stream) {
     const SelTarget tgr{p->k, p->idx_out, p->k};
     const SelTarget *tg = p->mode == CSA2_FULL ? tgf : &tgr;
     const int ntarget = (p->mode == CSA2_FULL && p->pool > 0) ? 2 : 1;
-    if (p->mode == CSA2_FULL && use_prefill_scoring(p->nq, nullptr, p->cache->page_size)) {
+    if (p->mode == CSA2_FULL && (use_prefill_scoring(p->nq, nullptr, p->cache->page_size) || p->nq > 1)) {
+      // several query rows per request share each read of the keys; the
+      // histogram (chunked selection only) is a pass of its own
       a.hist = nullptr;
-      if ((s = hip_check(csa2::launch_prefill_score(a, p->batch, st), "index_score"))) return s;
+      s = hip_check(use_prefill_scoring(p->nq, nullptr, p->cache->page_size)
+                        ? csa2::launch_prefill_score(a, p->batch, st)
+                        : csa2::launch_index_score_mq(a, p->batch, st),
+                    "index_score");
+      if (s) return s;
       if (L.compact &&
           (s = hip_check(csa2::launch_hist(scores, n_cols, rows, (uint32_t *)(ws + L.hist), st,
                                            p->cache->n_entries, p->q_pos, p->nq), "hist")))

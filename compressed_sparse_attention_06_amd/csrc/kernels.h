@@ -141,6 +141,8 @@ hipError_t launch_hist(const float *scores, int32_t n_cols, int rows, uint32_t *
                        hipStream_t st, const int32_t *n_entries = nullptr,
                        const int32_t *q_pos = nullptr, int32_t nq = 1);
 hipError_t launch_prefill_score(const ScoreArgs &a, int batch, hipStream_t st);
+// several query rows per request (2..63): key loads shared by the rows; no histogram
+hipError_t launch_index_score_mq(const ScoreArgs &a, int batch, hipStream_t st);
 hipError_t launch_compact(const CompactArgs &a, int rows, hipStream_t st);
 hipError_t launch_final(const FinalArgs &a, int rows, int ntarget, hipStream_t st);
 hipError_t launch_select_direct(const DirectArgs &a, int rows, int ntarget, hipStream_t st);

@@ -293,6 +293,11 @@ CONFIGS = {
         contexts=[131072], layers="F", k=2048, pool=0, nq=4096, prefill=True, stream=4),
     "ragged64_paged_20layer": dict(
         contexts=None, layers=_pattern20(), k=2048, pool=16384, shuffle=True, stream=5),
+    # speculative verification: the last 6 tokens (5 drafts + 1) of each 1M-token
+    # request are queries, each with its own position (block-causal visibility
+    # among the newest entries, causal window)
+    "b8_1m_spec6": dict(
+        contexts=[1 << 20] * 8, layers="FRUUUU", k=2048, pool=16384, nq=6, prefill=True, stream=6),
 }
 
 

@@ -59,6 +59,13 @@ def test_full_size_b8_1m():
     _check_requests("b8_1m_full_reindex_reuse4", [5])
 
 
+def test_full_size_spec6_1m():
+    """8 requests x 1,048,576 tokens with 6 query rows each (5 drafts + 1 of a
+    speculative step): per-query positions, block-causal visibility among the
+    newest entries, causal windows, [Full, Reindex, Reuse x4]."""
+    _check_requests("b8_1m_spec6", [2])
+
+
 def test_full_size_ragged_paged():
     """64 ragged requests (log-uniform 4K..1M tokens) in shuffled 64-entry pages, 20 layers."""
     name = "ragged64_paged_20layer"
