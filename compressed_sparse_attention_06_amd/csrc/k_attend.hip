@@ -530,24 +530,24 @@ __global__ __launch_bounds__(512) void k_attend_seg(AttendArgs a, SegArgs s) {
     // one row's units [x, xe): Q first, then the pipeline's prologue
     const int32_t row = (int32_t)(x / U);
     const int64_t xe = min(u_end, (int64_t)(row + 1) * U);
-    // Q loads first, then the ids of the first three units; Q is converted
-    // while the ids are in flight (loads complete in issue order)
+    // the first unit's rows are requested before Q is converted, so the id ->
+    // page -> row chain and the conversion overlap
     SegQ q;
     SegFetch fc, fn;
     int32_t id2;
+    SegSlice sc;
     {
       float qv[32];
       seg_load_q(a, row, qv);
       fc.id = seg_fetch_id(a, x, xe, U, prow);
       fn.id = seg_fetch_id(a, x + 1, xe, U, prow);
       id2 = seg_fetch_id(a, x + 2, xe, U, prow);
+      fc.page = seg_fetch_page(a, x, xe, U, prow, fc.id);
+      fn.page = seg_fetch_page(a, x + 1, xe, U, prow, fn.id);
+      seg_fetch_rows(a, x, xe, U, prow, g, fc, sc);
       seg_prepare_q(a, sh, qv, q);
     }
     // pipeline: rows of unit x in sc, id and page word of x + 1 in fn, id of x + 2 in id2
-    fc.page = seg_fetch_page(a, x, xe, U, prow, fc.id);
-    fn.page = seg_fetch_page(a, x + 1, xe, U, prow, fn.id);
-    SegSlice sc;
-    seg_fetch_rows(a, x, xe, U, prow, g, fc, sc);
     const int32_t nent = a.c.n_entries[row / a.nq];
     v4f accO[4];
 #pragma unroll

@@ -252,6 +252,49 @@ def test_sparse_attend_edge_cases():
     assert_attention_close(g_out.cpu().numpy(), g_lse.cpu().numpy(), o_out, o_lse, "no window")
 
 
+# How the attention work is cut: each row's set (k entries, then the window from
+# k rounded up to 16) in units of 128 positions, shared over at most 256
+# workgroups. These cases cover k below, at and off a multiple of 16, sets of
+# one unit, rows cut between workgroups at many offsets (T > 256 units, with
+# 2..20 units per workgroup), several query rows per request with their own
+# causal windows, and no window.
+UNIT_CASES = [
+    dict(contexts=[4 * 300, 4 * 40], k=1, nq=1, win=True),                       # U = 2
+    dict(contexts=[4 * 300], k=13, nq=1, win=False),                              # one unit, tail lanes empty
+    dict(contexts=[4 * 500, 4 * 200, 4 * 900], k=300, nq=1, win=True),            # k16 = 304
+    dict(contexts=[4 * 700] * 20, k=256, nq=3, win=True, prefill=True),           # 60 rows x 3 units
+    dict(contexts=[4 * 2200] * 30, k=2048, nq=1, win=True),                       # 30 x 17 units over 256
+    dict(contexts=[4 * 3000] * 6, k=2048, nq=50, win=True, prefill=True),         # 300 rows x 17 units
+]
+
+
+@pytest.mark.parametrize("case", UNIT_CASES, ids=["k1", "k13_nowin", "k300", "nq3_prefill", "b30_k2048",
+                                                 "nq50_k2048"])
+def test_sparse_attend_unit_geometry(case):
+    _log(f"sparse_attend geometry {case}")
+    wl = make_small_decode(contexts=case["contexts"], layers="F", k=case["k"], nq=case["nq"],
+                           prefill=case.get("prefill", False), page_size=32, shuffle=True, row_scale=True)
+    c, L = wl.caches[0], wl.layers[0]
+    rng = np.random.default_rng(len(case["contexts"]) * 7 + case["k"])
+    B, nq, k = L.q.shape[0], L.q.shape[1], wl.k
+    # ids: random visible entries, ascending, a few pads and out-of-range ids
+    idx = np.full((B, nq, k), -1, np.int32)
+    for b in range(B):
+        n = int(c.n_entries[b])
+        for q in range(nq):
+            lim = n if wl.q_pos is None else min(n, (int(wl.q_pos[b, q]) + 1) // 4)
+            m = min(k, lim)
+            if m > 0:
+                idx[b, q, :m] = np.sort(rng.choice(lim, size=m, replace=False))
+            if k > 4 and m == k:
+                idx[b, q, -1] = n + 5  # out of range: must be ignored
+    win = L.win if case["win"] else None
+    qp = wl.q_pos
+    g_out, g_lse = csa2.sparse_attend(dev_cache(c), t(idx), t(L.q), dev_window(win), q_pos=t(qp))
+    o_out, o_lse, _ = oracle.sparse_attend(c, idx, L.q, win, q_pos=qp, sm_scale=TAU)
+    assert_attention_close(g_out.cpu().numpy(), g_lse.cpu().numpy(), o_out, o_lse, f"geometry {case}")
+
+
 def test_sparse_attend_large_logits():
     """Rows of 2688 and a large query: the running max keeps the softmax finite."""
     wl = make_small_decode([4 * 64], layers="F", k=4)
