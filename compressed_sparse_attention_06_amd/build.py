@@ -29,9 +29,10 @@ def _run(cmd):
     return r.returncode, err
 
 
-# per-file additions: the attention kernels carry no NaN (every logit and
-# weight is finite or -inf), which lets max reductions skip NaN quieting
-FILE_FLAGS = {"k_attend.hip": ["-fno-honor-nans"]}
+# per-file additions: the attention kernels and the fused prefill selection
+# carry no NaN (logits, weights and index scores are finite or -inf), which
+# lets max reductions and ReLUs skip NaN quieting
+FILE_FLAGS = {"k_attend.hip": ["-fno-honor-nans"], "k_prefill_topk.hip": ["-fno-honor-nans"]}
 
 
 def build(verbose: bool = False) -> str:

@@ -39,6 +39,15 @@ constexpr int32_t kPrefillQueries = 64;  // queries per request from which scori
 bool use_prefill_scoring(int32_t nq, const int32_t *cand, int32_t page_size) {
   return nq >= kPrefillQueries && !cand && page_size >= 16;
 }
+constexpr int64_t kFusedTopkMinRows = 1024;  // query rows from which a prefill chunk selects without a score matrix
+
+// A Full layer over a prefill chunk of enough query rows (so that 16 rows per
+// workgroup fill the GPU), entries up to kPrefillTopkMaxCols and no pool:
+// scoring and top-K run as one kernel that keeps no score matrix.
+bool use_fused_topk(csa2_mode mode, int64_t batch, int32_t nq, int64_t n_cols, int32_t pool) {
+  return mode == CSA2_FULL && pool == 0 && nq >= kPrefillQueries && batch * nq >= kFusedTopkMinRows &&
+         n_cols >= 1 && n_cols <= csa2::kPrefillTopkMaxCols;
+}
 constexpr int64_t kMaxSelectCols = CSA2_MAX_SELECT_COLS;
 static_assert(CSA2_MAX_SELECT_COLS <= SEL_MAX_WG * 8192, "the chunked selection takes SEL_MAX_WG chunks of 8192");
 
@@ -65,6 +74,7 @@ struct WsLayout {
          total = 0;
   bool compact = false;   // chunked compaction + final selection (long rows)
   bool row_sel = false;   // one workgroup per row, keys in registers (rows up to kSelectRowMax)
+  bool fused = false;     // prefill scoring fused with the top-K: no score region
   int max_wg = 0, chunk = 0;
   int64_t seg_stride = 0;
   // attention: units of 128 positions, U per row, T in all, over G workgroups
@@ -89,10 +99,12 @@ void attend_geometry(WsLayout &L, int64_t rows, int32_t k, int32_t win_cap) {
                                     (int32_t)(owner(r * L.att_U + L.att_U - 1) - owner(r * L.att_U) + 1));
 }
 
-WsLayout ws_layout(csa2_mode mode, int64_t rows, int64_t n_cols, int32_t k, int32_t win_cap, int ntarget) {
+WsLayout ws_layout(csa2_mode mode, int64_t rows, int64_t n_cols, int32_t k, int32_t win_cap, int ntarget,
+                   bool fused = false) {
   WsLayout L;
   size_t off = 0;
-  if (mode == CSA2_FULL || mode == CSA2_REINDEX) {
+  L.fused = fused;
+  if ((mode == CSA2_FULL || mode == CSA2_REINDEX) && !fused) {
     // one workgroup per row pays off once there are enough rows to fill the
     // GPU; few long rows go through the chunked path, which spreads each row
     // over many workgroups
@@ -322,7 +334,9 @@ size_t csa2_workspace_bytes(csa2_mode mode, int32_t batch, int32_t nq, int32_t n
   if (batch <= 0 || nq <= 0 || k <= 0) return 0;
   if (mode == CSA2_REUSE) n_cols = 0;
   const int ntarget = (mode == CSA2_FULL && pool > 0) ? 2 : 1;
-  return ws_layout(mode, (int64_t)batch * nq, n_cols < 0 ? 0 : n_cols, k, win_cap, ntarget).total;
+  return ws_layout(mode, (int64_t)batch * nq, n_cols < 0 ? 0 : n_cols, k, win_cap, ntarget,
+                   use_fused_topk(mode, batch, nq, n_cols, pool))
+      .total;
 }
 
 csa2_status csa2_index_score(const csa2_cache *cache, const uint8_t *qix_codes,
@@ -430,13 +444,27 @@ csa2_status csa2_layer_step(const csa2_layer_args *p, void *stream) {
     return fail(CSA2_EUNSUPPORTED, "more than %lld entries per row to select from", (long long)kMaxSelectCols);
   const int32_t n_cols = p->mode == CSA2_FULL ? capacity : (p->mode == CSA2_REINDEX ? p->pool : 0);
   const int32_t wcap = win_cap_of(p->win, p->q_pos);
-  const WsLayout L = ws_layout(p->mode, rows, n_cols, p->k, wcap, (p->mode == CSA2_FULL && p->pool > 0) ? 2 : 1);
+  const WsLayout L = ws_layout(p->mode, rows, n_cols, p->k, wcap, (p->mode == CSA2_FULL && p->pool > 0) ? 2 : 1,
+                               use_fused_topk(p->mode, p->batch, p->nq, n_cols, p->pool));
   if ((s = check_ws(p->ws, p->ws_bytes, L.total))) return s;
   hipStream_t st = (hipStream_t)stream;
   char *ws = (char *)p->ws;
 
   const int32_t *att_idx = p->idx_in;
-  if (selecting) {
+  if (L.fused) {
+    csa2::PrefillTopkArgs a{};
+    a.c = dev_cache(p->cache);
+    a.qix_codes = p->qix_codes;
+    a.qix_scales = p->qix_scales;
+    a.w = p->w;
+    a.q_pos = p->q_pos;
+    a.nq = p->nq;
+    a.n_cols = n_cols;
+    a.k = p->k;
+    a.idx_out = p->idx_out;
+    if ((s = hip_check(csa2::launch_prefill_topk(a, p->batch, st), "prefill_topk"))) return s;
+    att_idx = p->idx_out;
+  } else if (selecting) {
     float *scores = (float *)(ws + L.scores);
     if (L.compact) {
       s = hip_check(csa2::launch_fill_u32((uint32_t *)(ws + L.hist), (int64_t)((L.zero_end - L.hist) / 4), 0u, st),

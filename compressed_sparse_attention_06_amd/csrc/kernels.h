@@ -141,6 +141,21 @@ hipError_t launch_hist(const float *scores, int32_t n_cols, int rows, uint32_t *
                        hipStream_t st, const int32_t *n_entries = nullptr,
                        const int32_t *q_pos = nullptr, int32_t nq = 1);
 hipError_t launch_prefill_score(const ScoreArgs &a, int batch, hipStream_t st);
+
+// Prefill chunk, scoring fused with the per-query top-K (no score matrix):
+// rows of at most kPrefillTopkMaxCols entries, 16 query rows per workgroup.
+constexpr int32_t kPrefillTopkMaxCols = 32768;
+struct PrefillTopkArgs {
+  DevCache c;
+  const uint8_t *qix_codes, *qix_scales;  // [rows][4][32], [rows][4][4]
+  const float *w;                         // [rows][4]
+  const int32_t *q_pos;                   // [rows] or null
+  int32_t nq;
+  int32_t n_cols;                         // cache capacity (bounds the visible entries)
+  int32_t k;
+  int32_t *idx_out;                       // [rows][k] ascending ids, then -1
+};
+hipError_t launch_prefill_topk(const PrefillTopkArgs &a, int batch, hipStream_t st);
 // several query rows per request (2..63): key loads shared by the rows; no histogram
 hipError_t launch_index_score_mq(const ScoreArgs &a, int batch, hipStream_t st);
 hipError_t launch_compact(const CompactArgs &a, int rows, hipStream_t st);

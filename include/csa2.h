@@ -156,7 +156,12 @@ csa2_status csa2_sparse_attend(const csa2_cache *cache, const int32_t *idx, int3
  *           holds the same selected set, in pool order rather than ascending
  *           once pool > 4096.
  *  REUSE:   idx_in [batch][nq][k] inherited; no indexer work; attend.
- * All modes use this layer's own q and window. */
+ * All modes use this layer's own q and window.
+ * A FULL call over a prefill chunk (nq >= 64, batch*nq >= 1024, pool = 0,
+ * capacity <= 32768 entries) scores and selects in one pass per query group
+ * and keeps no score matrix; csa2_workspace_bytes sizes its workspace
+ * accordingly. The selected sets are the same as those of csa2_index_score
+ * followed by csa2_topk on the same inputs. */
 typedef struct {
   csa2_mode mode;
   const csa2_cache *cache;

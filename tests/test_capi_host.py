@@ -148,3 +148,23 @@ def test_workspace_sizes(mode, n_cols, k, pool, win):
     if mode != csa2.REUSE:
         assert nb >= 8 * n_cols * 4
     assert csa2.workspace_bytes(mode, 0, 1, n_cols, k, pool, win) == 0
+
+
+@pytest.mark.parametrize("batch,nq,n_cols,pool,fused", [
+    (1, 4096, 32768, 0, True),      # the 4096-query chunk of a 128K context
+    (2, 512, 32768, 0, True),       # 1024 rows over two requests
+    (1, 4096, 32768, 2048, False),  # a pool to select as well
+    (1, 1000, 32768, 0, False),     # too few rows to fill the GPU 16 at a time
+    (32, 32, 32768, 0, False),      # fewer than 64 query rows per request
+    (1, 4096, 65536, 0, False),     # more entries than one row's bitmap covers
+])
+def test_fused_prefill_topk_workspace(batch, nq, n_cols, pool, fused):
+    """The fused prefill selection keeps no score matrix: its Full-layer
+    workspace is exactly the attention's; every other Full call reserves the
+    score rows."""
+    full = csa2.workspace_bytes(csa2.FULL, batch, nq, n_cols, 256, pool, 128)
+    att = csa2.workspace_bytes(csa2.REUSE, batch, nq, 0, 256, 0, 128)
+    if fused:
+        assert full == att
+    else:
+        assert full >= att + batch * nq * n_cols * 4
