@@ -519,11 +519,14 @@ __global__ __launch_bounds__(PT_NT) void k_prefill_topk(PrefillTopkArgs a) {
     if (general) pt_sweep<SW_GENERAL, TILEPAGE>(a, sh, b, A, W);
     else pt_sweep<SW_COLLECT_F, TILEPAGE>(a, sh, b, A, W);
     __syncthreads();
-    for (int half = 0; half < 2; ++half) {
-      const int r = 2 * wave + half;
-      const int md = sh.mode[r];
-      if (md == PT_HIST) pt_resolve_hist(sh, r);
-      else if (md == PT_COLLECT && sh.mode[r ^ 1] != PT_HIST) pt_resolve_collect(sh, r);
+    {
+      // modes as the sweep saw them (resolving one row of the pair changes its mode)
+      const int md2[2] = {sh.mode[2 * wave], sh.mode[2 * wave + 1]};
+      for (int half = 0; half < 2; ++half) {
+        const int r = 2 * wave + half;
+        if (md2[half] == PT_HIST) pt_resolve_hist(sh, r);
+        else if (md2[half] == PT_COLLECT && md2[half ^ 1] != PT_HIST) pt_resolve_collect(sh, r);
+      }
     }
     __syncthreads();
   }

@@ -98,3 +98,22 @@ def test_prefill_topk_fused_few_positive():
     kill = rng.random(c.ix_codes.shape[0] * c.ix_codes.shape[1]) < 0.95
     c.ix_codes.reshape(-1, c.ix_codes.shape[-1])[kill] = 0
     _check(wl, "few positive")
+
+
+def test_prefill_topk_fused_mixed_refinement():
+    """Every third query's indexer vector zeroed: those rows score all entries
+    0 and refine down to their lowest ids while the rows beside them (sharing
+    LDS with them in pairs) collect after one histogram; both kinds must come
+    out whole."""
+    _log("fused prefill top-k, rows refining beside rows collecting")
+    wl = make_small_decode([4 * 3000], layers="F", k=300, nq=1024, prefill=True, page_size=64,
+                           shuffle=True)
+    L = wl.layers[0]
+    tied = np.arange(wl.nq) % 3 == 0
+    L.qix_codes[:, tied] = 0
+    g = _check(wl, "mixed refinement")
+    V = _visible(wl)
+    for r in np.nonzero(tied)[0]:
+        n = min(wl.k, int(V[0, r]))
+        assert (g[0, r, :n] == np.arange(n)).all() and (g[0, r, n:] == -1).all(), f"row {r}"
+    assert ((g[0, ~tied] >= 0).sum(axis=-1) == wl.k).all()
