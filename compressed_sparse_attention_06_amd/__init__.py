@@ -69,7 +69,7 @@ def lib():
         L.csa2_status_string.restype = C.c_char_p
         L.csa2_version.restype = C.c_char_p
         for name in ("csa2_index_score", "csa2_topk", "csa2_sparse_attend", "csa2_layer_step",
-                     "csa2_dequant_fp4", "csa2_dequant_e4m3", "csa2_quantize_fp4", "csa2_kv_append",
+                     "csa2_index_topk", "csa2_dequant_fp4", "csa2_dequant_e4m3", "csa2_quantize_fp4", "csa2_kv_append",
                      "csa2_window_append"):
             getattr(L, name).restype = C.c_int
         _lib = L
@@ -77,7 +77,7 @@ def lib():
 
 
 EXPORTS = ["csa2_index_score", "csa2_topk", "csa2_sparse_attend", "csa2_layer_step",
-           "csa2_workspace_bytes", "csa2_dequant_fp4", "csa2_dequant_e4m3",
+           "csa2_index_topk", "csa2_workspace_bytes", "csa2_dequant_fp4", "csa2_dequant_e4m3",
            "csa2_quantize_fp4", "csa2_kv_append", "csa2_window_append",
            "csa2_status_string", "csa2_last_error", "csa2_version"]
 
@@ -202,6 +202,47 @@ def index_score(cache: Cache, qix_codes, qix_scales, w, q_pos=None, cand=None, o
                                   _ptr(cand), C.c_int32(n_cand), C.c_int32(B), C.c_int32(nq),
                                   _ptr(out), _ptr(hist), _stream()))
     return out
+
+
+class IndexTopkCall:
+    """Pre-marshalled arguments of one csa2_index_topk call: a Full layer's
+    scoring and selection without attention (reusable in a timed loop)."""
+
+    def __init__(self, cache: Cache, qix_codes, qix_scales, w, k: int, q_pos=None, pool: int = 0,
+                 idx_out=None, pool_out=None, ws=None):
+        B, nq = qix_codes.shape[0], qix_codes.shape[1]
+        _dev(qix_codes, torch.uint8, "qix_codes", (B, nq, 4, 32))
+        _dev(qix_scales, torch.uint8, "qix_scales", (B, nq, 4, 4))
+        _dev(w, torch.float32, "w", (B, nq, 4))
+        _dev(q_pos, torch.int32, "q_pos", (B, nq))
+        dev = qix_codes.device
+        if idx_out is None:
+            idx_out = torch.empty(B, nq, k, dtype=torch.int32, device=dev)
+        _dev(idx_out, torch.int32, "idx_out", (B, nq, k))
+        if pool > 0:
+            if pool_out is None:
+                pool_out = torch.empty(B, nq, pool, dtype=torch.int32, device=dev)
+            _dev(pool_out, torch.int32, "pool_out", (B, nq, pool))
+        need = workspace_bytes(FULL, B, nq, cache.capacity, k, pool, 0)
+        if ws is None:
+            ws = alloc_workspace(need, dev)
+        self.keep = (cache, qix_codes, qix_scales, w, q_pos, ws)
+        self.cs = cache.struct()
+        self.args = (C.byref(self.cs), _ptr(qix_codes), _ptr(qix_scales), _ptr(w), _ptr(q_pos),
+                     C.c_int32(B), C.c_int32(nq), C.c_int32(k), C.c_int32(pool), _ptr(idx_out),
+                     _ptr(pool_out), _ptr(ws), C.c_size_t(ws.numel()))
+        self.idx_out, self.pool_out = idx_out, pool_out
+
+    def __call__(self, stream=None):
+        st = _stream() if stream is None else C.c_void_p(stream)
+        _check(lib().csa2_index_topk(*self.args, st))
+        return self
+
+
+def index_topk(cache: Cache, qix_codes, qix_scales, w, k: int, q_pos=None, pool: int = 0):
+    """A Full layer's top-k (and pool) without attention -> (idx, pool or None)."""
+    c = IndexTopkCall(cache, qix_codes, qix_scales, w, k, q_pos=q_pos, pool=pool)()
+    return c.idx_out, c.pool_out
 
 
 def topk(scores, k: int, cand=None, out=None, ws=None):

@@ -411,46 +411,12 @@ csa2_status csa2_sparse_attend(const csa2_cache *cache, const int32_t *idx, int3
                     (hipStream_t)stream);
 }
 
-csa2_status csa2_layer_step(const csa2_layer_args *p, void *stream) {
-  if (!p) return fail(CSA2_EINVAL, "args is NULL");
-  const bool selecting = p->mode == CSA2_FULL || p->mode == CSA2_REINDEX;
-  if (p->mode != CSA2_FULL && p->mode != CSA2_REINDEX && p->mode != CSA2_REUSE)
-    return fail(CSA2_EINVAL, "unknown mode %d", (int)p->mode);
-  csa2_status s = check_cache(p->cache, true, selecting);
-  if (s) return s;
-  if ((s = check_window(p->win))) return s;
-  if (!p->q || !p->out || !p->lse) return fail(CSA2_EINVAL, "NULL q, out or lse");
-  if (p->batch <= 0 || p->nq <= 0) return fail(CSA2_EINVAL, "batch (%d) and nq (%d) must be positive", p->batch, p->nq);
-  if (p->k <= 0 || p->k > CSA2_MAX_K) return fail(CSA2_EINVAL, "k = %d outside [1, %d]", p->k, CSA2_MAX_K);
-  if (!isfinite(p->sm_scale)) return fail(CSA2_EINVAL, "sm_scale is not finite");
-  if (selecting && (!p->qix_codes || !p->qix_scales || !p->w || !p->idx_out))
-    return fail(CSA2_EINVAL, "a selecting layer needs qix_codes, qix_scales, w and idx_out");
-  if (p->mode == CSA2_FULL && p->pool != 0) {
-    if (p->pool < p->k || p->pool > CSA2_MAX_POOL)
-      return fail(CSA2_EINVAL, "pool %d outside [k=%d, %d]", p->pool, p->k, CSA2_MAX_POOL);
-    if (!p->pool_out) return fail(CSA2_EINVAL, "pool > 0 needs pool_out");
-  }
-  if (p->mode == CSA2_FULL && p->pool < 0) return fail(CSA2_EINVAL, "negative pool");
-  if (p->mode == CSA2_REINDEX) {
-    if (!p->idx_in) return fail(CSA2_EINVAL, "a Reindex layer needs the pool in idx_in");
-    if (p->pool < p->k || p->pool > CSA2_MAX_POOL)
-      return fail(CSA2_EINVAL, "pool %d outside [k=%d, %d]", p->pool, p->k, CSA2_MAX_POOL);
-  }
-  if (p->mode == CSA2_REUSE && !p->idx_in) return fail(CSA2_EINVAL, "a Reuse layer needs the inherited top-k in idx_in");
-
-  const int rows = p->batch * p->nq;
-  const int32_t capacity = p->cache->max_pages * p->cache->page_size;
-  if (selecting && (int64_t)(p->mode == CSA2_FULL ? capacity : p->pool) > kMaxSelectCols)
-    return fail(CSA2_EUNSUPPORTED, "more than %lld entries per row to select from", (long long)kMaxSelectCols);
-  const int32_t n_cols = p->mode == CSA2_FULL ? capacity : (p->mode == CSA2_REINDEX ? p->pool : 0);
-  const int32_t wcap = win_cap_of(p->win, p->q_pos);
-  const WsLayout L = ws_layout(p->mode, rows, n_cols, p->k, wcap, (p->mode == CSA2_FULL && p->pool > 0) ? 2 : 1,
-                               use_fused_topk(p->mode, p->batch, p->nq, n_cols, p->pool));
-  if ((s = check_ws(p->ws, p->ws_bytes, L.total))) return s;
-  hipStream_t st = (hipStream_t)stream;
+// Scoring and selection of a Full or Reindex layer into idx_out (and
+// pool_out): everything csa2_layer_step does before it attends.
+csa2_status run_layer_select(const csa2_layer_args *p, const WsLayout &L, int32_t n_cols, hipStream_t st) {
+  csa2_status s = CSA2_OK;
   char *ws = (char *)p->ws;
-
-  const int32_t *att_idx = p->idx_in;
+  const int rows = p->batch * p->nq;
   if (L.fused) {
     csa2::PrefillTopkArgs a{};
     a.c = dev_cache(p->cache);
@@ -463,8 +429,7 @@ csa2_status csa2_layer_step(const csa2_layer_args *p, void *stream) {
     a.k = p->k;
     a.idx_out = p->idx_out;
     if ((s = hip_check(csa2::launch_prefill_topk(a, p->batch, st), "prefill_topk"))) return s;
-    att_idx = p->idx_out;
-  } else if (selecting) {
+  } else {
     float *scores = (float *)(ws + L.scores);
     if (L.compact) {
       s = hip_check(csa2::launch_fill_u32((uint32_t *)(ws + L.hist), (int64_t)((L.zero_end - L.hist) / 4), 0u, st),
@@ -512,10 +477,95 @@ csa2_status csa2_layer_step(const csa2_layer_args *p, void *stream) {
     else
       s = run_select(L, ws, rows, n_cols, p->idx_in, nullptr, nullptr, p->nq, tg, 1, true, scores, st);
     if (s) return s;
+  }
+  return s;
+}
+
+csa2_status csa2_layer_step(const csa2_layer_args *p, void *stream) {
+  if (!p) return fail(CSA2_EINVAL, "args is NULL");
+  const bool selecting = p->mode == CSA2_FULL || p->mode == CSA2_REINDEX;
+  if (p->mode != CSA2_FULL && p->mode != CSA2_REINDEX && p->mode != CSA2_REUSE)
+    return fail(CSA2_EINVAL, "unknown mode %d", (int)p->mode);
+  csa2_status s = check_cache(p->cache, true, selecting);
+  if (s) return s;
+  if ((s = check_window(p->win))) return s;
+  if (!p->q || !p->out || !p->lse) return fail(CSA2_EINVAL, "NULL q, out or lse");
+  if (p->batch <= 0 || p->nq <= 0) return fail(CSA2_EINVAL, "batch (%d) and nq (%d) must be positive", p->batch, p->nq);
+  if (p->k <= 0 || p->k > CSA2_MAX_K) return fail(CSA2_EINVAL, "k = %d outside [1, %d]", p->k, CSA2_MAX_K);
+  if (!isfinite(p->sm_scale)) return fail(CSA2_EINVAL, "sm_scale is not finite");
+  if (selecting && (!p->qix_codes || !p->qix_scales || !p->w || !p->idx_out))
+    return fail(CSA2_EINVAL, "a selecting layer needs qix_codes, qix_scales, w and idx_out");
+  if (p->mode == CSA2_FULL && p->pool != 0) {
+    if (p->pool < p->k || p->pool > CSA2_MAX_POOL)
+      return fail(CSA2_EINVAL, "pool %d outside [k=%d, %d]", p->pool, p->k, CSA2_MAX_POOL);
+    if (!p->pool_out) return fail(CSA2_EINVAL, "pool > 0 needs pool_out");
+  }
+  if (p->mode == CSA2_FULL && p->pool < 0) return fail(CSA2_EINVAL, "negative pool");
+  if (p->mode == CSA2_REINDEX) {
+    if (!p->idx_in) return fail(CSA2_EINVAL, "a Reindex layer needs the pool in idx_in");
+    if (p->pool < p->k || p->pool > CSA2_MAX_POOL)
+      return fail(CSA2_EINVAL, "pool %d outside [k=%d, %d]", p->pool, p->k, CSA2_MAX_POOL);
+  }
+  if (p->mode == CSA2_REUSE && !p->idx_in) return fail(CSA2_EINVAL, "a Reuse layer needs the inherited top-k in idx_in");
+
+  const int rows = p->batch * p->nq;
+  const int32_t capacity = p->cache->max_pages * p->cache->page_size;
+  if (selecting && (int64_t)(p->mode == CSA2_FULL ? capacity : p->pool) > kMaxSelectCols)
+    return fail(CSA2_EUNSUPPORTED, "more than %lld entries per row to select from", (long long)kMaxSelectCols);
+  const int32_t n_cols = p->mode == CSA2_FULL ? capacity : (p->mode == CSA2_REINDEX ? p->pool : 0);
+  const int32_t wcap = win_cap_of(p->win, p->q_pos);
+  const WsLayout L = ws_layout(p->mode, rows, n_cols, p->k, wcap, (p->mode == CSA2_FULL && p->pool > 0) ? 2 : 1,
+                               use_fused_topk(p->mode, p->batch, p->nq, n_cols, p->pool));
+  if ((s = check_ws(p->ws, p->ws_bytes, L.total))) return s;
+  hipStream_t st = (hipStream_t)stream;
+  char *ws = (char *)p->ws;
+
+  const int32_t *att_idx = p->idx_in;
+  if (selecting) {
+    if ((s = run_layer_select(p, L, n_cols, st))) return s;
     att_idx = p->idx_out;
   }
   return run_attend(L, ws, p->cache, att_idx, p->k, p->q, p->win, p->q_pos, p->sm_scale, rows,
                     p->nq, p->out, p->lse, st);
+}
+
+csa2_status csa2_index_topk(const csa2_cache *cache, const uint8_t *qix_codes, const uint8_t *qix_scales,
+                            const float *w, const int32_t *q_pos, int32_t batch, int32_t nq, int32_t k,
+                            int32_t pool, int32_t *idx_out, int32_t *pool_out, void *ws, size_t ws_bytes,
+                            void *stream) {
+  csa2_status s = check_cache(cache, false, true);
+  if (s) return s;
+  if (!qix_codes || !qix_scales || !w || !idx_out)
+    return fail(CSA2_EINVAL, "NULL qix_codes, qix_scales, w or idx_out");
+  if (batch <= 0 || nq <= 0) return fail(CSA2_EINVAL, "batch (%d) and nq (%d) must be positive", batch, nq);
+  if (k <= 0 || k > CSA2_MAX_K) return fail(CSA2_EINVAL, "k = %d outside [1, %d]", k, CSA2_MAX_K);
+  if (pool < 0) return fail(CSA2_EINVAL, "negative pool");
+  if (pool != 0) {
+    if (pool < k || pool > CSA2_MAX_POOL) return fail(CSA2_EINVAL, "pool %d outside [k=%d, %d]", pool, k, CSA2_MAX_POOL);
+    if (!pool_out) return fail(CSA2_EINVAL, "pool > 0 needs pool_out");
+  }
+  const int32_t capacity = cache->max_pages * cache->page_size;
+  if ((int64_t)capacity > kMaxSelectCols)
+    return fail(CSA2_EUNSUPPORTED, "more than %lld entries per row to select from", (long long)kMaxSelectCols);
+  const WsLayout L = ws_layout(CSA2_FULL, (int64_t)batch * nq, capacity, k, 0, pool > 0 ? 2 : 1,
+                               use_fused_topk(CSA2_FULL, batch, nq, capacity, pool));
+  if ((s = check_ws(ws, ws_bytes, L.total))) return s;
+  csa2_layer_args a{};
+  a.mode = CSA2_FULL;
+  a.cache = cache;
+  a.qix_codes = qix_codes;
+  a.qix_scales = qix_scales;
+  a.w = w;
+  a.q_pos = q_pos;
+  a.batch = batch;
+  a.nq = nq;
+  a.k = k;
+  a.pool = pool;
+  a.idx_out = idx_out;
+  a.pool_out = pool_out;
+  a.ws = ws;
+  a.ws_bytes = ws_bytes;
+  return run_layer_select(&a, L, capacity, (hipStream_t)stream);
 }
 
 csa2_status csa2_quantize_fp4(const float *x, int64_t n_rows, int32_t channels, uint8_t *codes,

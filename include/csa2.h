@@ -183,6 +183,18 @@ typedef struct {
 
 csa2_status csa2_layer_step(const csa2_layer_args *args, void *stream);
 
+/* Scoring and selection of a Full layer without attention ([P2] "CSA2": a
+ * Full layer scores every visible entry and keeps its own top-K, and the
+ * pool Reindex layers rescore): idx_out [batch][nq][k] and, when pool > 0,
+ * pool_out [batch][nq][pool], exactly as csa2_layer_step(FULL) writes them
+ * before it attends (ascending ids, then -1). Arguments as for
+ * csa2_layer_step; the prefill-chunk shapes it names run the fused kernel.
+ * Workspace: csa2_workspace_bytes(CSA2_FULL, batch, nq, n_cols, k, pool, 0). */
+csa2_status csa2_index_topk(const csa2_cache *cache, const uint8_t *qix_codes,
+                            const uint8_t *qix_scales, const float *w, const int32_t *q_pos,
+                            int32_t batch, int32_t nq, int32_t k, int32_t pool, int32_t *idx_out,
+                            int32_t *pool_out, void *ws, size_t ws_bytes, void *stream);
+
 /* Workspace bytes for one call.
  *  FULL:    n_cols = max_pages*page_size of the cache; pool may be 0.
  *  REINDEX: n_cols = pool (also the size to use for csa2_topk with n = n_cols).

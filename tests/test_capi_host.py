@@ -132,6 +132,14 @@ def test_other_entry_points_validation():
     assert L.csa2_kv_append(C.byref(cw), p, None, p, 1, 1, None) == EUNSUPPORTED
     assert L.csa2_window_append(p, None, 0, p, p, 1, 1, None) == EINVAL
     assert L.csa2_window_append(p, None, 8, C.c_void_p(0x2008), p, 1, 1, None) == EINVAL
+    # scoring + selection without attention
+    big = C.c_size_t(1 << 40)
+    assert L.csa2_index_topk(C.byref(cs), None, p, p, None, 1, 1, 8, 0, p, None, p, big, None) == EINVAL
+    assert L.csa2_index_topk(C.byref(cs), p, p, p, None, 1, 1, 0, 0, p, None, p, big, None) == EINVAL
+    assert L.csa2_index_topk(C.byref(cs), p, p, p, None, 1, 1, 8, 4, p, p, p, big, None) == EINVAL  # pool < k
+    assert L.csa2_index_topk(C.byref(cs), p, p, p, None, 1, 1, 8, 16, p, None, p, big, None) == EINVAL
+    assert L.csa2_index_topk(C.byref(cs), p, p, p, None, 1, 1, 8, 0, p, None, None, C.c_size_t(0),
+                             None) == EWORKSPACE
 
 
 @pytest.mark.parametrize("mode,n_cols,k,pool,win", [

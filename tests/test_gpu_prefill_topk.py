@@ -117,3 +117,26 @@ def test_prefill_topk_fused_mixed_refinement():
         n = min(wl.k, int(V[0, r]))
         assert (g[0, r, :n] == np.arange(n)).all() and (g[0, r, n:] == -1).all(), f"row {r}"
     assert ((g[0, ~tied] >= 0).sum(axis=-1) == wl.k).all()
+
+
+@pytest.mark.parametrize("case", [
+    dict(contexts=[4 * 20000, 4 * 9000], k=256, pool=2048, nq=1, prefill=False, page_size=64),
+    dict(contexts=[4 * 3000], k=256, pool=0, nq=1040, prefill=True, page_size=32),
+], ids=["decode_pool", "prefill_fused"])
+def test_index_topk_matches_layer_step(case):
+    """csa2_index_topk writes exactly the top-k (and pool) a Full csa2_layer_step
+    selects before it attends."""
+    from devutil import DevWorkload
+    _log(f"index_topk vs layer_step {case}")
+    wl = make_small_decode(layers="F", shuffle=True, **case)
+    dw = DevWorkload(wl)
+    call = dw.calls()[0]
+    call()
+    F = dw.layers[0]
+    idx, pool = csa2.index_topk(dw.caches[0], F["qix_codes"], F["qix_scales"], F["w"], wl.k,
+                                q_pos=dw.q_pos, pool=wl.pool)
+    import torch
+    torch.cuda.synchronize()
+    assert torch.equal(idx, call.idx_out)
+    if wl.pool:
+        assert torch.equal(pool, call.pool_out)
