@@ -36,6 +36,8 @@
 namespace csa2 {
 
 #define PT_R 16                        // query rows per workgroup
+#define PT_MT (PT_R / 4)               // M tiles: 4 rows x 4 heads each
+#define PT_WG_PER_CU 1                 // minimum waves per SIMD for the register budget
 #define PT_NT 512                      // threads (8 waves)
 #define PT_WAVES (PT_NT / 64)
 #define PT_BINS 2048
@@ -203,23 +205,23 @@ __device__ __forceinline__ bool pt_open(const PtShared &sh, int kind, int r) {
 // 16-entry tile lies in one page and its addresses are wave-uniform.
 template <int KIND, bool TILEPAGE>
 __device__ __forceinline__ void pt_sweep(const PrefillTopkArgs &a, PtShared &sh, int b,
-                                         const v8h (&A)[4][2], const float (&W)[4][4]) {
+                                         const v8h (&A)[PT_MT][2], const float (&W)[PT_MT][4]) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int m = lane & 15, gq = lane >> 4;
   // per M tile: the lane's result row (4 mt + gq) and its pass parameters
-  int32_t vlim[4];
-  uint32_t inc[4];
-  uint64_t rlo[4], rhi[4];
-  float flo[4], fhi[4];
-  int32_t shf[4];
-  bool coll[4];
+  int32_t vlim[PT_MT];
+  uint32_t inc[PT_MT];
+  uint64_t rlo[PT_MT], rhi[PT_MT];
+  float flo[PT_MT], fhi[PT_MT];
+  int32_t shf[PT_MT];
+  bool coll[PT_MT];
   int32_t vmax = 0;
 #pragma unroll
   for (int i = 0; i < PT_R; ++i)
     if (pt_open(sh, KIND, i)) vmax = max(vmax, sh.vis[i]);
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
+  for (int mt = 0; mt < PT_MT; ++mt) {
     const int r = 4 * mt + gq;
     vlim[mt] = pt_open(sh, KIND, r) ? sh.vis[r] : 0;
     inc[mt] = 1u << (16 * (r & 1));
@@ -231,9 +233,9 @@ __device__ __forceinline__ void pt_sweep(const PrefillTopkArgs &a, PtShared &sh,
     coll[mt] = sh.mode[r] == PT_COLLECT;
   }
   // lane g < 4 writes the bitmap halves of row 4 mt + g when that row collects
-  bool wbits[4];
+  bool wbits[PT_MT];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
+  for (int mt = 0; mt < PT_MT; ++mt) {
     const int rr = 4 * mt + (lane & 3);
     wbits[mt] = lane < 4 && KIND != SW_HIST0 && pt_open(sh, KIND, rr) && sh.mode[rr] == PT_COLLECT;
   }
@@ -295,7 +297,7 @@ __device__ __forceinline__ void pt_sweep(const PrefillTopkArgs &a, PtShared &sh,
       const v8h b1 = fp4x8_dequant((uint32_t)__float_as_int(cur.code[u][1]), s);
       const int32_t e = et + m;
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
+      for (int mt = 0; mt < PT_MT; ++mt) {
         v4f acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[mt][0], b0, (v4f){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[mt][1], b1, acc, 0, 0, 0);
         float sc = 0.f;
@@ -429,7 +431,7 @@ __device__ void pt_resolve_collect(PtShared &sh, int r) {
 }
 
 template <bool TILEPAGE>
-__global__ __launch_bounds__(PT_NT) void k_prefill_topk(PrefillTopkArgs a) {
+__global__ __launch_bounds__(PT_NT, PT_WG_PER_CU) void k_prefill_topk(PrefillTopkArgs a) {
   __shared__ __attribute__((aligned(16))) PtShared sh;
   const int qb = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -472,10 +474,10 @@ __global__ __launch_bounds__(PT_NT) void k_prefill_topk(PrefillTopkArgs a) {
   // A operands (rows 4 mt + m/4, head m%4) and the head weights of the
   // lane's result rows 4 mt + gq
   const int m = lane & 15, gq = lane >> 4;
-  v8h A[4][2];
-  float W[4][4];
+  v8h A[PT_MT][2];
+  float W[PT_MT][4];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
+  for (int mt = 0; mt < PT_MT; ++mt) {
     const int ta = qb * PT_R + 4 * mt + (m >> 2), h = m & 3;
     const int64_t row_a = (int64_t)b * a.nq + min(ta, a.nq - 1);
     const v2f c = *(const v2f *)(a.qix_codes + (row_a * CSA2_HI + h) * 32 + 8 * gq);
@@ -493,7 +495,7 @@ __global__ __launch_bounds__(PT_NT) void k_prefill_topk(PrefillTopkArgs a) {
   if (any) {
     pt_sweep<SW_HIST0, TILEPAGE>(a, sh, b, A, W);
     __syncthreads();
-    for (int half = 0; half < 2; ++half) {
+    for (int half = 0; half < 2 && 2 * wave < PT_R; ++half) {
       const int r = 2 * wave + half;
       if (sh.mode[r] == PT_HIST0) pt_resolve_hist(sh, r);
     }
@@ -519,7 +521,7 @@ __global__ __launch_bounds__(PT_NT) void k_prefill_topk(PrefillTopkArgs a) {
     if (general) pt_sweep<SW_GENERAL, TILEPAGE>(a, sh, b, A, W);
     else pt_sweep<SW_COLLECT_F, TILEPAGE>(a, sh, b, A, W);
     __syncthreads();
-    {
+    if (2 * wave < PT_R) {
       // modes as the sweep saw them (resolving one row of the pair changes its mode)
       const int md2[2] = {sh.mode[2 * wave], sh.mode[2 * wave + 1]};
       for (int half = 0; half < 2; ++half) {
@@ -532,7 +534,7 @@ __global__ __launch_bounds__(PT_NT) void k_prefill_topk(PrefillTopkArgs a) {
   }
 
   // ascending ids of each row, then -1 pads (one wave per row pair)
-  for (int half = 0; half < 2; ++half) {
+  for (int half = 0; half < 2 && 2 * wave < PT_R; ++half) {
     const int r = 2 * wave + half;
     const int t = qb * PT_R + r;
     if (t >= a.nq) continue;
