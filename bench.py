@@ -266,7 +266,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(decode requests shard by batch with no exchange, see DESIGN.md)", file=sys.stderr)
+              "(decode requests shard by batch with no exchange between GPUs)", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch

@@ -61,7 +61,7 @@ extern "C" {
 typedef enum {
   CSA2_OK = 0,
   CSA2_EINVAL = 1,       /* null required pointer, non-positive size, inconsistent sizes */
-  CSA2_EUNSUPPORTED = 2, /* valid request this build does not implement */
+  CSA2_EUNSUPPORTED = 2, /* valid request this library does not implement */
   CSA2_EWORKSPACE = 3,   /* workspace missing, too small or misaligned */
   CSA2_EHIP = 4          /* a HIP launch failed; see csa2_last_error() */
 } csa2_status;

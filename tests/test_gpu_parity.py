@@ -1,6 +1,6 @@
 """HIP path vs the CPU oracle (GPU required).
 
-Tolerances (written here, derived in the design doc):
+Tolerances (the bars every GPU parity test applies):
  * dequantised values: bit-exact (fp16 of the FP4 path, fp32 of E4M3);
  * index scores: |gpu - oracle| <= 1e-6 |oracle| + 1e-6 max|row|;
  * top-K id sets: equal after dropping ids whose oracle score lies within
