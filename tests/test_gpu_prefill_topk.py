@@ -140,3 +140,37 @@ def test_index_topk_matches_layer_step(case):
     assert torch.equal(idx, call.idx_out)
     if wl.pool:
         assert torch.equal(pool, call.pool_out)
+
+
+def test_prefill_topk_fused_graph_replays():
+    """The fused prefill layer (selection + attention) captured in a HIP graph
+    replays to the eager result every time, with other work in between."""
+    import torch
+    from devutil import DevWorkload
+    _log("fused prefill top-k, graph replays")
+    wl = make_small_decode([4 * 3000], layers="F", k=256, nq=1040, prefill=True, page_size=32,
+                           shuffle=True)
+    dw = DevWorkload(wl)
+    call = dw.calls()[0]
+    call()
+    torch.cuda.synchronize()
+    ref = (call.out.clone(), call.lse.clone(), call.idx_out.clone())
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for rep in range(3):
+        call.out.fill_(float("nan"))
+        call.lse.zero_()
+        call.idx_out.fill_(-5)
+        junk = torch.randn(1 << 20, device="cuda").sum()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.isfinite(junk)
+        assert torch.equal(call.idx_out, ref[2]), f"replay {rep}"
+        assert torch.equal(call.out, ref[0]) and torch.equal(call.lse, ref[1]), f"replay {rep}"
