@@ -165,7 +165,7 @@ def test_topk_exact_ties(n, k):
     assert (g == o).all()
 
 
-@pytest.mark.parametrize("n,k", [(5000, 2048), (262144, 4096), (40000, 1)])
+@pytest.mark.parametrize("n,k", [(5000, 2048), (262144, 4096), (40000, 1), (524288, 4096)])
 def test_topk_random_scores(n, k):
     _log(f"topk random n={n} k={k}")
     rng = np.random.default_rng(7)
@@ -335,11 +335,14 @@ LAYER_CASES = [
     dict(contexts=[4 * 60000, 4 * 9000], layers="FRU", k=1024, pool=12000, page_size=64, shuffle=True),
     # 520 query rows of a prefill chunk: attention runs one workgroup per query row
     dict(contexts=[4 * 3000], layers="FRU", k=256, pool=1024, nq=520, prefill=True, page_size=32),
+    # the largest k and pool the library takes (4096, 65536): 33 attention units per row
+    dict(contexts=[4 * 70000, 4 * 20000], layers="FRU", k=4096, pool=65536, page_size=64, shuffle=True),
 ]
 
 
 @pytest.mark.parametrize("case", LAYER_CASES, ids=["tiny_full", "full_reuse", "full_reindex_reuse",
-                                                   "rowscale", "short_ctx", "long_pool", "prefill_rows"])
+                                                   "rowscale", "short_ctx", "long_pool", "prefill_rows",
+                                                   "max_k_pool"])
 def test_layer_step_chain(case):
     _log(f"layer chain {case}")
     wl = make_small_decode(**case)
