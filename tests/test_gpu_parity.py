@@ -337,12 +337,15 @@ LAYER_CASES = [
     dict(contexts=[4 * 3000], layers="FRU", k=256, pool=1024, nq=520, prefill=True, page_size=32),
     # the largest k and pool the library takes (4096, 65536): 33 attention units per row
     dict(contexts=[4 * 70000, 4 * 20000], layers="FRU", k=4096, pool=65536, page_size=64, shuffle=True),
+    # the page-size extremes: every entry its own page; whole requests in one or a few pages
+    dict(contexts=[4 * 3000, 4 * 1000], layers="FRU", k=256, pool=1024, page_size=1, shuffle=True),
+    dict(contexts=[4 * 20000, 4 * 5000], layers="FRU", k=512, pool=2048, page_size=4096, shuffle=True),
 ]
 
 
 @pytest.mark.parametrize("case", LAYER_CASES, ids=["tiny_full", "full_reuse", "full_reindex_reuse",
                                                    "rowscale", "short_ctx", "long_pool", "prefill_rows",
-                                                   "max_k_pool"])
+                                                   "max_k_pool", "page_1", "page_4096"])
 def test_layer_step_chain(case):
     _log(f"layer chain {case}")
     wl = make_small_decode(**case)
