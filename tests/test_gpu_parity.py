@@ -340,12 +340,14 @@ LAYER_CASES = [
     # the page-size extremes: every entry its own page; whole requests in one or a few pages
     dict(contexts=[4 * 3000, 4 * 1000], layers="FRU", k=256, pool=1024, page_size=1, shuffle=True),
     dict(contexts=[4 * 20000, 4 * 5000], layers="FRU", k=512, pool=2048, page_size=4096, shuffle=True),
+    # an empty request (no entries, no window rows) beside a full one and one shorter than k
+    dict(contexts=[4 * 3000, 0, 4 * 10], layers="FRU", k=64, pool=256, page_size=16, shuffle=True),
 ]
 
 
 @pytest.mark.parametrize("case", LAYER_CASES, ids=["tiny_full", "full_reuse", "full_reindex_reuse",
                                                    "rowscale", "short_ctx", "long_pool", "prefill_rows",
-                                                   "max_k_pool", "page_1", "page_4096"])
+                                                   "max_k_pool", "page_1", "page_4096", "empty_request"])
 def test_layer_step_chain(case):
     _log(f"layer chain {case}")
     wl = make_small_decode(**case)
