@@ -10,7 +10,9 @@ The 128K-context workload (batch 32, [Full, Reuse x5]) is timed beside it.
 --workload selects another workload for the JSON line: the 128K one, the
 ragged 64-request 20-layer stack, or the 4096-query prefill chunk.
 
-Printed: one JSON line (metric, value = queries/s, CPU-oracle baseline, and
+Printed: one JSON line (metric, value = queries/s, CPU-oracle baseline with
+the host's CPU model and a one-thread timing of the tiny workload, a measured
+stream-copy peak (1 GiB device copy) beside the 8 TB/s datasheet figure, and
 rooflines measured live with HIP events: `roofline` for the kernel that takes
 the most step time, the attention call (k_attend_seg and its merge), and
 `roofline_scoring` for the indexer scoring kernel (HBM-bound in decode;
@@ -138,6 +140,18 @@ def attend_bytes(wl, li) -> int:
             win = int(L.win.length[b]) * (512 + (4 if L.win.row_scale is not None else 0))
         total += wl.nq * (292 * K + win + 32768 + 32832)
     return total
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (first "model name" line of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def prefill_score_flops(wl) -> int:
@@ -512,6 +526,24 @@ def main():
         log(f"128K workload: {secondary['ms_per_step']} ms/step, {secondary['value']} queries/s")
         del chains2, copies2
 
+    # ---- measured stream-copy peak: a plain 1 GiB device copy (read + write),
+    # event-timed, the practical ceiling beside the 8 TB/s datasheet figure ----
+    nb = 1 << 30
+    xs = torch.empty(nb, dtype=torch.uint8, device=dev)
+    ys = torch.empty_like(xs)
+    for _ in range(2):
+        ys.copy_(xs)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        ys.copy_(xs)
+    e1.record()
+    torch.cuda.synchronize()
+    stream_gbps = 2 * nb * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del xs, ys
+    log(f"stream copy: {stream_gbps:.0f} GB/s (read + write, 1 GiB)")
+
     # ---- CPU oracle baseline (bounded sample, host cores) ----
     cpu = None
     if not args.skip_cpu:
@@ -534,8 +566,21 @@ def main():
         cores = min(oracle.num_threads(), len(os.sched_getaffinity(0)))
         cpu = dict(value=round(sq * reps / t_cpu, 3), unit="queries/s", cores=cores, kind="oracle",
                    sample=f"the whole {len(wl.layers)}-layer step of {what}, repeated {reps}x "
-                          f"({t_cpu:.1f}s); fp64 C oracle, OpenMP over query rows")
-        log(f"cpu oracle: {cpu['value']} queries/s on {cores} threads")
+                          f"({t_cpu:.1f}s); fp64 C oracle, OpenMP over query rows",
+                   cpu_model=cpu_model())
+        # one thread on the tiny workload (1 request, 8192 tokens, one Full layer, top-256)
+        tiny = make_decode_workload("tiny_b1_8k_full")
+        oracle.set_num_threads(1)
+        n1, w1 = 0, time.perf_counter()
+        while n1 == 0 or time.perf_counter() - w1 < 1.0:
+            oracle.run_workload(tiny)
+            n1 += 1
+        t1 = time.perf_counter() - w1
+        oracle.set_num_threads(cores)
+        cpu["single_thread_tiny"] = {"value": round(n1 / t1, 2), "unit": "queries/s",
+                                     "workload": "tiny_b1_8k_full", "repeats": n1}
+        log(f"cpu oracle: {cpu['value']} queries/s on {cores} threads; "
+            f"1 thread on the tiny workload: {cpu['single_thread_tiny']['value']} queries/s")
 
     line = {
         "metric": "CSA2 decode queries/s + achieved HBM GB/s (% of peak) at 128K and 1M ctx",
@@ -557,12 +602,15 @@ def main():
                    "timing": "graph" if (graph_s is not None and graph_s <= eager_s) else "eager"},
         "step_gbps": round(gbps, 1),
         "step_pct_of_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
+        "stream_copy_gbps": round(stream_gbps, 1),
+        "step_pct_of_stream_copy": round(100 * gbps / stream_gbps, 2),
         "step_algorithmic_bytes": sbytes,
         "eager_ms_per_step": round(eager_s / args.steps * 1e3, 4),
         "graph_ms_per_step": None if graph_s is None else round(graph_s / args.steps * 1e3, 4),
         "roofline": {"kernel": "csa2_sparse_attend: k_attend_seg + k_merge_seg (first layer's selection)",
                      "bound": "hbm", "achieved": round(att_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(att_gbps / HBM_PEAK_GBPS, 4), "traffic": att_traffic,
+                     "frac_of_stream_copy": round(att_gbps / stream_gbps, 4),
                      "bytes_per_launch": att_b, "us_per_launch": round(att_ms * 1e3, 3)},
         "roofline_scoring": (
             {"kernel": "k_prefill_topk (prefill-chunk indexer scoring fused with the per-query top-K: "
@@ -574,6 +622,7 @@ def main():
             {"kernel": "k_index_score (Full-layer lightning-indexer scoring)", "bound": "hbm",
              "achieved": round(k_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
              "frac": round(k_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
+             "frac_of_stream_copy": round(k_gbps / stream_gbps, 4),
              "bytes_per_launch": kb, "us_per_launch": round(k_ms * 1e3, 3)}),
         "append": app,
         "topk_vs_torch": topk_cmp,

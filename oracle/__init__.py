@@ -374,3 +374,8 @@ def run_workload(wl, layers=None, want_scores=False):
 
 def num_threads() -> int:
     return lib().orc_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    """OpenMP threads for later calls (timing only: results do not depend on it)."""
+    lib().orc_set_num_threads(int(n))

@@ -30,6 +30,15 @@ int orc_num_threads(void) {
 #endif
 }
 
+/* Threads for the following calls (timing only; results do not depend on it). */
+void orc_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 /* ---- Step 1: the two number formats ([P2-FP4]) --------------------------
  * E2M1: sign | 2 exponent bits | 1 mantissa bit, bias 1, subnormal at e=0:
  *   e == 0: 0.5*m; else 2^(e-1) * (1 + m/2).

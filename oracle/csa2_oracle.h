@@ -132,6 +132,7 @@ void orc_window_append(uint8_t *codes, float *row_scale, int32_t rows, const flo
                        const int32_t *row, int32_t B, int32_t n_new);
 
 int orc_num_threads(void);
+void orc_set_num_threads(int n);
 
 #ifdef __cplusplus
 }
