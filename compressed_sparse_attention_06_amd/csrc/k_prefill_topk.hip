@@ -13,13 +13,16 @@
 //            below in bin 0, above in bin 2047);
 //   pass 1+  the bin holding the K-th largest score is known, so every entry
 //            above it is selected (one bit per entry id) and the entries
-//            inside it, usually a few dozen, are collected as candidates and
-//            ranked exactly. A row whose threshold bin holds more than 128
-//            entries is refined by another histogram over that bin instead.
+//            inside it, usually a few dozen to a few hundred, are collected
+//            as candidates (in the row's histogram space) and ranked
+//            exactly. A row whose threshold bin holds more than 512 entries
+//            is refined by another histogram over that bin instead.
 // Ranking and refinement work on the 64-bit composite (order key of the
 // score, ~entry id): it is unique per entry and orders by score descending,
 // then id ascending, so ties need no special case and every refinement step
-// narrows the range by 2^11 until it holds at most 128 entries.
+// narrows the range by 2^11 until it holds at most 512 entries. Two rows
+// share each histogram word (16-bit counts); a collecting row waits while
+// the other row of its pair refines.
 // The output is each row's selected ids in ascending order (a scan of the
 // row's bitmap), then -1 pads.
 //
