@@ -142,6 +142,20 @@ def attend_bytes(wl, li) -> int:
     return total
 
 
+def attend_flops(wl, li) -> int:
+    """Useful matrix flops of one attention call of layer li: per query row and
+    attended row (selected entries, then window rows), 16 heads x 512 channels
+    x 2 for QK^T and x 2 for P.V."""
+    L = wl.layers[li]
+    c = wl.caches[L.cache_id]
+    total = 0
+    for b in range(wl.batch):
+        K = min(wl.k, int(c.n_entries[b]))
+        win = wl.window if wl.q_pos is not None else int(L.win.length[b])
+        total += wl.nq * (K + win) * 16 * 512 * 4
+    return total
+
+
 def cpu_model() -> str:
     """The host CPU's model name (first "model name" line of /proc/cpuinfo)."""
     try:
@@ -382,7 +396,10 @@ def main():
     att_ms = ev0.elapsed_time(ev1) / args.kernel_iters
     att_b = attend_bytes(wl, li0)
     att_gbps = att_b / (att_ms * 1e-3) / 1e9
-    log(f"attention call: {att_ms * 1e3:.2f} us/launch, {att_gbps:.0f} GB/s algorithmic")
+    att_f = attend_flops(wl, li0)
+    att_tflops = att_f / (att_ms * 1e-3) / 1e12
+    log(f"attention call: {att_ms * 1e3:.2f} us/launch, {att_gbps:.0f} GB/s algorithmic, "
+        f"{att_tflops:.0f} TFLOP/s useful")
 
     att_traffic = None
     if os.path.exists(ATT_TRAFFIC_FILE):
@@ -607,11 +624,21 @@ def main():
         "step_algorithmic_bytes": sbytes,
         "eager_ms_per_step": round(eager_s / args.steps * 1e3, 4),
         "graph_ms_per_step": None if graph_s is None else round(graph_s / args.steps * 1e3, 4),
-        "roofline": {"kernel": "csa2_sparse_attend: k_attend_seg + k_merge_seg (first layer's selection)",
-                     "bound": "hbm", "achieved": round(att_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(att_gbps / HBM_PEAK_GBPS, 4), "traffic": att_traffic,
-                     "frac_of_stream_copy": round(att_gbps / stream_gbps, 4),
-                     "bytes_per_launch": att_b, "us_per_launch": round(att_ms * 1e3, 3)},
+        # decode attention streams its gathered rows from HBM; the prefill
+        # chunk's 4096 queries gather from a 9.4 MB cache that stays in the
+        # on-chip caches, so there the matrix cores are the roofline
+        "roofline": ({"kernel": "csa2_sparse_attend: k_attend_seg (first layer's selection; no merge: "
+                                "every row falls whole to one workgroup)",
+                      "bound": "mfma", "achieved": round(att_tflops, 1), "peak": MFMA_F16_PEAK_TFLOPS,
+                      "unit": "TFLOP/s", "frac": round(att_tflops / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
+                      "flops_per_launch": att_f, "bytes_per_launch": att_b,
+                      "us_per_launch": round(att_ms * 1e3, 3)} if prefill else
+                     {"kernel": "csa2_sparse_attend: k_attend_seg + k_merge_seg (first layer's selection)",
+                      "bound": "hbm", "achieved": round(att_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                      "frac": round(att_gbps / HBM_PEAK_GBPS, 4), "traffic": att_traffic,
+                      "frac_of_stream_copy": round(att_gbps / stream_gbps, 4),
+                      "bytes_per_launch": att_b, "flops_per_launch": att_f,
+                      "us_per_launch": round(att_ms * 1e3, 3)}),
         "roofline_scoring": (
             {"kernel": "k_prefill_topk (prefill-chunk indexer scoring fused with the per-query top-K: "
                        "two fp16-MFMA scoring passes and the selection; achieved = one pass's useful "
