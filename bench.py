@@ -13,7 +13,8 @@ ragged 64-request 20-layer stack, or the 4096-query prefill chunk.
 Printed: one JSON line (metric, value = queries/s, CPU-oracle baseline with
 the host's CPU model and a one-thread timing of the tiny workload, a measured
 stream-copy peak (1 GiB device copy) beside the 8 TB/s datasheet figure, and
-rooflines measured live with HIP events: `roofline` for the kernel that takes
+rooflines measured live with HIP events around back-to-back calls replayed
+from one HIP graph on the stream they run on: `roofline` for the kernel that takes
 the most step time, the attention call (k_attend_seg and its merge), and
 `roofline_scoring` for the indexer scoring kernel (HBM-bound in decode;
 in the prefill chunk the kernel that scores and selects without a score
@@ -344,18 +345,34 @@ def main():
             csa2.index_score(caches[0], layers[0]["qix_codes"], layers[0]["qix_scales"], layers[0]["w"],
                              q_pos=qp, out=scores, hist=hist)
 
-    for i in range(5):
-        score_once(i)
-    torch.cuda.synchronize()
-    # back-to-back launches on the stream they run on (torch's current stream,
-    # which the binding passes to the library), bracketed by two HIP events
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record()
-    for i in range(args.kernel_iters):
-        score_once(i)
-    ev1.record()
-    torch.cuda.synchronize()
-    k_ms = ev0.elapsed_time(ev1) / args.kernel_iters
+
+    def time_calls(fn, iters):
+        """us per call: `iters` calls captured in one HIP graph and replayed, so that
+        the binding's host-side overhead is not what is timed."""
+        for i in range(3):
+            fn(i)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        s_cap = torch.cuda.Stream()
+        s_cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s_cap):
+            with torch.cuda.graph(g, stream=s_cap):
+                for i in range(iters):
+                    fn(i)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ev0.record()
+        g.replay()
+        ev1.record()
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / iters * 1e3
+
+    # back-to-back launches captured in one HIP graph and replayed between two
+    # HIP events on the stream the graph runs on (torch's current stream), so
+    # that the binding's per-call host work is not part of the kernel's time
+    k_ms = time_calls(score_once, args.kernel_iters) * 1e-3
     if prefill:
         kflops = prefill_score_flops(wl)
         k_tflops = kflops / (k_ms * 1e-3) / 1e12
@@ -385,15 +402,7 @@ def main():
         cache, idx, q, win, out, lse, ws = att_args[i % len(att_args)]
         csa2.sparse_attend(cache, idx, q, win, q_pos=qp, sm_scale=wl.sm_scale, out=out, lse=lse, ws=ws)
 
-    for i in range(5):
-        attend_once(i)
-    torch.cuda.synchronize()
-    ev0.record()
-    for i in range(args.kernel_iters):
-        attend_once(i)
-    ev1.record()
-    torch.cuda.synchronize()
-    att_ms = ev0.elapsed_time(ev1) / args.kernel_iters
+    att_ms = time_calls(attend_once, args.kernel_iters) * 1e-3
     att_b = attend_bytes(wl, li0)
     att_gbps = att_b / (att_ms * 1e-3) / 1e9
     att_f = attend_flops(wl, li0)
@@ -412,28 +421,6 @@ def main():
             att_traffic = None
 
     # ---- the cache's write side: what one decode step appends, and a prefill chunk's worth ----
-    def time_calls(fn, iters):
-        """us per call: `iters` calls captured in one HIP graph and replayed, so that
-        the binding's host-side overhead is not what is timed."""
-        for i in range(3):
-            fn(i)
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        s_cap = torch.cuda.Stream()
-        s_cap.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s_cap):
-            with torch.cuda.graph(g, stream=s_cap):
-                for i in range(iters):
-                    fn(i)
-        torch.cuda.synchronize()
-        g.replay()
-        torch.cuda.synchronize()
-        ev0.record()
-        g.replay()
-        ev1.record()
-        torch.cuda.synchronize()
-        return ev0.elapsed_time(ev1) / iters * 1e3
-
     gen = torch.Generator(device=dev).manual_seed(11)
     cache0 = copies[0][0][0]
     app = {}

@@ -572,10 +572,41 @@ __global__ __launch_bounds__(512) void k_attend_seg(AttendArgs a, SegArgs s) {
 // Combine the partials of rows cut between workgroups of k_attend_seg (rows
 // written whole are skipped). Workgroup w's partial for row r sits in slot 0
 // when r is the first row of w's range, else in slot 1. One workgroup per
-// (head, row), four channels per thread; BATCH partials are loaded together.
+// (head, row), four channels per thread. The partials are taken BATCH at a
+// time, and every load of a batch goes out before any is used: lane u of each
+// wave reads the running max and sum of partial u (vector loads, so that the
+// batch does not queue on scalar registers), each thread reads its four
+// channels of every partial, and the weights reach the other lanes by
+// readlane.
+// reductions over a wave: within rows of 16 lanes by DPP, then across the
+// four rows through readlane (the result is uniform)
+__device__ __forceinline__ float wave_max64(float v) {
+  v = row16_max(v);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fmax_nc(fmax_nc(r0, r1), fmax_nc(r2, r3));
+}
+
+__device__ __forceinline__ float wave_sum64(float v) {
+  v += dpp_f32<0xB1>(v);
+  v += dpp_f32<0x4E>(v);
+  v += dpp_f32<0x141>(v);
+  v += dpp_f32<0x140>(v);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
+// (waves_per_eu: few merge waves share a SIMD, so the compiler may hold a
+// whole batch in registers instead of recycling them between loads)
 template <int BATCH>
-__global__ __launch_bounds__(128) void k_merge_seg(MergeArgs a, SegArgs s) {
-  const int h = blockIdx.x, r = blockIdx.y, t = threadIdx.x;
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 2))) void k_merge_seg(MergeArgs a,
+                                                                                              SegArgs s) {
+  const int h = blockIdx.x, r = blockIdx.y, t = threadIdx.x, lane = t & 63;
   const int64_t u0 = (int64_t)r * s.U, u1 = u0 + s.U - 1;
   const int32_t first = (int32_t)(((u0 + 1) * s.G + s.T - 1) / s.T - 1);
   const int32_t last = (int32_t)(((u1 + 1) * s.G + s.T - 1) / s.T - 1);
@@ -583,37 +614,39 @@ __global__ __launch_bounds__(128) void k_merge_seg(MergeArgs a, SegArgs s) {
   const int n = last - first + 1;
   // the first workgroup holds this row in slot 0 only when its range starts in it
   const int first_slot = ((int64_t)first * s.T / s.G / s.U == r) ? 0 : 1;
+  // partial i of this row, head h: workgroup first + i, slot first_slot for i = 0, else 0
+  const float *hb = a.part + (int64_t)h * kPartStride + 4 * t;
   float M = -INFINITY, L = 0.f;
   v4f o = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < n; s0 += BATCH) {
-    const int cnt = min(BATCH, n - s0);
-    float mv[BATCH], lv[BATCH];
+  for (int b0 = 0; b0 < n; b0 += BATCH) {
+    const int cnt = min(BATCH, n - b0);
+    float mu = -INFINITY, lu = 0.f;
+    if (lane < cnt) {
+      const int i = b0 + lane;
+      const int slot = (i == 0) ? first_slot : 0;
+      const float *ps = a.part + (((int64_t)(first + i) * 2 + slot) * CSA2_H + h) * kPartStride;
+      mu = ps[CSA2_D];
+      lu = ps[CSA2_D + 1];
+    }
     v4f ov[BATCH];
 #pragma unroll
     for (int u = 0; u < BATCH; ++u) {
-      const int wi = s0 + min(u, cnt - 1);
-      const int slot = (wi == 0) ? first_slot : 0;
-      const float *ps = a.part + (((int64_t)(first + wi) * 2 + slot) * CSA2_H + h) * kPartStride;
-      mv[u] = ps[CSA2_D];
-      lv[u] = ps[CSA2_D + 1];
-      ov[u] = *(const v4f *)&ps[4 * t];
+      const int i = b0 + min(u, cnt - 1);  // repeats of the last partial weigh nothing
+      const int slot = (i == 0) ? first_slot : 0;
+      ov[u] = *(const v4f *)(hb + ((int64_t)(first + i) * 2 + slot) * CSA2_H * kPartStride);
     }
-    // repeats of the batch's last partial weigh nothing
-#pragma unroll
-    for (int u = 1; u < BATCH; ++u) mv[u] = (u < cnt) ? mv[u] : -INFINITY;
-    float bm = M;
-#pragma unroll
-    for (int u = 0; u < BATCH; ++u) bm = fmaxf(bm, mv[u]);
-    if (bm == -INFINITY) continue;
-    const float f = __builtin_amdgcn_exp2f(M - bm);  // 0 while M is -inf
-    L *= f;
+    __builtin_amdgcn_sched_barrier(0);  // every load of the batch is issued before the first wait
+    // no branch on the maxima, so that the loads above stay ahead of any use;
+    // with nothing finite so far the reference is 0 and every weight is 0
+    const float bm = fmaxf(M, wave_max64(mu));
+    const float bref = (bm == -INFINITY) ? 0.f : bm;
+    const float f = __builtin_amdgcn_exp2f(M - bref);  // 0 while M is -inf
+    const float wu = __builtin_amdgcn_exp2f(mu - bref);  // 0 past the batch or for an empty partial
+    L = L * f + wave_sum64(wu * lu);
     o *= f;
 #pragma unroll
-    for (int u = 0; u < BATCH; ++u) {
-      const float wgt = __builtin_amdgcn_exp2f(mv[u] - bm);  // 0 for an empty partial
-      L += wgt * lv[u];
-      o += wgt * ov[u];
-    }
+    for (int u = 0; u < BATCH; ++u)
+      o += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wu), u)) * ov[u];
     M = bm;
   }
   const float inv = (L > 0.f) ? 1.f / L : 0.f;
@@ -630,12 +663,13 @@ hipError_t launch_attend_seg(const AttendArgs &a, const SegArgs &s, int max_slot
   MergeArgs m{};
   m.part = a.part;
   const dim3 grid(CSA2_H, (unsigned)(s.T / s.U));
+  // one batch of loads covers up to 24 partials (the 1M decode rows have 17)
   if (max_slots <= 8)
     hipLaunchKernelGGL(k_merge_seg<8>, grid, dim3(128), 0, st, m, s);
   else if (max_slots <= 16)
     hipLaunchKernelGGL(k_merge_seg<16>, grid, dim3(128), 0, st, m, s);
   else
-    hipLaunchKernelGGL(k_merge_seg<32>, grid, dim3(128), 0, st, m, s);
+    hipLaunchKernelGGL(k_merge_seg<24>, grid, dim3(128), 0, st, m, s);
   return hipGetLastError();
 }
 
