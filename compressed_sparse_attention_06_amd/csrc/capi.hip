@@ -85,12 +85,29 @@ struct WsLayout {
 
 // Attention work split: each row's attention set (k entries, then the window
 // from k rounded up to 16) in units of 128 positions, shared out evenly over
-// at most one workgroup per compute unit.
+// at most one workgroup per compute unit. Workgroup w takes units
+// [w T / G, (w + 1) T / G) of the T = rows x U in row order. With G a
+// multiple of the row count (P workgroups per row), every workgroup's range
+// lies inside one row: a workgroup whose range crosses a row boundary pays
+// the second row's Q conversion and id -> page -> row chain as well, so such
+// a G is taken whenever its largest range is no longer than that of the
+// plain split over min(T, 256) workgroups, with the fewest workgroups per row
+// that keep that length (fewer partials for the merge).
 void attend_geometry(WsLayout &L, int64_t rows, int32_t k, int32_t win_cap) {
   const int64_t span = (((int64_t)k + 15) & ~(int64_t)15) + (win_cap > 0 ? win_cap : 0);
   L.att_U = (int32_t)((span + 127) / 128);
   L.att_T = rows * L.att_U;
   L.att_G = (int32_t)std::min<int64_t>(L.att_T, csa2::kSegMaxWg);
+  if (rows <= csa2::kSegMaxWg) {
+    const int64_t U = L.att_U;
+    const int64_t longest = (L.att_T + L.att_G - 1) / L.att_G;  // units of the plain split's largest range
+    int64_t P = std::min<int64_t>(U, csa2::kSegMaxWg / rows);
+    const int64_t per = (U + P - 1) / P;
+    if (per <= longest) {
+      while (P > 1 && (U + P - 2) / (P - 1) == per) --P;
+      L.att_G = (int32_t)(rows * P);
+    }
+  }
   const int64_t rows_n = L.att_T / L.att_U;
   auto owner = [&](int64_t u) { return ((u + 1) * L.att_G + L.att_T - 1) / L.att_T - 1; };
   L.att_slots = 1;

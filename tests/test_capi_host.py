@@ -176,3 +176,22 @@ def test_fused_prefill_topk_workspace(batch, nq, n_cols, pool, fused):
         assert full == att
     else:
         assert full >= att + batch * nq * n_cols * 4
+
+
+@pytest.mark.parametrize("rows,groups", [
+    (8, 136),    # 17 units per row, one workgroup each
+    (32, 192),   # 6 workgroups per row: 2-3 units each, none spanning two rows
+    (48, 240),   # 5 per row: 3-4 units each
+    (64, 256),   # 4 per row: 4-5 units each
+    (100, 256),  # a row-aligned split would give 9 units to some workgroup: plain split (6-7)
+])
+def test_attention_split_workgroups(rows, groups):
+    """A Reuse call's workspace is the attention partials, two slots of
+    16 x 516 floats per workgroup: it shows how many workgroups share the rows
+    (2048 entries + a 128-row window = 17 units of 128 positions per row).
+    When some multiple of the row count keeps the largest range as short as
+    the plain split over 256 workgroups, whole rows are shared out (no range
+    spans two rows), with the fewest workgroups per row that do so."""
+    part = 2 * 16 * (512 + 4) * 4
+    nb = csa2.workspace_bytes(csa2.REUSE, rows, 1, 0, 2048, 0, 128)
+    assert nb == -(-groups * part // 256) * 256
