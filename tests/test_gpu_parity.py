@@ -257,7 +257,8 @@ def test_sparse_attend_edge_cases():
 # workgroups. These cases cover k below, at and off a multiple of 16, sets of
 # one unit, rows cut between workgroups at many offsets (T > 256 units, with
 # 2..20 units per workgroup), several query rows per request with their own
-# causal windows, and no window.
+# causal windows, no window, and rows cut into more partials (33) than the
+# merge loads in one batch.
 UNIT_CASES = [
     dict(contexts=[4 * 300, 4 * 40], k=1, nq=1, win=True),                       # U = 2
     dict(contexts=[4 * 300], k=13, nq=1, win=False),                              # one unit, tail lanes empty
@@ -265,11 +266,13 @@ UNIT_CASES = [
     dict(contexts=[4 * 700] * 20, k=256, nq=3, win=True, prefill=True),           # 60 rows x 3 units
     dict(contexts=[4 * 2200] * 30, k=2048, nq=1, win=True),                       # 30 x 17 units over 256
     dict(contexts=[4 * 3000] * 6, k=2048, nq=50, win=True, prefill=True),         # 300 rows x 17 units
+    dict(contexts=[4 * 5000], k=4096, nq=1, win=True),                            # 33 partials of one row:
+    dict(contexts=[4 * 5000, 4 * 4500, 4 * 6000], k=4096, nq=1, win=True),        # the merge takes two batches
 ]
 
 
 @pytest.mark.parametrize("case", UNIT_CASES, ids=["k1", "k13_nowin", "k300", "nq3_prefill", "b30_k2048",
-                                                 "nq50_k2048"])
+                                                 "nq50_k2048", "k4096_b1", "k4096_b3"])
 def test_sparse_attend_unit_geometry(case):
     _log(f"sparse_attend geometry {case}")
     wl = make_small_decode(contexts=case["contexts"], layers="F", k=case["k"], nq=case["nq"],
