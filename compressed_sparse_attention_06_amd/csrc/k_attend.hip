@@ -569,15 +569,6 @@ __global__ __launch_bounds__(512) void k_attend_seg(AttendArgs a, SegArgs s) {
   }
 }
 
-// Combine the partials of rows cut between workgroups of k_attend_seg (rows
-// written whole are skipped). Workgroup w's partial for row r sits in slot 0
-// when r is the first row of w's range, else in slot 1. One workgroup per
-// (head, row), four channels per thread. The partials are taken BATCH at a
-// time, and every load of a batch goes out before any is used: lane u of each
-// wave reads the running max and sum of partial u (vector loads, so that the
-// batch does not queue on scalar registers), each thread reads its four
-// channels of every partial, and the weights reach the other lanes by
-// readlane.
 // reductions over a wave: within rows of 16 lanes by DPP, then across the
 // four rows through readlane (the result is uniform)
 __device__ __forceinline__ float wave_max64(float v) {
@@ -601,6 +592,15 @@ __device__ __forceinline__ float wave_sum64(float v) {
   return (r0 + r1) + (r2 + r3);
 }
 
+// Combine the partials of rows cut between workgroups of k_attend_seg (rows
+// written whole are skipped). Workgroup w's partial for row r sits in slot 0
+// when r is the first row of w's range, else in slot 1. One workgroup per
+// (head, row), four channels per thread. The partials are taken BATCH at a
+// time, and every load of a batch goes out before any is used: lane u of each
+// wave reads the running max and sum of partial u (vector loads, so that the
+// batch does not queue on scalar registers), each thread reads its four
+// channels of every partial, and the weights reach the other lanes by
+// readlane.
 // (waves_per_eu: few merge waves share a SIMD, so the compiler may hold a
 // whole batch in registers instead of recycling them between loads)
 template <int BATCH>
