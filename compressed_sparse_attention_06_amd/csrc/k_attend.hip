@@ -513,7 +513,7 @@ __device__ __forceinline__ void seg_finish(const AttendArgs &a, const SegArgs &s
     float *part = a.part + ((int64_t)w * 2 + slot) * CSA2_H * kPartStride;
     // 16 x 516 floats as 2064 float4
     for (int v = tid; v < CSA2_H * kPartStride / 4; v += 512)
-      *(v4f *)&part[4 * v] = *(const v4f *)&stage[4 * v];
+      store_wt(&part[4 * v], *(const v4f *)&stage[4 * v]);
   }
 }
 
