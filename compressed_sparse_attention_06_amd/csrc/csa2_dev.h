@@ -32,6 +32,20 @@ __device__ __forceinline__ void store_wt(float *p, v4f x) {
   asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1" ::"v"(p), "v"(x) : "memory");
 }
 
+// ---- sums across the four 16-lane rows of a wave ------------------------------
+// t(l) + t(l ^ 16) + t(l ^ 32) + t(l ^ 48) in every lane l, with gfx950's row
+// swaps (VALU moves, no LDS round trip): a 16-lane swap of a register with
+// itself leaves rows {0, 1} and {2, 3} split between the two results, so their
+// sum is the pair sum; the 32-lane swap does the same for the halves. The
+// additions pair the same operands as t += t(l ^ 16); t += t(l ^ 32), so the
+// result is bit for bit the same.
+__device__ __forceinline__ float sum_rows4(float t) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(t), __float_as_uint(t), false, false);
+  const float s = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // ---- order-preserving keys for fp32 scores ---------------------------------
 // Larger score -> larger key. -0 is folded onto +0 so that equal values tie.
 __device__ __forceinline__ uint32_t score_key(float s) {

@@ -160,10 +160,8 @@ __global__ __launch_bounds__(256) void k_index_score(ScoreArgs a) {
         t2 = wh * fmaxf(p, 0.f);
       }
       // sum the four heads (lanes n, n+16, n+32, n+48 hold heads 0..3 of column n)
-      t1 += __shfl_xor(t1, 16);
-      t1 += __shfl_xor(t1, 32);
-      t2 += __shfl_xor(t2, 16);
-      t2 += __shfl_xor(t2, 32);
+      t1 = sum_rows4(t1);
+      t2 = sum_rows4(t2);
       if (lane < 32) {
         const int64_t col = e0 + lane;  // lanes 0..15: first tile; 16..31: second tile
         const float sc = (lane < 16) ? t1 : t2;
@@ -321,11 +319,7 @@ __global__ __launch_bounds__(256) void k_index_score_mq(ScoreArgs a, int32_t qbl
         p2 = fmaf(C2[1], sq[q][1] * l2[1], p2);
         p2 = fmaf(C2[2], sq[q][2] * h2[0], p2);
         p2 = fmaf(C2[3], sq[q][3] * h2[1], p2);
-        float t1 = wh[q] * fmaxf(p1, 0.f), t2 = wh[q] * fmaxf(p2, 0.f);
-        t1 += __shfl_xor(t1, 16);
-        t1 += __shfl_xor(t1, 32);
-        t2 += __shfl_xor(t2, 16);
-        t2 += __shfl_xor(t2, 32);
+        const float t1 = sum_rows4(wh[q] * fmaxf(p1, 0.f)), t2 = sum_rows4(wh[q] * fmaxf(p2, 0.f));
         if (lane < 32 && col < col_end) {
           const float sc = (lane < 16) ? t1 : t2;
           const int64_t r = (int64_t)b * a.nq + t0 + q;
