@@ -23,10 +23,31 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) {
   return v;
 }
 
+// Reductions over the 64 lanes of a wave, the result in every lane: DPP moves
+// within each row of 16 lanes (swap neighbours, swap pairs, mirror within 8,
+// mirror within 16), then gfx950's 16- and 32-lane row swaps of the register
+// with itself, whose two results together hold both rows of each pair. All
+// VALU: no LDS permutes.
+template <class OP>
+__device__ __forceinline__ uint32_t wave_reduce(uint32_t v, OP op) {
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));  // row_mirror
+  const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = op((uint32_t)a[0], (uint32_t)a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return op((uint32_t)b[0], (uint32_t)b[1]);
+}
+
 __device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-  return v;
+  return wave_reduce(v, [](uint32_t x, uint32_t y) { return x + y; });
+}
+__device__ __forceinline__ uint32_t wave_min(uint32_t v) {
+  return wave_reduce(v, [](uint32_t x, uint32_t y) { return x < y ? x : y; });
+}
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+  return wave_reduce(v, [](uint32_t x, uint32_t y) { return x > y ? x : y; });
 }
 
 // Exclusive prefix sum of one value per thread in thread order; returns this

@@ -35,6 +35,7 @@
 // M tiles cover the 16 rows and share each dequantised key tile.
 #include "csa2_dev.h"
 #include "kernels.h"
+#include "block_ops.h"
 
 namespace csa2 {
 
@@ -104,21 +105,9 @@ __device__ __forceinline__ bool pt_float_bounds(uint64_t lo, uint64_t hi, float 
   return whole && lok && hok;
 }
 
-__device__ __forceinline__ uint32_t pt_wave_sum(uint32_t v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-  return v;
-}
-
-__device__ __forceinline__ uint32_t pt_wave_incl_scan(uint32_t v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t o = __shfl_up(v, off);
-    if (lane >= off) v += o;
-  }
-  return v;
-}
+// wave sums and inclusive scans: the DPP / row-swap forms of block_ops.h
+__device__ __forceinline__ uint32_t pt_wave_sum(uint32_t v) { return wave_sum(v); }
+__device__ __forceinline__ uint32_t pt_wave_incl_scan(uint32_t v) { return wave_inclusive_scan(v); }
 
 // Wave-level: in half `half` of the pair histogram h, the highest bin T whose
 // count together with every higher bin reaches `need` (1 <= need <= total).

@@ -806,11 +806,8 @@ hipError_t launch_select_direct(const DirectArgs &a, int rows, int ntarget, hipS
 
 // min and max over the workgroup (s: ROW_NT / 64 x 2 words)
 __device__ __forceinline__ void block_minmax(uint32_t lo, uint32_t hi, uint32_t *s, uint32_t &mn, uint32_t &mx) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    lo = min(lo, (uint32_t)__shfl_xor((int)lo, off));
-    hi = max(hi, (uint32_t)__shfl_xor((int)hi, off));
-  }
+  lo = wave_min(lo);
+  hi = wave_max(hi);
   const int t = threadIdx.x, nw = blockDim.x >> 6;
   if ((t & 63) == 0) {
     s[2 * (t >> 6)] = lo;
