@@ -175,10 +175,10 @@ __device__ void pt_find_bin(const uint32_t *h, int half, uint32_t need, int *T, 
     }
   }
   const uint64_t m = __ballot(hit);
-  const int src = m ? (int)__ffsll((unsigned long long)m) - 1 : 0;
-  *T = __shfl(t, src);
-  *above = __shfl(a, src);
-  *cnt = __shfl(cc, src);
+  const int src = m ? (int)__ffsll((unsigned long long)m) - 1 : 0;  // uniform: from the ballot
+  *T = __builtin_amdgcn_readlane(t, src);
+  *above = (uint32_t)__builtin_amdgcn_readlane((int)a, src);
+  *cnt = (uint32_t)__builtin_amdgcn_readlane((int)cc, src);
 }
 
 // Is row r taking part in a sweep of this kind? A collect row waits while
@@ -550,7 +550,7 @@ __global__ __launch_bounds__(PT_NT, PT_WG_PER_CU) void k_prefill_topk(PrefillTop
         if (p < K) out[p] = wi * 32 + bit;
         ++p;
       }
-      pos += (int32_t)__shfl(incl, 63);
+      pos += __builtin_amdgcn_readlane((int)incl, 63);
     }
     for (int p = pos + lane; p < K; p += 64) out[p] = -1;
   }
