@@ -90,6 +90,22 @@ def test_index_score_full(case):
     _check_scores(g, o, "full")
 
 
+@pytest.mark.parametrize("nq", [2, 3, 6, 8])
+def test_index_score_rows_kernels_agree(nq):
+    """Several query rows per request (the kernel that reads each key once
+    for all of them) give, bit for bit, what one row at a time gives: both
+    multiply the same FP4 codes on the matrix cores and apply scales, ReLU,
+    weights and the head sum in the same fp32 order."""
+    wl = make_small_decode([4 * 6000, 4 * 1500], layers="F", k=16, nq=nq, page_size=64, shuffle=True)
+    L, c = wl.layers[0], wl.caches[0]
+    dc = dev_cache(c)
+    g = csa2.index_score(dc, t(L.qix_codes), t(L.qix_scales), t(L.w)).cpu().numpy()
+    for q in range(nq):
+        one = csa2.index_score(dc, t(L.qix_codes[:, q:q + 1]), t(L.qix_scales[:, q:q + 1]),
+                               t(L.w[:, q:q + 1])).cpu().numpy()
+        assert np.array_equal(g[:, q:q + 1].view(np.uint32), one.view(np.uint32)), f"row {q} of {nq}"
+
+
 def test_index_score_histogram():
     """The optional histogram counts each finite score's top 12 order-key bits."""
     wl = make_small_decode([4 * 9000, 4 * 100], layers="F", k=16, page_size=64, shuffle=True)
