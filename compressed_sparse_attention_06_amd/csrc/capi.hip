@@ -98,7 +98,7 @@ void attend_geometry(WsLayout &L, int64_t rows, int32_t k, int32_t win_cap) {
   L.att_U = (int32_t)((span + 127) / 128);
   L.att_T = rows * L.att_U;
   L.att_G = (int32_t)std::min<int64_t>(L.att_T, csa2::kSegMaxWg);
-  if (rows <= csa2::kSegMaxWg) {
+  if (rows >= 1 && rows <= csa2::kSegMaxWg) {
     const int64_t U = L.att_U;
     const int64_t longest = (L.att_T + L.att_G - 1) / L.att_G;  // units of the plain split's largest range
     int64_t P = std::min<int64_t>(U, csa2::kSegMaxWg / rows);
