@@ -284,11 +284,14 @@ UNIT_CASES = [
     dict(contexts=[4 * 3000] * 6, k=2048, nq=50, win=True, prefill=True),         # 300 rows x 17 units
     dict(contexts=[4 * 5000], k=4096, nq=1, win=True),                            # 33 partials of one row:
     dict(contexts=[4 * 5000, 4 * 4500, 4 * 6000], k=4096, nq=1, win=True),        # the merge takes two batches
+    dict(contexts=[4 * 2200] * 16, k=2048, nq=1, win=True),                       # 9 workgroups per row
+    dict(contexts=[4 * 2200] * 40, k=2048, nq=1, win=True),                       # 6 per row, 240 in all
 ]
 
 
 @pytest.mark.parametrize("case", UNIT_CASES, ids=["k1", "k13_nowin", "k300", "nq3_prefill", "b30_k2048",
-                                                 "nq50_k2048", "k4096_b1", "k4096_b3"])
+                                                 "nq50_k2048", "k4096_b1", "k4096_b3", "b16_k2048",
+                                                 "b40_k2048"])
 def test_sparse_attend_unit_geometry(case):
     _log(f"sparse_attend geometry {case}")
     wl = make_small_decode(contexts=case["contexts"], layers="F", k=case["k"], nq=case["nq"],
