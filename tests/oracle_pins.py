@@ -420,6 +420,67 @@ def pin_layer_full_pool_nesting():
                            idx_in=allpool)
     assert (rr["idx"] == r["idx"]).all()
     assert np.allclose(rr["out"], r["out"], rtol=0, atol=0)
+    # Reindex over the Full layer's own pool (ascending ids of a strict subset, then -1
+    # pads for the short request) with the same indexer query: the Full top-K lies inside
+    # the pool, so the Reindex selection is the Full one
+    wl2 = make_small_decode([600, 257], layers="F", k=24, pool=100, page_size=16, shuffle=True)
+    L2, c2 = wl2.layers[0], wl2.caches[0]
+    r2 = oracle.layer_step("F", c2, L2.win, L2.q, L2.qix_codes, L2.qix_scales, L2.w, k=24, pool=100)
+    assert (r2["pool"][1, 0] == -1).sum() == 100 - 64  # the 257-token request has 64 entries
+    rr2 = oracle.layer_step("R", c2, L2.win, L2.q, L2.qix_codes, L2.qix_scales, L2.w, k=24, pool=100,
+                            idx_in=r2["pool"])
+    assert (rr2["idx"] == r2["idx"]).all()
+    assert (rr2["out"] == r2["out"]).all()
+
+
+def _brute_select(scores_row, ids, k):
+    """Top-k of (score, id) pairs by (score desc, id asc) with Python's sort; ascending ids, -1 pads."""
+    pairs = sorted(((float(scores_row[i]), int(i)) for i in ids), key=lambda t: (-t[0], t[1]))
+    sel = sorted(i for _, i in pairs[:k])
+    return sel + [-1] * (k - len(sel))
+
+
+def pin_layer_reindex_pool_mapping():
+    """Reindex with a shuffled pool that is not arange(n) -- a random subset in random order
+    with -1 pads and ids at or past the request's entry count -- scores exactly the pool's
+    ids with the layer's own indexer query and returns entry ids, not pool slots. Expected
+    set: the scores of every entry under that query, restricted to the pool's valid ids and
+    ranked by a plain sort on (score desc, id asc)."""
+    wl = make_small_decode([2400, 1030], layers="FR", k=20, pool=96, page_size=16, shuffle=True)
+    c, R = wl.caches[0], wl.layers[1]
+    n_ent = [int(x) for x in c.n_entries]  # 600 and 257
+    cap = c.block_table.shape[1] * c.page_size
+    P, K = 96, 20
+    rng = np.random.default_rng(5)
+    pool = np.full((2, 1, P), -1, np.int32)
+    for b, n in enumerate(n_ent):
+        ids = rng.choice(np.arange(1, n), size=70, replace=False)  # never entry 0, never in order
+        extra = [n, n + 3, cap - 1, 10 ** 7, -1, -5]                # not entries of this request
+        row = np.concatenate([ids, extra]).astype(np.int32)
+        rng.shuffle(row)
+        pool[b, 0, :row.size] = row
+    assert not (np.diff(pool[0, 0, :70]) > 0).all()
+    full = oracle.index_score(c, R.qix_codes, R.qix_scales, R.w)  # every entry, this layer's query
+    want = np.full((2, 1, K), -1, np.int32)
+    for b, n in enumerate(n_ent):
+        valid = [int(s) for s in pool[b, 0] if 0 <= s < n]
+        want[b, 0] = _brute_select(full[b, 0], valid, K)
+    rr = oracle.layer_step("R", c, R.win, R.q, R.qix_codes, R.qix_scales, R.w, k=K, pool=P, idx_in=pool)
+    assert (rr["idx"] == want).all(), (rr["idx"], want)
+    # the layer attends the entries it selected, with its own query and window
+    o, l, _ = oracle.sparse_attend(c, want, R.q, R.win, sm_scale=TAU)
+    assert (rr["out"] == o).all() and (rr["lse"] == l).all()
+    # the pool's own scores are the full scores at the pool's ids (-inf elsewhere)
+    ps = oracle.index_score(c, R.qix_codes, R.qix_scales, R.w, cand=pool)
+    for b, n in enumerate(n_ent):
+        for j, s in enumerate(pool[b, 0]):
+            assert ps[b, 0, j] == (full[b, 0, s] if 0 <= s < n else -np.inf)
+    # a pool shorter than K takes all its valid ids, then -1
+    short = np.full((2, 1, P), -1, np.int32)
+    short[:, 0, :5] = [[7, 3, 599, 600, 11], [200, 256, 257, 1, 0]]
+    rs = oracle.layer_step("R", c, R.win, R.q, R.qix_codes, R.qix_scales, R.w, k=K, pool=P, idx_in=short)
+    assert rs["idx"][0, 0].tolist() == [3, 7, 11, 599] + [-1] * (K - 4)
+    assert rs["idx"][1, 0].tolist() == [0, 1, 200, 256] + [-1] * (K - 4)
 
 
 def pin_short_rows_pad():
@@ -594,7 +655,7 @@ ALL_PINS = [
     pin_score_all_ones, pin_score_one_hot_signs, pin_score_all_heads_negative,
     pin_score_entry_placement, pin_score_block_causal, pin_score_candidates,
     pin_score_exact_product_bound, pin_topk_ties_and_padding, pin_topk_bruteforce,
-    pin_layer_full_pool_nesting, pin_short_rows_pad, pin_attend_golden,
+    pin_layer_full_pool_nesting, pin_layer_reindex_pool_mapping, pin_short_rows_pad, pin_attend_golden,
     pin_attend_dense_equals_sdpa, pin_attend_special_cases, pin_attend_large_logits,
     pin_attend_permutation_and_window_rows, pin_prefill_window_bounds,
     pin_reuse_equals_full_given_indices, pin_paged_equals_contiguous,

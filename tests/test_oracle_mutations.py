@@ -44,6 +44,9 @@ MUTATIONS = [
     ("window row scale /240", "rs = amax > 0.0f ? amax / 448.0f : 1.0f;", "rs = amax > 0.0f ? amax / 240.0f : 1.0f;"),
     ("append slot reversed", "int64_t row = (int64_t)page * c->page_size + s % c->page_size;",
      "int64_t row = (int64_t)page * c->page_size + (c->page_size - 1 - s % c->page_size);"),
+    ("Reindex scores the first pool columns", "const int32_t *cand = (mode == 0) ? NULL : idx_in;",
+     "const int32_t *cand = NULL;"),
+    ("Reindex returns pool slots", "orc_topk(sc, cand, B, nq, n, k, idx_out);", "orc_topk(sc, NULL, B, nq, n, k, idx_out);"),
     ("append indexer into main KV scales", "c->ix_codes + row * (ORC_DI / 2), c->ix_scales + row * (ORC_DI / ORC_G));",
      "c->ix_codes + row * (ORC_DI / 2), c->kv_scales + row * (ORC_D / ORC_G));"),
 ]
