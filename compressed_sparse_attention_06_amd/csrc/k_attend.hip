@@ -86,9 +86,6 @@ __device__ __forceinline__ void window_range(const AttendArgs &a, int r, int b, 
 #define AS_UNIT 128   // positions per unit (8 waves x 16)
 #define AS_PPITCH 136 // halfs per LDS row of P (128 + 8)
 #define AS_RPITCH 512 // halfs per LDS row of the R tile (unpadded; 16-byte chunks are swizzled)
-#ifndef SEG_QLO_LDS
-#define SEG_QLO_LDS 1 // the low halves of Q are read from LDS at each step
-#endif
 
 // R tile swizzle: in row r, the 16-byte chunk c of each 256-byte block is
 // stored at chunk c ^ seg_rswz(r). Sixteen consecutive rows then fill every
@@ -98,17 +95,10 @@ __device__ __forceinline__ int seg_rswz(int r) { return ((r & 3) << 1) | ((r >> 
 
 struct SegShared {
   union {
-    struct {
-      _Float16 q[CSA2_H * AT_PITCH];
-#if !SEG_QLO_LDS
-      _Float16 qlo[CSA2_H * AT_PITCH];
-#endif
-    };
+    _Float16 q[CSA2_H * AT_PITCH];  // hi halves of Q, staged once per row
     _Float16 r[AS_UNIT * AS_RPITCH];
   };
-#if SEG_QLO_LDS
-  _Float16 qlo[CSA2_H * AT_PITCH];
-#endif
+  _Float16 qlo[CSA2_H * AT_PITCH];  // lo halves of Q, read at every step
   _Float16 p[CSA2_H * AS_PPITCH];
   float wmax[CSA2_H][8], wsum[CSA2_H][8];  // [head][wave]
   float m[CSA2_H], l[CSA2_H], qexp[CSA2_H];
@@ -116,9 +106,6 @@ struct SegShared {
 
 struct SegQ {
   v8h qa[16];
-#if !SEG_QLO_LDS
-  v8h ql[16];
-#endif
   float qs[4];  // logit scale (sm_scale * log2 e * 2^e) of heads 4g + i
 };
 
@@ -175,38 +162,50 @@ __device__ __forceinline__ int32_t seg_fetch_page(const AttendArgs &a, int64_t y
   return a.c.block_table[(int64_t)b * a.c.max_pages + pg];
 }
 
-// The address depends only on the id and the page word; whether the id is
-// below the request's entry count is decided when the unit is computed.
+// The address depends only on the id and the page word (a position with no
+// entry reads physical row 0, always in bounds). Its bytes must not reach the
+// R tile: the scale words of such a position are zeroed, and since E2M1 has
+// no NaN or infinity every code times a zero scale is 0. `use` is false for
+// positions past k; ids at or past the request's entry count (`nent`, an
+// unwritten slot) are not rows either.
 __device__ __forceinline__ void seg_load_entry(const AttendArgs &a, int32_t id, int32_t page, int kq,
-                                               SegSlice &f) {
+                                               int32_t nent, bool use, SegSlice &f) {
   const int sh = a.c.page_shift;
-  const bool ok = id >= 0 && (id >> sh) < a.c.max_pages && page >= 0 && page < a.c.num_pages;
-  const int64_t crow = ok ? ((int64_t)page << sh) + (id & ((1 << sh) - 1)) : 0;
+  const bool addr_ok = id >= 0 && (id >> sh) < a.c.max_pages && page >= 0 && page < a.c.num_pages;
+  const int64_t crow = addr_ok ? ((int64_t)page << sh) + (id & ((1 << sh) - 1)) : 0;
   const uint8_t *cp = a.c.kv_codes + crow * 256 + kq * 64;
 #pragma unroll
   for (int i = 0; i < 4; ++i) f.c[i] = *(const v4i *)(cp + 16 * i);
   const v2f sc = *(const v2f *)(a.c.kv_scales + crow * 32 + kq * 8);
-  f.s0 = (uint32_t)__float_as_int(sc[0]);
-  f.s1 = (uint32_t)__float_as_int(sc[1]);
+  const bool ok = addr_ok && use && id < nent;
+  f.s0 = ok ? (uint32_t)__float_as_int(sc[0]) : 0u;
+  f.s1 = ok ? (uint32_t)__float_as_int(sc[1]) : 0u;
   f.rs = 1.f;
   f.tag = id;
   f.kind = ok ? 1 : 0;
 }
 
+// A window position with no visible row reads the request's row 0 (in
+// bounds) and keeps zero codes and a unit row scale, so that a NaN byte or
+// scale of an unwritten row never reaches the R tile or P.
 __device__ __forceinline__ void seg_load_window(const AttendArgs &a, int b, int32_t j, bool ok, int kq,
                                                 SegSlice &f) {
   const int32_t wr = b * a.win_rows + (ok ? j : 0);
   const uint8_t *src = a.win_codes + (int64_t)wr * CSA2_D + kq * 128;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) f.c[i] = *(const v4i *)(src + 16 * i);
+  for (int i = 0; i < 4; ++i) {
+    const v4i x = *(const v4i *)(src + 16 * i);
+    f.c[i] = ok ? x : (v4i){0, 0, 0, 0};
+  }
   f.s0 = f.s1 = 0u;
-  f.rs = a.win_row_scale ? a.win_row_scale[wr] : 1.f;
+  const float rs = a.win_row_scale ? a.win_row_scale[wr] : 1.f;
+  f.rs = ok ? rs : 1.f;
   f.tag = wr;
   f.kind = ok ? 2 : 0;
 }
 
 __device__ __forceinline__ void seg_fetch_rows(const AttendArgs &a, int64_t y, int64_t u_end, int32_t U,
-                                               int prow, int kq, const SegFetch &fe, SegSlice &s) {
+                                               int prow, int kq, int32_t nent, const SegFetch &fe, SegSlice &s) {
   // a position with no row still feeds the R tile: zeros, never stale registers
 #pragma unroll
   for (int i = 0; i < 4; ++i) s.c[i] = (v4i){0, 0, 0, 0};
@@ -219,8 +218,7 @@ __device__ __forceinline__ void seg_fetch_rows(const AttendArgs &a, int64_t y, i
   const int32_t pos = j * AS_UNIT + prow;
   const int32_t kw = seg_kw(a.k);
   if (j * AS_UNIT + (prow & ~15) < kw) {  // entry wave
-    seg_load_entry(a, fe.id, fe.page, kq, s);
-    if (pos >= a.k) s.kind = 0;
+    seg_load_entry(a, fe.id, fe.page, kq, nent, pos < a.k, s);
     return;
   }
   if (!a.win_codes) return;  // no window
@@ -261,10 +259,14 @@ __device__ __forceinline__ void seg_qk(const AttendArgs &a, const SegShared &sh,
   v4i h2[4];
   if constexpr (KIND == SPLIT_WINDOW) {
     if (a.win_codes) {
-      const int32_t wr = (f.kind == 2) ? f.tag : 0;
+      const bool ok = f.kind == 2;
+      const int32_t wr = ok ? f.tag : 0;
       const uint8_t *src = a.win_codes + (int64_t)wr * CSA2_D + kq * 128 + 64;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) h2[i] = *(const v4i *)(src + 16 * i);
+      for (int i = 0; i < 4; ++i) {
+        const v4i x = *(const v4i *)(src + 16 * i);
+        h2[i] = ok ? x : (v4i){0, 0, 0, 0};  // no bytes of a position without a row
+      }
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) h2[i] = (v4i){0, 0, 0, 0};
@@ -272,12 +274,8 @@ __device__ __forceinline__ void seg_qk(const AttendArgs &a, const SegShared &sh,
   }
   // byte offset of the lane's chunk 0 in the R tile (row prow, block kq), swizzled
   const uint32_t rbase = (uint32_t)(prow * AS_RPITCH * 2 + kq * 256 + 16 * seg_rswz(prow));
-#if SEG_QLO_LDS
   const _Float16 *qlo = &sh.qlo[n * AT_PITCH + kq * 128];
 #define CSA2_QLO(KS) (*(const v8h *)(qlo + 8 * (KS)))
-#else
-#define CSA2_QLO(KS) (q.ql[KS])
-#endif
   v2h sc[4];
   if constexpr (KIND == SPLIT_ENTRIES) {
     sc[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(f.s0, 1.0f, false);
@@ -343,9 +341,6 @@ __device__ __forceinline__ void seg_prepare_q(const AttendArgs &a, SegShared &sh
 #pragma unroll
   for (int ks = 0; ks < 16; ++ks) {
     q.qa[ks] = *(const v8h *)&sh.q[n * AT_PITCH + g * 128 + 8 * ks];
-#if !SEG_QLO_LDS
-    q.ql[ks] = *(const v8h *)&sh.qlo[n * AT_PITCH + g * 128 + 8 * ks];
-#endif
   }
   __syncthreads();  // the R tile overwrites the staged Q
 }
@@ -536,6 +531,7 @@ __global__ __launch_bounds__(512) void k_attend_seg(AttendArgs a, SegArgs s) {
     SegFetch fc, fn;
     int32_t id2;
     SegSlice sc;
+    const int32_t nent = a.c.n_entries[row / a.nq];
     {
       float qv[32];
       seg_load_q(a, row, qv);
@@ -544,18 +540,17 @@ __global__ __launch_bounds__(512) void k_attend_seg(AttendArgs a, SegArgs s) {
       id2 = seg_fetch_id(a, x + 2, xe, U, prow);
       fc.page = seg_fetch_page(a, x, xe, U, prow, fc.id);
       fn.page = seg_fetch_page(a, x + 1, xe, U, prow, fn.id);
-      seg_fetch_rows(a, x, xe, U, prow, g, fc, sc);
+      seg_fetch_rows(a, x, xe, U, prow, g, nent, fc, sc);
       seg_prepare_q(a, sh, qv, q);
     }
     // pipeline: rows of unit x in sc, id and page word of x + 1 in fn, id of x + 2 in id2
-    const int32_t nent = a.c.n_entries[row / a.nq];
     v4f accO[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) accO[i] = (v4f){0.f, 0.f, 0.f, 0.f};
     for (; x < xe; ++x) {
       // rows of x + 1, page word of x + 2 and id of x + 3 load while unit x computes
       SegSlice sn;
-      seg_fetch_rows(a, x + 1, xe, U, prow, g, fn, sn);
+      seg_fetch_rows(a, x + 1, xe, U, prow, g, nent, fn, sn);
       const int32_t pg2 = seg_fetch_page(a, x + 2, xe, U, prow, id2);
       const int32_t id3 = seg_fetch_id(a, x + 3, xe, U, prow);
       seg_unit(a, sh, (int32_t)(x % U) * AS_UNIT, nent, sc, q, accO);

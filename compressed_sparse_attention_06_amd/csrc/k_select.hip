@@ -800,8 +800,9 @@ hipError_t launch_select_direct(const DirectArgs &a, int rows, int ntarget, hipS
 // found exactly by radix levels over the row's own key range: level 1 bins
 // key - kmin by its top 12 significant bits, the next levels refine the
 // boundary bin 12 bits at a time. Every key above the threshold is taken, and
-// of the keys equal to it the first ones in column order (the lower entry ids
-// when ids grow with the column). Ids are written in column order, then -1.
+// of the keys equal to it those with the lowest entry ids (by column, or by
+// radix levels over the mapped ids when a map is given). Ids are written in
+// column order, then -1.
 #define ROW_NT 1024
 
 // min and max over the workgroup (s: ROW_NT / 64 x 2 words)
@@ -919,22 +920,77 @@ __global__ __launch_bounds__(ROW_NT) void k_select_row(DirectArgs a) {
     }
   }
 
-  // ---- emission in column order ----
-  uint32_t na = 0, ne = 0;
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    na += key[j] > thr ? 1u : 0u;
-    ne += key[j] == thr ? 1u : 0u;
-  }
-  uint32_t tot;
-  const uint32_t eb = block_exclusive_scan(ne, scan, &tot);  // equal keys in earlier threads
-  const int eq_take = max(0, min((int)ne, take_eq - (int)eb));
-  const uint32_t off = block_exclusive_scan(na + (uint32_t)eq_take, scan, &tot);
+  // ---- ties at the threshold ----
+  // Of the keys equal to thr, the take_eq with the lowest ids are taken.
+  // Without a map the id is the column, so these are the first ones in column
+  // order. With a map, column order is not id order: when only some of them
+  // are taken, radix levels over their ids (bits 31..20, 19..8, 7..0 of an
+  // order key in which a lower id is larger) find the boundary id exactly.
+  // Afterwards an equal key is taken when its id key's bits from ishift up
+  // exceed iprefix, or equal it and it is among the first ineed such.
   const int32_t *map = a.cand_map ? a.cand_map + (int64_t)r * a.n_cols : nullptr;
+  auto id_key = [&](int j) { return ~((uint32_t)map[min(c0 + j, a.n_cols - 1)] ^ 0x80000000u); };
+  uint32_t ne = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) ne += key[j] == thr ? 1u : 0u;
+  uint32_t tot_eq;
+  block_exclusive_scan(ne, scan, &tot_eq);
+  int ishift = 32;  // 32: ids play no part
+  uint32_t iprefix = 0;
+  int ineed = take_eq;
+  if (map && take_eq < (int)tot_eq) {  // uniform over the workgroup
+    constexpr int kShift[3] = {20, 8, 0};
+    for (int level = 0; level < 3; ++level) {
+      const int shift = kShift[level];
+      for (int i = t; i < DIG_BINS; i += ROW_NT) hist[i] = 0;
+      __syncthreads();
+      const uint32_t mask = ishift >= 32 ? (uint32_t)(DIG_BINS - 1) : ((1u << (ishift - shift)) - 1u);
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        if (key[j] != thr) continue;
+        const uint32_t ik = id_key(j);
+        if (ishift >= 32 || (ik >> ishift) == iprefix) atomicAdd(&hist[(ik >> shift) & mask], 1u);
+      }
+      __syncthreads();
+      hist_threshold_n<DIG_BINS, ROW_NT, true>(hist, (uint32_t)ineed, scan, hout);
+      const int bin = hout[0];
+      const int before = hout[1];
+      __syncthreads();
+      if (bin < 0) break;  // the current set holds exactly ineed keys: all are taken
+      ineed -= before;
+      iprefix = (ishift >= 32 ? 0u : (iprefix << (ishift - shift))) | (uint32_t)bin;
+      ishift = shift;
+    }
+  }
+  // bit j of take_m: key j taken outright; of eq_m: key j equal to thr with
+  // an id matching the boundary prefix (the first ineed of those are taken)
+  uint32_t take_m = 0, eq_m = 0;
+  if (ishift >= 32) {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      take_m |= (key[j] > thr ? 1u : 0u) << j;
+      eq_m |= (key[j] == thr ? 1u : 0u) << j;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const uint32_t ik = key[j] == thr ? id_key(j) >> ishift : 0u;
+      take_m |= (key[j] > thr || (key[j] == thr && ik > iprefix) ? 1u : 0u) << j;
+      eq_m |= (key[j] == thr && ik == iprefix ? 1u : 0u) << j;
+    }
+  }
+
+  // ---- emission in column order ----
+  uint32_t tot;
+  const uint32_t eb = block_exclusive_scan((uint32_t)__builtin_popcount(eq_m), scan, &tot);
+  const int eq_take = max(0, min(__builtin_popcount(eq_m), ineed - (int)eb));
+  const uint32_t off = block_exclusive_scan((uint32_t)(__builtin_popcount(take_m) + eq_take), scan, &tot);
   int o = (int)off, e = 0;
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
-    const bool take = key[j] > thr || (key[j] == thr && e++ < eq_take);
+    const bool eq = (eq_m >> j) & 1u;
+    const bool take = ((take_m >> j) & 1u) || (eq && e < eq_take);
+    e += eq ? 1 : 0;
     if (take) {
       gout[o++] = map ? map[c0 + j] : c0 + j;
     }

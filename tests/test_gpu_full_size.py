@@ -56,7 +56,7 @@ def test_full_size_b32_128k():
 
 def test_full_size_b8_1m():
     """8 requests x 1,048,576 tokens, [Full, Reindex (pool 16384), Reuse x4], top-2048."""
-    _check_requests("b8_1m_full_reindex_reuse4", [5])
+    _check_requests("b8_1m_full_reindex_reuse4", [0, 7])
 
 
 def test_full_size_spec6_1m():
@@ -83,13 +83,28 @@ def test_full_size_ragged_paged():
 
 def test_full_size_prefill_chunk():
     """4096 query tokens at positions 126976..131071 of a 131072-token context:
-    block-causal scoring of 32768 entries, per-query top-2048, causal window."""
+    block-causal scoring of 32768 entries, per-query top-2048, causal window.
+    The oracle recomputes 64 query rows spread evenly over the chunk (first and
+    last included); the fused scoring + top-K kernel's selection is compared
+    bit for bit with the materialised path (prefill scoring kernel, then
+    csa2_topk) on every one of the 4096 rows."""
+    import compressed_sparse_attention_06_amd as csa2
+    from devutil import dev_cache, t
+
     _log("prefill: generating")
     wl = make_prefill_workload()
     _log(f"prefill: GPU, {wl.nq} query rows")
     res_g = run_gpu(wl)
-    qs = [0, 1, 1234, 2047, 3000, 4095]
+    L, c = wl.layers[0], wl.caches[0]
+    _log("prefill: materialised scores + csa2_topk on all rows")
+    sc = csa2.index_score(dev_cache(c), t(L.qix_codes), t(L.qix_scales), t(L.w), q_pos=t(wl.q_pos))
+    ref = csa2.topk(sc, wl.k).cpu().numpy()
+    del sc
+    g = res_g[0]["idx"]
+    assert (g == ref).all(), f"fused and materialised selections differ in {int((g != ref).any(axis=-1).sum())} rows"
+    qs = sorted(set(int(round(x)) for x in np.linspace(0, wl.nq - 1, 64)))
+    assert len(qs) == 64
     sub = slice_queries(wl, qs)
-    _log(f"prefill: oracle on query rows {qs}")
+    _log(f"prefill: oracle on {len(qs)} query rows")
     res_o = oracle.run_workload(sub, want_scores=True)
-    compare_workload(sub, _slice_res(res_g, qs=qs), res_o, f"prefill rows {qs}")
+    compare_workload(sub, _slice_res(res_g, qs=qs), res_o, f"prefill {len(qs)} rows")

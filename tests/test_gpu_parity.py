@@ -2,7 +2,9 @@
 
 Tolerances (the bars every GPU parity test applies):
  * dequantised values: bit-exact (fp16 of the FP4 path, fp32 of E4M3);
- * index scores: |gpu - oracle| <= 1e-6 |oracle| + 1e-6 max|row|;
+ * index scores: |gpu - oracle| <= 1e-6 |oracle| + 1e-6 max|row| (the second
+   term covers a head sum that cancels: fp32 rounding scales with the terms,
+   not with the result);
  * top-K id sets: equal after dropping ids whose oracle score lies within
    1e-5 (relative) of the oracle's K-th score; exact when scores are exact;
  * attention, given the oracle's indices: out max-abs <= 2e-3, mean-abs <=
@@ -67,9 +69,10 @@ def _check_scores(g, o, what):
     g = np.asarray(g, np.float64)
     masked = np.isneginf(o)
     assert (np.isneginf(g) == masked).all(), f"{what}: masked columns differ"
-    rowmax = np.where(masked, 0, np.abs(o)).max(axis=-1, keepdims=True)
-    tol = SCORE_RTOL * np.abs(np.where(masked, 0, o)) + SCORE_RTOL * rowmax
-    d = np.abs(np.where(masked, 0, g - o))
+    o0, g0 = np.where(masked, 0, o), np.where(masked, 0, g)  # no inf - inf
+    rowmax = np.abs(o0).max(axis=-1, keepdims=True)
+    tol = SCORE_RTOL * np.abs(o0) + SCORE_RTOL * rowmax
+    d = np.abs(g0 - o0)
     assert (d <= tol).all(), f"{what}: score error {d.max():.3e}"
 
 
@@ -219,6 +222,51 @@ def test_topk_many_rows_one_workgroup_each(dist):
     g = csa2.topk(t(s32), k, cand=t(cand)).cpu().numpy()
     o = oracle.topk(s32.astype(np.float64), k, cand=cand)
     assert (g == o).all()
+    # a permuted map: keys tied at the threshold are settled by the mapped id,
+    # not by the column (the "ties" rows hold ~300 keys per value)
+    cand = np.stack([rng.choice(10 ** 6, size=n, replace=False) for _ in range(rows)])[:, None, :]
+    cand = cand.astype(np.int32)
+    g = csa2.topk(t(s32), k, cand=t(cand)).cpu().numpy()
+    o = oracle.topk(s32.astype(np.float64), k, cand=cand)
+    assert (g == o).all(), f"{int((g != o).any(axis=-1).sum())} rows differ"
+
+
+def test_reindex_shuffled_pool_many_rows():
+    """A Reindex layer over 40 requests whose pools (5000 of each request's 6000
+    entries, in random order, with -1 pads and ids past the entry count) are
+    not ascending, so selection runs one workgroup per row with an id map; 70%
+    of the indexer keys are zero, so about half of each selection is a tie at
+    score 0 settled by entry id. Selected sets against the oracle (exact: the
+    tied scores are exactly 0 on both sides; elsewhere outside the 1e-5 band),
+    attention against the oracle's attention over the GPU's selection."""
+    _log("reindex, shuffled pool, 40 rows")
+    B, P, K = 40, 5000, 2048
+    wl = make_small_decode([4 * 6000] * B, layers="FR", k=K, pool=P, page_size=64, shuffle=True)
+    c, R = wl.caches[0], wl.layers[1]
+    rng = np.random.default_rng(21)
+    kill = rng.random(c.ix_codes.shape[0] * c.ix_codes.shape[1]) < 0.7
+    c.ix_codes.reshape(-1, c.ix_codes.shape[-1])[kill] = 0
+    pool = np.full((B, 1, P), -1, np.int32)
+    for b in range(B):
+        ids = rng.choice(6000, size=P - 40, replace=False)
+        row = np.concatenate([ids, [6000, 6001, 10 ** 6, -3], np.full(36, -1)]).astype(np.int32)
+        rng.shuffle(row)
+        pool[b, 0] = row
+    call = csa2.LayerCall("R", dev_cache(c), dev_window(R.win), t(R.q), K, pool=P, qix_codes=t(R.qix_codes),
+                          qix_scales=t(R.qix_scales), w=t(R.w), idx_in=t(pool))
+    call()
+    torch.cuda.synchronize()
+    g_idx = call.idx_out.cpu().numpy()
+    o = oracle.layer_step("R", c, R.win, R.q, R.qix_codes, R.qix_scales, R.w, k=K, pool=P, idx_in=pool,
+                          want_scores=True)
+    n_exact = 0
+    for b in range(B):
+        id_to_col = {int(e): j for j, e in enumerate(pool[b, 0]) if e >= 0}
+        n_exact += assert_selection_matches(o["scores"][b, 0], o["idx"][b, 0], g_idx[b, 0],
+                                            id_to_col=id_to_col, what=f"reindex b{b}")
+    _log(f"{n_exact}/{B} selections identical")
+    o_out, o_lse, _ = oracle.sparse_attend(c, g_idx, R.q, R.win, sm_scale=TAU)
+    assert_attention_close(call.out.cpu().numpy(), call.lse.cpu().numpy(), o_out, o_lse, "reindex attend")
 
 
 def test_topk_candidate_map():
@@ -266,6 +314,49 @@ def test_sparse_attend_edge_cases():
     g_out, g_lse = csa2.sparse_attend(dev_cache(c), t(idx), t(L.q), None)
     o_out, o_lse, _ = oracle.sparse_attend(c, idx, L.q, None, sm_scale=TAU)
     assert_attention_close(g_out.cpu().numpy(), g_lse.cpu().numpy(), o_out, o_lse, "no window")
+
+
+def test_sparse_attend_poisoned_unused_bytes():
+    """Bytes that no position of the attention set may use are NaN patterns
+    (0xFF: an E4M3 NaN as a scale or window byte): a physical page no request
+    maps (page 0, which a position without an entry addresses), the slots past
+    each request's entry count, the window rows past each request's length and
+    their row scales. Positions without a row (-1 pads, ids past the entry
+    count, ids past the page table, positions k..k16-1) must still give the
+    oracle's output."""
+    _log("sparse_attend, poisoned unused bytes")
+    wl = make_small_decode([4 * 700, 4 * 33, 4 * 5, 4 * 1500 + 3], layers="F", k=300, page_size=16,
+                           shuffle=True, row_scale=True)
+    c0, L = wl.caches[0], wl.layers[0]
+    r = oracle.layer_step("F", c0, L.win, L.q, L.qix_codes, L.qix_scales, L.w, k=wl.k)
+    # one extra physical page in front, mapped by no request
+    bt = np.where(c0.block_table >= 0, c0.block_table + 1, -1).astype(np.int32)
+    pad = lambda a: np.concatenate([np.full((1,) + a.shape[1:], 0xFF, np.uint8), a])  # noqa: E731
+    c = type(c0)(kv_codes=pad(c0.kv_codes), kv_scales=pad(c0.kv_scales), ix_codes=pad(c0.ix_codes),
+                 ix_scales=pad(c0.ix_scales), block_table=bt, n_entries=c0.n_entries, page_size=c0.page_size)
+    ps = c.page_size
+    for b, n in enumerate(c.n_entries):
+        for s_ in range(int(n), (int(n) + ps - 1) // ps * ps):  # tail slots of the last page
+            p = bt[b, s_ // ps]
+            c.kv_codes[p, s_ % ps] = 0xFF
+            c.kv_scales[p, s_ % ps] = 0xFF
+    win = L.win
+    for b, n in enumerate(win.length):
+        win.codes[b, int(n):] = 0xFF
+        win.row_scale[b, int(n):] = np.nan
+    idx = r["idx"].copy()
+    for b, n in enumerate(c.n_entries):  # pads of the short requests -> ids with no row
+        row = idx[b, 0]
+        free = np.nonzero(row < 0)[0]
+        bad = [int(n), int(n) + 1, 10 ** 7, -9]
+        for j, v in zip(free, bad):
+            row[j] = v
+    g_out, g_lse = csa2.sparse_attend(dev_cache(c), t(idx), t(L.q), dev_window(win))
+    torch.cuda.synchronize()
+    g_out, g_lse = g_out.cpu().numpy(), g_lse.cpu().numpy()
+    assert np.isfinite(g_out).all(), "a masked position leaked a NaN"
+    o_out, o_lse, _ = oracle.sparse_attend(c, idx, L.q, win, sm_scale=TAU)
+    assert_attention_close(g_out, g_lse, o_out, o_lse, "poisoned")
 
 
 # How the attention work is cut: each row's set (k entries, then the window from
