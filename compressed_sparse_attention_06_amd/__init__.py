@@ -68,7 +68,8 @@ def lib():
         L.csa2_last_error.restype = C.c_char_p
         L.csa2_status_string.restype = C.c_char_p
         L.csa2_version.restype = C.c_char_p
-        for name in ("csa2_index_score", "csa2_topk", "csa2_sparse_attend", "csa2_layer_step",
+        for name in ("csa2_index_score", "csa2_topk", "csa2_sparse_attend", "csa2_sparse_attend_noalloc",
+                     "csa2_layer_step",
                      "csa2_index_topk", "csa2_dequant_fp4", "csa2_dequant_e4m3", "csa2_quantize_fp4", "csa2_kv_append",
                      "csa2_window_append"):
             getattr(L, name).restype = C.c_int
@@ -76,7 +77,7 @@ def lib():
     return _lib
 
 
-EXPORTS = ["csa2_index_score", "csa2_topk", "csa2_sparse_attend", "csa2_layer_step",
+EXPORTS = ["csa2_index_score", "csa2_topk", "csa2_sparse_attend", "csa2_sparse_attend_noalloc", "csa2_layer_step",
            "csa2_index_topk", "csa2_workspace_bytes", "csa2_dequant_fp4", "csa2_dequant_e4m3",
            "csa2_quantize_fp4", "csa2_kv_append", "csa2_window_append",
            "csa2_status_string", "csa2_last_error", "csa2_version"]
@@ -285,6 +286,28 @@ def sparse_attend(cache: Cache, idx, q, win: Optional[Window], q_pos=None, sm_sc
                                     None if wsct is None else C.byref(wsct), _ptr(q_pos),
                                     C.c_float(sm_scale), C.c_int32(B), C.c_int32(nq), _ptr(out),
                                     _ptr(lse), _ptr(ws), C.c_size_t(ws.numel()), _stream()))
+    return out, lse
+
+
+def sparse_attend_noalloc(cache: Cache, idx, q, win: Optional[Window], out, lse, q_pos=None, sm_scale=None):
+    """csa2_sparse_attend_noalloc: the attention with the library's own scratch.
+    Allocates nothing: the caller passes out [B, nq, 16, 512] and lse [B, nq, 16]."""
+    B, nq, k = idx.shape
+    _dev(idx, torch.int32, "idx")
+    _dev(q, torch.float32, "q", (B, nq, HEADS, LATENT))
+    _dev(q_pos, torch.int32, "q_pos", (B, nq))
+    if out is None or lse is None:
+        raise CSA2Error(1, "out and lse must be given (this entry point allocates nothing)")
+    _dev(out, torch.float32, "out", (B, nq, HEADS, LATENT))
+    _dev(lse, torch.float32, "lse", (B, nq, HEADS))
+    if sm_scale is None:
+        sm_scale = LATENT ** -0.5
+    cs = cache.struct()
+    wsct = None if win is None else win.struct()
+    _check(lib().csa2_sparse_attend_noalloc(C.byref(cs), _ptr(idx), C.c_int32(k), _ptr(q),
+                                            None if wsct is None else C.byref(wsct), _ptr(q_pos),
+                                            C.c_float(sm_scale), C.c_int32(B), C.c_int32(nq), _ptr(out),
+                                            _ptr(lse), _stream()))
     return out, lse
 
 

@@ -7,9 +7,18 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "csa2_dev.h"
 #include "kernels.h"
+
+// Library-owned scratch of csa2_sparse_attend_noalloc: the attention's split
+// partials for callers that cannot allocate. Host code never uses this name
+// as an address (on the host it is only a stand-in for the symbol): the
+// device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[CSA2_NOALLOC_SCRATCH_BYTES];
+static_assert(CSA2_NOALLOC_SCRATCH_BYTES == csa2::kSegMaxWg * 2 * CSA2_H * csa2::kPartStride * 4,
+              "the scratch holds two partials for each of the attention's workgroups");
 
 namespace {
 
@@ -411,10 +420,13 @@ csa2_status csa2_topk(const float *scores, const int32_t *cand, int32_t batch, i
   return hip_check(csa2::launch_sort_rows(idx_out, k, k, batch * nq, (hipStream_t)stream), "sort");
 }
 
-csa2_status csa2_sparse_attend(const csa2_cache *cache, const int32_t *idx, int32_t k, const float *q,
-                               const csa2_window *win, const int32_t *q_pos, float sm_scale,
-                               int32_t batch, int32_t nq, float *out, float *lse, void *ws,
-                               size_t ws_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+csa2_status check_attend(const csa2_cache *cache, const int32_t *idx, int32_t k, const float *q,
+                         const csa2_window *win, float sm_scale, int32_t batch, int32_t nq, const float *out,
+                         const float *lse) {
   csa2_status s = check_cache(cache, true, false);
   if (s) return s;
   if ((s = check_window(win))) return s;
@@ -422,8 +434,60 @@ csa2_status csa2_sparse_attend(const csa2_cache *cache, const int32_t *idx, int3
   if (batch <= 0 || nq <= 0) return fail(CSA2_EINVAL, "batch (%d) and nq (%d) must be positive", batch, nq);
   if (k <= 0 || k > CSA2_MAX_K) return fail(CSA2_EINVAL, "k = %d outside [1, %d]", k, CSA2_MAX_K);
   if (!isfinite(sm_scale)) return fail(CSA2_EINVAL, "sm_scale is not finite");
+  return CSA2_OK;
+}
+
+// Device address of `scratch` on the current device, looked up on the first
+// call made with that device current and kept per device (each GPU holds its
+// own copy of the array at its own address).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_dev[kMaxDevices] = {};
+
+csa2_status scratch_address(void **out) {
+  int dev = -1;
+  csa2_status s = hip_check(hipGetDevice(&dev), "hipGetDevice");
+  if (s) return s;
+  if (dev < 0 || dev >= kMaxDevices) return fail(CSA2_EUNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void *p = nullptr;
+    if ((s = hip_check(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)"))) return s;
+    if (!p) return fail(CSA2_EHIP, "hipGetSymbolAddress(scratch) gave NULL");
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return CSA2_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+csa2_status csa2_sparse_attend(const csa2_cache *cache, const int32_t *idx, int32_t k, const float *q,
+                               const csa2_window *win, const int32_t *q_pos, float sm_scale,
+                               int32_t batch, int32_t nq, float *out, float *lse, void *ws,
+                               size_t ws_bytes, void *stream) {
+  csa2_status s = check_attend(cache, idx, k, q, win, sm_scale, batch, nq, out, lse);
+  if (s) return s;
   const WsLayout L = ws_layout(CSA2_REUSE, (int64_t)batch * nq, 0, k, win_cap_of(win, q_pos), 1);
   if ((s = check_ws(ws, ws_bytes, L.total))) return s;
+  return run_attend(L, (char *)ws, cache, idx, k, q, win, q_pos, sm_scale, batch * nq, nq, out, lse,
+                    (hipStream_t)stream);
+}
+
+csa2_status csa2_sparse_attend_noalloc(const csa2_cache *cache, const int32_t *idx, int32_t k,
+                                       const float *q, const csa2_window *win, const int32_t *q_pos,
+                                       float sm_scale, int32_t batch, int32_t nq, float *out,
+                                       float *lse, void *stream) {
+  csa2_status s = check_attend(cache, idx, k, q, win, sm_scale, batch, nq, out, lse);
+  if (s) return s;
+  const WsLayout L = ws_layout(CSA2_REUSE, (int64_t)batch * nq, 0, k, win_cap_of(win, q_pos), 1);
+  if (L.total > (size_t)CSA2_NOALLOC_SCRATCH_BYTES)
+    return fail(CSA2_EUNSUPPORTED, "the attention split needs %zu bytes of scratch, the library holds %d",
+                L.total, CSA2_NOALLOC_SCRATCH_BYTES);
+  void *ws = nullptr;
+  if (L.total > 0 && (s = scratch_address(&ws))) return s;
   return run_attend(L, (char *)ws, cache, idx, k, q, win, q_pos, sm_scale, batch * nq, nq, out, lse,
                     (hipStream_t)stream);
 }

@@ -143,6 +143,27 @@ csa2_status csa2_sparse_attend(const csa2_cache *cache, const int32_t *idx, int3
                                float sm_scale, int32_t batch, int32_t nq, float *out,
                                float *lse, void *ws, size_t ws_bytes, void *stream);
 
+/* csa2_sparse_attend for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. The same computation and kernels as csa2_sparse_attend, but the
+ * split partials (the only scratch the attention uses) live in a
+ * library-owned device array of CSA2_NOALLOC_SCRATCH_BYTES (one copy per GPU
+ * the library runs on, held until the process ends) instead of a caller
+ * workspace; the caller still passes every input and output. The array's
+ * device address is looked up once per device, on the first call made with
+ * that device current. Nothing is allocated or freed, and nothing in the
+ * array needs to start at any value. Every call on one GPU shares that GPU's
+ * array: calls that overlap in time on the same GPU (other streams, other
+ * threads) race and must be serialised by the caller. A call whose attention
+ * split would need more scratch than the array holds returns
+ * CSA2_EUNSUPPORTED (the split uses at most 256 workgroups, so no valid
+ * call does). */
+#define CSA2_NOALLOC_SCRATCH_BYTES (256 * 2 * 16 * 516 * 4) /* 16,908,288 */
+csa2_status csa2_sparse_attend_noalloc(const csa2_cache *cache, const int32_t *idx, int32_t k,
+                                       const float *q, const csa2_window *win, const int32_t *q_pos,
+                                       float sm_scale, int32_t batch, int32_t nq, float *out,
+                                       float *lse, void *stream);
+
 /* One CSA2 layer ([P1], [P2] "CSA2").
  *  FULL:    score every visible entry with this layer's indexer query; select
  *           the top `pool` entries into pool_out [batch][nq][pool] (when
