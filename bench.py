@@ -6,17 +6,23 @@ tokens of context per request (262,144 compressed entries), layers
 128-token FP8 window per layer. Inputs are seeded and synthetic and resident
 in HBM before timing; the step's inputs are rotated over several device
 copies so the 256 MB Infinity Cache cannot hold one step's data for the next.
-The 128K-context workload (batch 32, [Full, Reuse x5]) is timed beside it.
---workload selects another workload for the JSON line: the 128K one, the
-ragged 64-request 20-layer stack, or the 4096-query prefill chunk.
+Steps are timed eager and replayed from HIP graphs that each hold one step per
+input copy; the better of the two is the value.
 
-Printed: one JSON line (metric, value = queries/s, CPU-oracle baseline with
-the host's CPU model and a one-thread timing of the tiny workload, a measured
-stream-copy peak (1 GiB device copy) beside the 8 TB/s datasheet figure, and
-rooflines measured live with HIP events around back-to-back calls replayed
-from one HIP graph on the stream they run on: `roofline` for the kernel that takes
-the most step time, the attention call (k_attend_seg and its merge), and
-`roofline_scoring` for the indexer scoring kernel (HBM-bound in decode;
+Beside it, under "workloads", the other benchmark workloads are measured the
+same way with two input copies and ten steps: the 128K-context batch-32
+[Full, Reuse x5] step, the 4096-query prefill chunk, the ragged 64-request
+20-layer stack and the speculative step (8 x 6 query rows at 1M). --workload
+makes another workload the JSON line's own.
+
+Printed: one JSON line (metric, value = queries/s (tokens/s for the prefill
+chunk), CPU-oracle baseline with the host's CPU model and a one-thread timing
+of the tiny workload, two measured ceilings beside the 8 TB/s datasheet
+figure -- a 1 GiB device copy (read + write) and a 2 GiB read-only stream --,
+and rooflines measured live with HIP events around back-to-back calls replayed
+from one HIP graph on the stream they run on: `roofline` for the kernel that
+takes the most step time, the attention call (k_attend_seg and its merge),
+and `roofline_scoring` for the indexer scoring kernel (HBM-bound in decode;
 in the prefill chunk the kernel that scores and selects without a score
 matrix, against the fp16 matrix-core peak)).
 """
@@ -68,7 +74,12 @@ def parse():
     p.add_argument("--no-topk-compare", action="store_true",
                    help="skip the standalone top-K comparison against torch.topk")
     p.add_argument("--no-secondary", action="store_true",
-                   help="skip the 128K-context (batch 32) workload reported beside the main one")
+                   help="skip the other workloads reported beside the main one")
+    p.add_argument("--attend-variants", action="store_true",
+                   help="after the main workload, 5 attention calls each with (a) its first layer's "
+                        "selection, (b) a selection of 512 runs of 4 consecutive entries per row (four "
+                        "entries share each 128-byte line of scale bytes), (c) (a) without the window: "
+                        "the inputs of the per-array traffic breakdown taken with counters")
     return p.parse_args()
 
 
@@ -245,7 +256,13 @@ def upload_chains(wl, n_copies, dev):
 
 
 def time_steps(chains, steps, warmup, use_graph):
-    """Seconds for `steps` steps, eager and (optionally) replayed from HIP graphs."""
+    """Seconds for `steps` steps, eager and (optionally) replayed from HIP graphs.
+
+    The timed graph holds all `steps` steps (rotating over the input copies) and
+    is replayed once, after one replay of a graph of the warm-up steps: every
+    graph launch costs a fixed few microseconds on the GPU (measured at 1M with
+    two copies: one step per graph 162.6 us/step, five per graph 153.5, eager
+    156.3), which a graph per step would charge to every step."""
     import torch
 
     def run_step(i):
@@ -263,7 +280,6 @@ def time_steps(chains, steps, warmup, use_graph):
     graph_s = None
     if use_graph:
         try:
-            graphs = []
             s = torch.cuda.Stream()
             s.wait_stream(torch.cuda.current_stream())
             with torch.cuda.stream(s):
@@ -271,24 +287,249 @@ def time_steps(chains, steps, warmup, use_graph):
                     run_step(ci)
             torch.cuda.current_stream().wait_stream(s)
             torch.cuda.synchronize()
-            for ci in range(len(chains)):
+
+            def capture(n):
                 g = torch.cuda.CUDAGraph()
                 with torch.cuda.graph(g):
-                    run_step(ci)
-                graphs.append(g)
+                    for i in range(n):
+                        run_step(i)
+                return g
+
+            g_warm = capture(max(1, warmup))
+            g_main = capture(steps)
             torch.cuda.synchronize()
-            for i in range(warmup):
-                graphs[i % len(graphs)].replay()
+            g_warm.replay()
             torch.cuda.synchronize()
             w0 = time.perf_counter()
-            for i in range(steps):
-                graphs[i % len(graphs)].replay()
+            g_main.replay()
             torch.cuda.synchronize()
             graph_s = time.perf_counter() - w0
+            del g_warm, g_main
         except Exception as e:  # capture unsupported: report eager only
             log(f"graph capture failed: {e!r}")
             graph_s = None
     return eager_s, graph_s
+
+
+def traffic_of(path, src, name):
+    """Calibrated counter bytes per launch from a profiles/ record, while the
+    kernel source it was taken from is unchanged and the workload matches."""
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+        src_hash = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        if rec.get("kernel_source_sha256") == src_hash and rec.get("workload") == name:
+            return rec.get("bytes_per_launch")
+    except Exception:
+        return None
+    return None
+
+
+def measure_workload(wl, name, n_copies, steps, warmup, kernel_iters, use_graph, dev):
+    """One workload's step time (eager and graph-replayed), its indexer-scoring
+    kernel and its first layer's attention call, each timed live with HIP events
+    around back-to-back calls replayed from one HIP graph. Returns (result dict,
+    device copies, chains) so that the caller can reuse the uploaded inputs."""
+    import torch
+
+    import compressed_sparse_attention_06_amd as csa2
+
+    prefill = wl.q_pos is not None and wl.nq >= 64
+    copies, chains = upload_chains(wl, n_copies, dev)
+    log(f"{name}: inputs on device, {n_copies} copies, {torch.cuda.memory_allocated() / 2**30:.2f} GiB allocated")
+    B, nq, k = wl.batch, wl.nq, wl.k
+    eager_s, graph_s = time_steps(chains, steps, warmup, use_graph)
+    log(f"{name}: eager {eager_s / steps * 1e3:.4f} ms/step" +
+        ("" if graph_s is None else f"; graph {graph_s / steps * 1e3:.4f} ms/step"))
+    best_s = min(x for x in (eager_s, graph_s) if x is not None)
+    sbytes = step_bytes(wl)
+
+    qp = None if wl.q_pos is None else torch.from_numpy(wl.q_pos).to(dev)
+    if prefill:
+        topk_calls = [csa2.IndexTopkCall(caches[0], layers[0]["qix_codes"], layers[0]["qix_scales"],
+                                         layers[0]["w"], k, q_pos=qp) for caches, layers in copies]
+
+        def score_once(i):
+            topk_calls[i % len(topk_calls)]()
+    else:
+        scores = torch.empty(B, nq, copies[0][0][0].capacity, dtype=torch.float32, device=dev)
+        hist = torch.zeros(B, nq, 4096, dtype=torch.int32, device=dev)
+
+        def score_once(i):
+            caches, layers = copies[i % len(copies)]
+            csa2.index_score(caches[0], layers[0]["qix_codes"], layers[0]["qix_scales"], layers[0]["w"],
+                             q_pos=qp, out=scores, hist=hist)
+
+    k_ms = time_calls(score_once, kernel_iters) * 1e-3
+    if prefill:
+        kflops = prefill_score_flops(wl)
+        k_tflops = kflops / (k_ms * 1e-3) / 1e12
+        log(f"{name}: prefill scoring + top-k kernel {k_ms * 1e3:.2f} us/launch, {k_tflops:.1f} TFLOP/s")
+        rs = {"kernel": "k_prefill_topk (prefill-chunk indexer scoring fused with the per-query top-K: "
+                        "two fp16-MFMA scoring passes and the selection; achieved = one pass's useful "
+                        "flops per launch time)", "bound": "mfma",
+              "achieved": round(k_tflops, 1), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+              "frac": round(k_tflops / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
+              "flops_per_launch": kflops, "us_per_launch": round(k_ms * 1e3, 3)}
+    else:
+        kb = score_kernel_bytes(wl)
+        k_gbps = kb / (k_ms * 1e-3) / 1e9
+        log(f"{name}: index_score kernel {k_ms * 1e3:.2f} us/launch, {k_gbps:.0f} GB/s algorithmic")
+        rs = {"kernel": ("k_index_score_mq (several query rows per request share each key read) + k_hist"
+                         if nq > 1 else "k_index_score (Full-layer lightning-indexer scoring)"),
+              "bound": "hbm", "achieved": round(k_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+              "frac": round(k_gbps / HBM_PEAK_GBPS, 4),
+              "traffic": traffic_of(TRAFFIC_FILE, SCORE_SRC, name),
+              "bytes_per_launch": kb, "us_per_launch": round(k_ms * 1e3, 3)}
+
+    # the dominant kernel by step time: attention (k_attend_seg + its merge) of the
+    # first layer, called with that layer's selection
+    li0 = 0
+    att_args = []
+    for ci, (caches, layers) in enumerate(copies):
+        Lh, L = wl.layers[li0], layers[li0]
+        win = csa2.Window(codes=L["win_codes"], length=L["win_len"], pos0=L["win_pos0"],
+                          row_scale=L["win_rs"], window=wl.window)
+        idx = chains[ci][li0].idx_out
+        out = torch.empty_like(L["q"])
+        lse = torch.empty(L["q"].shape[:3], dtype=torch.float32, device=dev)
+        wcap = win.span(qp)
+        ws = csa2.alloc_workspace(csa2.workspace_bytes("U", B, nq, 0, k, 0, wcap), dev)
+        att_args.append((caches[Lh.cache_id], idx, L["q"], win, out, lse, ws))
+
+    def attend_once(i):
+        cache, idx, q, win, out, lse, ws = att_args[i % len(att_args)]
+        csa2.sparse_attend(cache, idx, q, win, q_pos=qp, sm_scale=wl.sm_scale, out=out, lse=lse, ws=ws)
+
+    att_ms = time_calls(attend_once, kernel_iters) * 1e-3
+    att_b = attend_bytes(wl, li0)
+    att_gbps = att_b / (att_ms * 1e-3) / 1e9
+    att_f = attend_flops(wl, li0)
+    att_tflops = att_f / (att_ms * 1e-3) / 1e12
+    log(f"{name}: attention call {att_ms * 1e3:.2f} us/launch, {att_gbps:.0f} GB/s algorithmic, "
+        f"{att_tflops:.0f} TFLOP/s useful")
+    # decode attention streams its gathered rows from HBM; the prefill chunk's
+    # 4096 queries gather from a 9.4 MB cache that stays in the on-chip caches,
+    # so there the matrix cores are the roofline
+    if prefill:
+        ra = {"kernel": "csa2_sparse_attend: k_attend_seg (first layer's selection; no merge: "
+                        "every row falls whole to one workgroup)",
+              "bound": "mfma", "achieved": round(att_tflops, 1), "peak": MFMA_F16_PEAK_TFLOPS,
+              "unit": "TFLOP/s", "frac": round(att_tflops / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
+              "flops_per_launch": att_f, "bytes_per_launch": att_b, "us_per_launch": round(att_ms * 1e3, 3)}
+    else:
+        ra = {"kernel": "csa2_sparse_attend: k_attend_seg + k_merge_seg (first layer's selection)",
+              "bound": "hbm", "achieved": round(att_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+              "frac": round(att_gbps / HBM_PEAK_GBPS, 4),
+              "traffic": traffic_of(ATT_TRAFFIC_FILE, ATT_SRC, name),
+              "bytes_per_launch": att_b, "flops_per_launch": att_f, "us_per_launch": round(att_ms * 1e3, 3)}
+
+    rows = B * nq
+    res = dict(workload=name, batch=B, queries_per_request=nq, context_tokens=int(wl.contexts.max()),
+               layers=wl.modes, input_copies=n_copies, steps=steps, warmup=warmup,
+               value=round(rows * steps / best_s, 1),
+               unit="tokens/s" if prefill else "queries/s",
+               ms_per_step=round(best_s / steps * 1e3, 4),
+               step_gbps=round(sbytes / (best_s / steps) / 1e9, 1),
+               step_pct_of_peak=round(100 * sbytes / (best_s / steps) / 1e9 / HBM_PEAK_GBPS, 2),
+               step_algorithmic_bytes=sbytes,
+               eager_ms_per_step=round(eager_s / steps * 1e3, 4),
+               graph_ms_per_step=None if graph_s is None else round(graph_s / steps * 1e3, 4),
+               timing="graph" if (graph_s is not None and graph_s <= eager_s) else "eager",
+               roofline=ra, roofline_scoring=rs)
+    return res, copies, chains
+
+
+_EV = None
+
+
+def time_calls(fn, iters):
+    """us per call: `iters` calls captured in one HIP graph and replayed between two
+    HIP events on the stream the graph runs on (torch's current stream), so that
+    the binding's per-call host work is not what is timed."""
+    import torch
+
+    global _EV
+    if _EV is None:
+        _EV = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    ev0, ev1 = _EV
+    for i in range(3):
+        fn(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s_cap = torch.cuda.Stream()
+    s_cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s_cap):
+        with torch.cuda.graph(g, stream=s_cap):
+            for i in range(iters):
+                fn(i)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    ev0.record()
+    g.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / iters * 1e3
+
+
+def stream_probes(dev):
+    """Practical HBM ceilings measured in the same run: a plain 1 GiB device copy
+    (read + write) and a 2 GiB read-only stream (csa2_stream_read, several grid
+    sizes, the best kept), both event-timed; neither fits the 256 MB Infinity Cache."""
+    import torch
+
+    import compressed_sparse_attention_06_amd as csa2
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    nb = 1 << 30
+    xs = torch.empty(nb, dtype=torch.uint8, device=dev)
+    ys = torch.empty_like(xs)
+    for _ in range(2):
+        ys.copy_(xs)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(10):
+        ys.copy_(xs)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbps = 2 * nb * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del xs, ys
+    nr = 2 << 30
+    xr = torch.ones(nr // 4, dtype=torch.int32, device=dev)
+    sink = torch.zeros(1024, dtype=torch.int32, device=dev)
+    read = {}
+    for blocks in (2048, 8192, 16384, 32768):
+        for _ in range(2):
+            csa2.stream_read(xr, sink, blocks)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(10):
+            csa2.stream_read(xr, sink, blocks)
+        e1.record()
+        torch.cuda.synchronize()
+        read[blocks] = nr * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del xr, sink
+    best = max(read, key=read.get)
+    log(f"stream copy: {copy_gbps:.0f} GB/s (read + write, 1 GiB); stream read: "
+        + ", ".join(f"{b} WGs {g:.0f}" for b, g in read.items()) + " GB/s (2 GiB)")
+    return copy_gbps, read[best], best
+
+
+def add_ceilings(res, copy_gbps, read_gbps):
+    """The step's and each HBM roofline's rate against the measured ceilings."""
+    g = res["step_gbps"]
+    res["step_pct_of_stream_copy"] = round(100 * g / copy_gbps, 2)
+    res["step_pct_of_stream_read"] = round(100 * g / read_gbps, 2)
+    for key in ("roofline", "roofline_scoring"):
+        r = res.get(key)
+        if r and r["unit"] == "GB/s":
+            r["frac_of_stream_copy"] = round(r["achieved"] / copy_gbps, 4)
+            r["frac_of_stream_read"] = round(r["achieved"] / read_gbps, 4)
+
+
+EXTRA_WORKLOADS = [WORKLOAD_128K, "prefill_4096q_128k", "ragged64_paged_20layer", "b8_1m_spec6"]
 
 
 def main():
@@ -312,113 +553,11 @@ def main():
     wl = make_prefill_workload() if prefill else make_decode_workload(name)
     log(f"workload {name} generated in {time.time() - t0:.1f}s; modes {wl.modes}, "
         f"batch {wl.batch}, queries/request {wl.nq}, N/request {int(wl.caches[0].n_entries[0])}")
-    copies, chains = upload_chains(wl, args.copies, dev)
-    log(f"inputs on device: {args.copies} copies, "
-        f"{torch.cuda.memory_allocated() / 2**30:.2f} GiB allocated")
+    main_res, copies, chains = measure_workload(wl, name, args.copies, args.steps, args.warmup,
+                                                args.kernel_iters, not args.no_graph, dev)
     B, nq, k, pool = wl.batch, wl.nq, wl.k, wl.pool
-
-    eager_s, graph_s = time_steps(chains, args.steps, args.warmup, not args.no_graph)
-    log(f"eager: {eager_s / args.steps * 1e3:.3f} ms/step" +
-        ("" if graph_s is None else f"; graph: {graph_s / args.steps * 1e3:.3f} ms/step"))
-    best_s = min(x for x in (eager_s, graph_s) if x is not None)
-    ms_per_step = best_s / args.steps * 1e3
-    qps = B * nq * args.steps / best_s
-    sbytes = step_bytes(wl)
-    gbps = sbytes / (best_s / args.steps) / 1e9
-
-    # ---- the Full layer's indexer scoring, timed live with HIP events: decode
-    # times the scoring kernel alone; the prefill chunk times what its step
-    # runs, scoring fused with the per-query top-K (no score matrix) ----
-    qp = None if wl.q_pos is None else torch.from_numpy(wl.q_pos).to(dev)
-    if prefill:
-        topk_calls = [csa2.IndexTopkCall(caches[0], layers[0]["qix_codes"], layers[0]["qix_scales"],
-                                         layers[0]["w"], k, q_pos=qp) for caches, layers in copies]
-
-        def score_once(i):
-            topk_calls[i % len(topk_calls)]()
-    else:
-        scores = torch.empty(B, nq, copies[0][0][0].capacity, dtype=torch.float32, device=dev)
-        hist = torch.zeros(B, nq, 4096, dtype=torch.int32, device=dev)
-
-        def score_once(i):
-            caches, layers = copies[i % len(copies)]
-            csa2.index_score(caches[0], layers[0]["qix_codes"], layers[0]["qix_scales"], layers[0]["w"],
-                             q_pos=qp, out=scores, hist=hist)
-
+    gen = torch.Generator(device=dev).manual_seed(11)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-
-    def time_calls(fn, iters):
-        """us per call: `iters` calls captured in one HIP graph and replayed, so that
-        the binding's host-side overhead is not what is timed."""
-        for i in range(3):
-            fn(i)
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        s_cap = torch.cuda.Stream()
-        s_cap.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s_cap):
-            with torch.cuda.graph(g, stream=s_cap):
-                for i in range(iters):
-                    fn(i)
-        torch.cuda.synchronize()
-        g.replay()
-        torch.cuda.synchronize()
-        ev0.record()
-        g.replay()
-        ev1.record()
-        torch.cuda.synchronize()
-        return ev0.elapsed_time(ev1) / iters * 1e3
-
-    # back-to-back launches captured in one HIP graph and replayed between two
-    # HIP events on the stream the graph runs on (torch's current stream), so
-    # that the binding's per-call host work is not part of the kernel's time
-    k_ms = time_calls(score_once, args.kernel_iters) * 1e-3
-    if prefill:
-        kflops = prefill_score_flops(wl)
-        k_tflops = kflops / (k_ms * 1e-3) / 1e12
-        log(f"prefill scoring + top-k kernel: {k_ms * 1e3:.2f} us/launch, {k_tflops:.1f} TFLOP/s "
-            f"(one scoring pass's useful flops)")
-    else:
-        kb = score_kernel_bytes(wl)
-        k_gbps = kb / (k_ms * 1e-3) / 1e9
-        log(f"index_score kernel: {k_ms * 1e3:.2f} us/launch, {k_gbps:.0f} GB/s algorithmic")
-
-    # ---- the dominant kernel by step time: attention (k_attend_seg + its merge) of
-    # the first layer, called with that layer's selection, timed live the same way ----
-    li0 = 0
-    att_args = []
-    for ci, (caches, layers) in enumerate(copies):
-        Lh, L = wl.layers[li0], layers[li0]
-        win = csa2.Window(codes=L["win_codes"], length=L["win_len"], pos0=L["win_pos0"],
-                          row_scale=L["win_rs"], window=wl.window)
-        idx = chains[ci][li0].idx_out
-        out = torch.empty_like(L["q"])
-        lse = torch.empty(L["q"].shape[:3], dtype=torch.float32, device=dev)
-        wcap = win.span(qp)
-        ws = csa2.alloc_workspace(csa2.workspace_bytes("U", B, nq, 0, k, 0, wcap), dev)
-        att_args.append((caches[Lh.cache_id], idx, L["q"], win, out, lse, ws))
-
-    def attend_once(i):
-        cache, idx, q, win, out, lse, ws = att_args[i % len(att_args)]
-        csa2.sparse_attend(cache, idx, q, win, q_pos=qp, sm_scale=wl.sm_scale, out=out, lse=lse, ws=ws)
-
-    att_ms = time_calls(attend_once, args.kernel_iters) * 1e-3
-    att_b = attend_bytes(wl, li0)
-    att_gbps = att_b / (att_ms * 1e-3) / 1e9
-    att_f = attend_flops(wl, li0)
-    att_tflops = att_f / (att_ms * 1e-3) / 1e12
-    log(f"attention call: {att_ms * 1e3:.2f} us/launch, {att_gbps:.0f} GB/s algorithmic, "
-        f"{att_tflops:.0f} TFLOP/s useful")
-
-    att_traffic = None
-    if os.path.exists(ATT_TRAFFIC_FILE):
-        try:
-            rec = json.load(open(ATT_TRAFFIC_FILE))
-            src_hash = hashlib.sha256(open(ATT_SRC, "rb").read()).hexdigest()
-            if rec.get("kernel_source_sha256") == src_hash and rec.get("workload") == name:
-                att_traffic = rec.get("bytes_per_launch")
-        except Exception:
-            att_traffic = None
 
     # ---- the cache's write side: what one decode step appends, and a prefill chunk's worth ----
     gen = torch.Generator(device=dev).manual_seed(11)
@@ -484,16 +623,6 @@ def main():
             del sc, out_i, wsk, tv, ti
         log(f"topk vs torch.topk: {topk_cmp}")
 
-    traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        try:
-            rec = json.load(open(TRAFFIC_FILE))
-            src_hash = hashlib.sha256(open(SCORE_SRC, "rb").read()).hexdigest()
-            if rec.get("kernel_source_sha256") == src_hash and rec.get("workload") == name:
-                traffic = rec.get("bytes_per_launch")
-        except Exception:
-            traffic = None
-
     if args.copy_probe_mb:
         n = args.copy_probe_mb * 2**20
         x = torch.empty(n, dtype=torch.uint8, device=dev)
@@ -509,44 +638,52 @@ def main():
         torch.cuda.synchronize()
         log(f"copy probe: 5 x {args.copy_probe_mb} MiB device copies (blit) + 5 (elementwise)")
 
-    # ---- the 128K-context workload (batch 32, [Full, Reuse x5]) beside it ----
-    secondary = None
-    if not args.no_secondary and name == WORKLOAD:
+    # ---- attention input variants for the counter breakdown of its traffic ----
+    if args.attend_variants and wl.q_pos is None:
+        caches, layers = copies[0]
+        L = layers[0]
+        win = csa2.Window(codes=L["win_codes"], length=L["win_len"], pos0=None, row_scale=L["win_rs"],
+                          window=wl.window)
+        idx = chains[0][0].idx_out
+        n_ent = int(wl.caches[0].n_entries.min())
+        rng = np.random.default_rng(0)
+        runs = np.stack([np.sort(4 * rng.choice(n_ent // 4, k // 4, replace=False)[:, None] + np.arange(4)[None, :],
+                                 axis=None) for _ in range(B * nq)])
+        idx_cl = torch.from_numpy(runs.reshape(B, nq, k).astype(np.int32)).to(dev)
+        out = torch.empty_like(L["q"])
+        lse = torch.empty(L["q"].shape[:3], dtype=torch.float32, device=dev)
+        wsv = csa2.alloc_workspace(csa2.workspace_bytes("U", B, nq, 0, k, 0, win.span(None)), dev)
+        for vi, (vidx, vwin) in enumerate(((idx, win), (idx_cl, win), (idx, None))):
+            for _ in range(5):
+                csa2.sparse_attend(caches[0], vidx, L["q"], vwin, sm_scale=wl.sm_scale, out=out, lse=lse, ws=wsv)
+        torch.cuda.synchronize()
+        log("attention variants: 5 calls each of (a) the selection, (b) runs of 4 consecutive entries, "
+            "(c) the selection without the window (the last 15 k_attend_seg dispatches)")
+
+    # ---- the other workloads beside the main one (two input copies each, fewer steps) ----
+    extras = {}
+    if not args.no_secondary:
         del chains, copies
         torch.cuda.empty_cache()
-        wl2 = make_decode_workload(WORKLOAD_128K)
-        copies2, chains2 = upload_chains(wl2, args.copies, dev)
-        e2, g2 = time_steps(chains2, args.steps, args.warmup, not args.no_graph)
-        b2 = min(x for x in (e2, g2) if x is not None)
-        sb2 = step_bytes(wl2)
-        secondary = dict(workload=WORKLOAD_128K, batch=wl2.batch, context_tokens=int(wl2.contexts[0]),
-                         layers=wl2.modes, value=round(wl2.batch * wl2.nq * args.steps / b2, 1),
-                         unit="queries/s", ms_per_step=round(b2 / args.steps * 1e3, 4),
-                         step_gbps=round(sb2 / (b2 / args.steps) / 1e9, 1),
-                         step_pct_of_peak=round(100 * sb2 / (b2 / args.steps) / 1e9 / HBM_PEAK_GBPS, 2),
-                         step_algorithmic_bytes=sb2,
-                         eager_ms_per_step=round(e2 / args.steps * 1e3, 4),
-                         graph_ms_per_step=None if g2 is None else round(g2 / args.steps * 1e3, 4))
-        log(f"128K workload: {secondary['ms_per_step']} ms/step, {secondary['value']} queries/s")
-        del chains2, copies2
+        for xname in EXTRA_WORKLOADS:
+            if xname == name:
+                continue
+            t0 = time.time()
+            xwl = make_prefill_workload() if xname == "prefill_4096q_128k" else make_decode_workload(xname)
+            log(f"workload {xname} generated in {time.time() - t0:.1f}s")
+            xs_steps = min(args.steps, 10)
+            xres, xc, xch = measure_workload(xwl, xname, min(args.copies, 2), xs_steps, min(args.warmup, 3),
+                                             min(args.kernel_iters, 10), not args.no_graph, dev)
+            extras[xname] = xres
+            log(f"{xname}: {xres['ms_per_step']} ms/step, {xres['value']} {xres['unit']}")
+            del xc, xch, xwl
+            torch.cuda.empty_cache()
 
-    # ---- measured stream-copy peak: a plain 1 GiB device copy (read + write),
-    # event-timed, the practical ceiling beside the 8 TB/s datasheet figure ----
-    nb = 1 << 30
-    xs = torch.empty(nb, dtype=torch.uint8, device=dev)
-    ys = torch.empty_like(xs)
-    for _ in range(2):
-        ys.copy_(xs)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(10):
-        ys.copy_(xs)
-    e1.record()
-    torch.cuda.synchronize()
-    stream_gbps = 2 * nb * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
-    del xs, ys
-    log(f"stream copy: {stream_gbps:.0f} GB/s (read + write, 1 GiB)")
+    # ---- measured ceilings: stream copy (read + write) and read-only stream ----
+    copy_gbps, read_gbps, read_blocks = stream_probes(dev)
+    add_ceilings(main_res, copy_gbps, read_gbps)
+    for xres in extras.values():
+        add_ceilings(xres, copy_gbps, read_gbps)
 
     # ---- CPU oracle baseline (bounded sample, host cores) ----
     cpu = None
@@ -588,12 +725,12 @@ def main():
 
     line = {
         "metric": "CSA2 decode queries/s + achieved HBM GB/s (% of peak) at 128K and 1M ctx",
-        "value": round(qps, 1),
-        "unit": "queries/s",
+        "value": main_res["value"],
+        "unit": main_res["unit"],
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": main_res["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -603,45 +740,24 @@ def main():
                    "context_tokens": int(wl.contexts[0]),
                    "entries_per_request": int(wl.caches[0].n_entries[0]), "layers": wl.modes,
                    "top_k": k, "pool": pool, "window": 128, "input_copies": args.copies,
-                   "timing": "graph" if (graph_s is not None and graph_s <= eager_s) else "eager"},
-        "step_gbps": round(gbps, 1),
-        "step_pct_of_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
-        "stream_copy_gbps": round(stream_gbps, 1),
-        "step_pct_of_stream_copy": round(100 * gbps / stream_gbps, 2),
-        "step_algorithmic_bytes": sbytes,
-        "eager_ms_per_step": round(eager_s / args.steps * 1e3, 4),
-        "graph_ms_per_step": None if graph_s is None else round(graph_s / args.steps * 1e3, 4),
-        # decode attention streams its gathered rows from HBM; the prefill
-        # chunk's 4096 queries gather from a 9.4 MB cache that stays in the
-        # on-chip caches, so there the matrix cores are the roofline
-        "roofline": ({"kernel": "csa2_sparse_attend: k_attend_seg (first layer's selection; no merge: "
-                                "every row falls whole to one workgroup)",
-                      "bound": "mfma", "achieved": round(att_tflops, 1), "peak": MFMA_F16_PEAK_TFLOPS,
-                      "unit": "TFLOP/s", "frac": round(att_tflops / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
-                      "flops_per_launch": att_f, "bytes_per_launch": att_b,
-                      "us_per_launch": round(att_ms * 1e3, 3)} if prefill else
-                     {"kernel": "csa2_sparse_attend: k_attend_seg + k_merge_seg (first layer's selection)",
-                      "bound": "hbm", "achieved": round(att_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                      "frac": round(att_gbps / HBM_PEAK_GBPS, 4), "traffic": att_traffic,
-                      "frac_of_stream_copy": round(att_gbps / stream_gbps, 4),
-                      "bytes_per_launch": att_b, "flops_per_launch": att_f,
-                      "us_per_launch": round(att_ms * 1e3, 3)}),
-        "roofline_scoring": (
-            {"kernel": "k_prefill_topk (prefill-chunk indexer scoring fused with the per-query top-K: "
-                       "two fp16-MFMA scoring passes and the selection; achieved = one pass's useful "
-                       "flops per launch time)", "bound": "mfma",
-             "achieved": round(k_tflops, 1), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-             "frac": round(k_tflops / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
-             "flops_per_launch": kflops, "us_per_launch": round(k_ms * 1e3, 3)} if prefill else
-            {"kernel": "k_index_score (Full-layer lightning-indexer scoring)", "bound": "hbm",
-             "achieved": round(k_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-             "frac": round(k_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
-             "frac_of_stream_copy": round(k_gbps / stream_gbps, 4),
-             "bytes_per_launch": kb, "us_per_launch": round(k_ms * 1e3, 3)}),
+                   "timing": main_res["timing"]},
+        "step_gbps": main_res["step_gbps"],
+        "step_pct_of_peak": main_res["step_pct_of_peak"],
+        "stream_copy_gbps": round(copy_gbps, 1),
+        "stream_read_gbps": round(read_gbps, 1),
+        "stream_read_workgroups": read_blocks,
+        "step_pct_of_stream_copy": main_res["step_pct_of_stream_copy"],
+        "step_pct_of_stream_read": main_res["step_pct_of_stream_read"],
+        "step_algorithmic_bytes": main_res["step_algorithmic_bytes"],
+        "eager_ms_per_step": main_res["eager_ms_per_step"],
+        "graph_ms_per_step": main_res["graph_ms_per_step"],
+        "roofline": main_res["roofline"],
+        "roofline_scoring": main_res["roofline_scoring"],
         "append": app,
         "topk_vs_torch": topk_cmp,
         "cpu_baseline": cpu,
-        "secondary": secondary,
+        "workloads": extras,
+        "secondary": extras.get(WORKLOAD_128K),
     }
     print(json.dumps(line), flush=True)
 

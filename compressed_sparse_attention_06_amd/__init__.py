@@ -71,7 +71,7 @@ def lib():
         for name in ("csa2_index_score", "csa2_topk", "csa2_sparse_attend", "csa2_sparse_attend_noalloc",
                      "csa2_layer_step",
                      "csa2_index_topk", "csa2_dequant_fp4", "csa2_dequant_e4m3", "csa2_quantize_fp4", "csa2_kv_append",
-                     "csa2_window_append"):
+                     "csa2_window_append", "csa2_stream_read"):
             getattr(L, name).restype = C.c_int
         _lib = L
     return _lib
@@ -79,7 +79,7 @@ def lib():
 
 EXPORTS = ["csa2_index_score", "csa2_topk", "csa2_sparse_attend", "csa2_sparse_attend_noalloc", "csa2_layer_step",
            "csa2_index_topk", "csa2_workspace_bytes", "csa2_dequant_fp4", "csa2_dequant_e4m3",
-           "csa2_quantize_fp4", "csa2_kv_append", "csa2_window_append",
+           "csa2_quantize_fp4", "csa2_kv_append", "csa2_window_append", "csa2_stream_read",
            "csa2_status_string", "csa2_last_error", "csa2_version"]
 
 
@@ -287,6 +287,14 @@ def sparse_attend(cache: Cache, idx, q, win: Optional[Window], q_pos=None, sm_sc
                                     C.c_float(sm_scale), C.c_int32(B), C.c_int32(nq), _ptr(out),
                                     _ptr(lse), _ptr(ws), C.c_size_t(ws.numel()), _stream()))
     return out, lse
+
+
+def stream_read(x: torch.Tensor, sink: torch.Tensor, blocks: int = 2048):
+    """Measurement probe: read every byte of the device tensor x once (csa2_stream_read)."""
+    if not x.is_cuda or not sink.is_cuda or sink.dtype != torch.int32 or sink.numel() < 1024:
+        raise CSA2Error(1, "x and sink (>= 1024 int32) must be device tensors")
+    _check(lib().csa2_stream_read(_ptr(x), C.c_size_t(x.numel() * x.element_size()), _ptr(sink),
+                                  C.c_int32(blocks), _stream()))
 
 
 def sparse_attend_noalloc(cache: Cache, idx, q, win: Optional[Window], out, lse, q_pos=None, sm_scale=None):

@@ -9,6 +9,7 @@
 #include <algorithm>
 #include <mutex>
 
+#include "../../include/csa2_probe.h"
 #include "csa2_dev.h"
 #include "kernels.h"
 
@@ -331,6 +332,7 @@ csa2_status run_attend(const WsLayout &L, char *ws, const csa2_cache *cache, con
   sg.T = L.att_T;
   sg.U = L.att_U;
   sg.G = L.att_G;
+  sg.xcd = 1;
   sg.out = out;
   sg.lse = lse;
   return hip_check(csa2::launch_attend_seg(a, sg, L.att_slots, st), "attend");
@@ -703,6 +705,13 @@ csa2_status csa2_dequant_fp4(const uint8_t *codes, const uint8_t *scales, int64_
   if (n_rows < 0 || channels <= 0 || channels % 32) return fail(CSA2_EINVAL, "channels must be a positive multiple of 32");
   return hip_check(csa2::launch_dequant_fp4(codes, scales, n_rows, channels, out_f16, (hipStream_t)stream),
                    "dequant_fp4");
+}
+
+csa2_status csa2_stream_read(const void *p, size_t n_bytes, uint32_t *sink, int32_t blocks, void *stream) {
+  if (!p || !sink) return fail(CSA2_EINVAL, "NULL pointer");
+  if (n_bytes < 16 || n_bytes % 16 || ((uintptr_t)p & 15)) return fail(CSA2_EINVAL, "n_bytes must be a positive multiple of 16, p 16-byte aligned");
+  if (blocks < 1) return fail(CSA2_EINVAL, "blocks must be positive");
+  return hip_check(csa2::launch_stream_read(p, (int64_t)n_bytes, sink, blocks, (hipStream_t)stream), "stream_read");
 }
 
 csa2_status csa2_dequant_e4m3(const uint8_t *bytes, int64_t n, float *out, void *stream) {

@@ -102,6 +102,19 @@ __device__ __forceinline__ v4h e4m3x4_to_f16(uint32_t word) {
   return r;
 }
 
+// ---- XCD-aware workgroup order ----------------------------------------------------
+// MI355X hands the workgroups of a 1-D grid to its 8 XCDs (each with its own
+// L2) in turn: workgroup b runs on XCD b % 8. xcd_order(b, n) renumbers them
+// so that XCD x runs one contiguous block of the logical order (from
+// x * (n / 8) + min(x, n % 8), the first n % 8 XCDs taking one more): logical
+// neighbours, which read the same data (one query row's Q, one row's
+// partials), then share one L2 and fetch it from memory once. A bijection of
+// [0, n).
+__device__ __forceinline__ int xcd_order(int b, int n) {
+  const int x = b & 7, s = b >> 3, q = n >> 3, r = n & 7;
+  return x * q + min(x, r) + s;
+}
+
 // ---- paged cache addressing ----------------------------------------------------
 struct DevCache {
   const uint8_t *kv_codes, *kv_scales, *ix_codes, *ix_scales;

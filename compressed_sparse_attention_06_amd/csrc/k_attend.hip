@@ -514,7 +514,7 @@ __device__ __forceinline__ void seg_finish(const AttendArgs &a, const SegArgs &s
 
 __global__ __launch_bounds__(512) void k_attend_seg(AttendArgs a, SegArgs s) {
   __shared__ __attribute__((aligned(16))) SegShared sh;
-  const int w = blockIdx.x;
+  const int w = s.xcd ? xcd_order(blockIdx.x, gridDim.x) : blockIdx.x;
   const int32_t U = s.U;
   const int64_t u_begin = (int64_t)w * s.T / s.G, u_end = (int64_t)(w + 1) * s.T / s.G;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -601,7 +601,8 @@ __device__ __forceinline__ float wave_sum64(float v) {
 template <int BATCH>
 __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 2))) void k_merge_seg(MergeArgs a,
                                                                                               SegArgs s) {
-  const int h = blockIdx.x, r = blockIdx.y, t = threadIdx.x, lane = t & 63;
+  const int hr = s.xcd ? xcd_order(blockIdx.x, gridDim.x) : blockIdx.x;  // row-major (row, head)
+  const int h = hr & (CSA2_H - 1), r = hr >> 4, t = threadIdx.x, lane = t & 63;
   const int64_t u0 = (int64_t)r * s.U, u1 = u0 + s.U - 1;
   const int32_t first = (int32_t)(((u0 + 1) * s.G + s.T - 1) / s.T - 1);
   const int32_t last = (int32_t)(((u1 + 1) * s.G + s.T - 1) / s.T - 1);
@@ -657,7 +658,7 @@ hipError_t launch_attend_seg(const AttendArgs &a, const SegArgs &s, int max_slot
   if (e != hipSuccess || max_slots < 2) return e;
   MergeArgs m{};
   m.part = a.part;
-  const dim3 grid(CSA2_H, (unsigned)(s.T / s.U));
+  const dim3 grid((unsigned)(CSA2_H * (s.T / s.U)));
   // one batch of loads covers up to 24 partials (the 1M decode rows have 17)
   if (max_slots <= 8)
     hipLaunchKernelGGL(k_merge_seg<8>, grid, dim3(128), 0, st, m, s);

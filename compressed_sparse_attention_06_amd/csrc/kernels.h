@@ -112,6 +112,7 @@ constexpr int kSegMaxWg = 256;
 struct SegArgs {
   int64_t T;
   int32_t U, G;
+  int32_t xcd;  // 1: workgroups renumbered so that each XCD runs a contiguous block of rows
   float *out, *lse;
 };
 
@@ -171,6 +172,7 @@ hipError_t launch_attend_seg(const AttendArgs &a, const SegArgs &s, int max_slot
 hipError_t launch_dequant_fp4(const uint8_t *codes, const uint8_t *scales, int64_t n_rows,
                               int32_t channels, uint16_t *out, hipStream_t st);
 hipError_t launch_dequant_e4m3(const uint8_t *bytes, int64_t n, float *out, hipStream_t st);
+hipError_t launch_stream_read(const void *p, int64_t n_bytes, uint32_t *sink, int blocks, hipStream_t st);
 
 constexpr int kPartStride = CSA2_D + 4;  // per head: 512 unnormalised outputs, max, sum, 2 pad
 

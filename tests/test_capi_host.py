@@ -2,6 +2,7 @@
 rejects bad arguments before launching anything (no GPU needed)."""
 
 import ctypes as C
+import glob
 import os
 import re
 
@@ -10,13 +11,14 @@ import pytest
 import compressed_sparse_attention_06_amd as csa2
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "csa2.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 EINVAL, EUNSUPPORTED, EWORKSPACE = 1, 2, 3
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    """Every csa2_* function declared in include/*.h."""
+    text = "".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(csa2_[a-z0-9_]+)\s*\(", text)))
 
