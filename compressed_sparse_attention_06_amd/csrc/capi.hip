@@ -39,7 +39,6 @@ csa2_status hip_check(hipError_t e, const char *what) {
 }
 
 constexpr int kFinItems = 4096;        // rows up to this length select in LDS directly
-constexpr int64_t kRowSelectMinRows = 32;  // rows from which rows up to 16384 select one workgroup per row
 constexpr int kScoreChunk = 2048;      // scoring columns per workgroup (contiguous entries)
 constexpr int kScoreChunkCand = 512;   // ... when gathering a candidate list
 constexpr int32_t kPrefillQueries = 64;  // queries per request from which scoring is a matrix-core contraction
@@ -83,7 +82,7 @@ struct WsLayout {
          eq1 = 0, part = 0,
          total = 0;
   bool compact = false;   // chunked compaction + final selection (long rows)
-  bool row_sel = false;   // one workgroup per row, keys in registers (rows up to kSelectRowMax)
+  bool row_sel = false;   // one workgroup per row, keys in registers, histogram in LDS (rows up to kSelectRowMax)
   bool fused = false;     // prefill scoring fused with the top-K: no score region
   int max_wg = 0, chunk = 0;
   int64_t seg_stride = 0;
@@ -135,8 +134,8 @@ WsLayout ws_layout(csa2_mode mode, int64_t rows, int64_t n_cols, int32_t k, int3
     // one workgroup per row pays off once there are enough rows to fill the
     // GPU; few long rows go through the chunked path, which spreads each row
     // over many workgroups
-    L.row_sel = n_cols > kFinItems && n_cols <= csa2::kSelectRowMax && rows >= kRowSelectMinRows;
-    L.compact = n_cols > kFinItems && !L.row_sel;
+    L.row_sel = n_cols > kFinItems && n_cols <= csa2::kSelectRowMax;
+    L.compact = n_cols > csa2::kSelectRowMax;
     L.scores = off;
     off = align256(off + (size_t)rows * n_cols * 4);
     L.hist = off;  // zeroed by a fill before the scoring kernel adds to it
@@ -249,7 +248,7 @@ csa2_status run_select(const WsLayout &L, char *ws, int rows, int32_t n_cols, co
       d.out[i] = tg[i].out;
       d.out_stride[i] = tg[i].stride;
     }
-    return hip_check(L.row_sel ? csa2::launch_select_row(d, rows, ntarget, st)
+    return hip_check(L.row_sel ? csa2::launch_sel_rowwise(d, rows, ntarget, st)
                                : csa2::launch_select_direct(d, rows, ntarget, st),
                      "select");
   }

@@ -25,7 +25,8 @@
 // Output in column order is ascending id order whenever ids grow with the
 // column (no candidate map, or an ascending one).
 // Rows that fit in LDS use k_select_direct: one workgroup loads every key,
-// selects, and writes ids through a bitmap sort.
+// selects, and writes ids through a bitmap sort. Rows of up to 16384 columns
+// take k_sel_rowwise (k_select2.hip).
 #include "csa2_dev.h"
 #include "kernels.h"
 #include "block_ops.h"
@@ -50,20 +51,6 @@ hipError_t launch_fill_u32(uint32_t *p, int64_t n, uint32_t v, hipStream_t st) {
   if (blocks > 4096) blocks = 4096;
   hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)blocks), dim3(256), 0, st, p, n, v);
   return hipGetLastError();
-}
-
-__device__ __forceinline__ int32_t row_limit(const int32_t *n_entries, const int32_t *q_pos,
-                                             int nq, int r, int32_t n_cols) {
-  int32_t lim = n_cols;
-  if (n_entries) {
-    int32_t V = n_entries[r / nq];
-    if (q_pos) {
-      const int64_t vp = ((int64_t)q_pos[r] + 1) / CSA2_TOKENS_PER_ENTRY;
-      if (vp < V) V = (int32_t)(vp < 0 ? 0 : vp);
-    }
-    if (V < lim) lim = V;
-  }
-  return lim < 0 ? 0 : lim;
 }
 
 // ---- standalone histogram ------------------------------------------------------
@@ -281,125 +268,6 @@ hipError_t launch_compact(const CompactArgs &a, int rows, hipStream_t st) {
   if (a.ntarget == 1) return vec ? launch_compact_n<1, true>(a, grid, st) : launch_compact_n<1, false>(a, grid, st);
   if (a.ntarget == 2) return vec ? launch_compact_n<2, true>(a, grid, st) : launch_compact_n<2, false>(a, grid, st);
   return hipErrorInvalidValue;
-}
-
-// ---- exact selection at the boundary ------------------------------------------------
-template <int BITS>
-struct SelShared {
-  uint32_t hist[1 << BITS];
-  uint32_t scan[16];
-  int out[4];
-  uint32_t kmin, kmax, mcount, cnt;
-};
-
-// An item with key k and id d is selected iff (k & kmask) > kpref, or
-// (k & kmask) == kpref and d <= idthr.
-struct SelRule {
-  uint32_t kmask, kpref, idthr;
-};
-
-__device__ __forceinline__ bool rule_pass(const SelRule &R, uint32_t k, int32_t d) {
-  const uint32_t km = k & R.kmask;
-  return km > R.kpref || (km == R.kpref && (uint32_t)d <= R.idthr);
-}
-
-// The rule that keeps the `need` best (key desc, id asc) of the items whose
-// key is above KEY_NEG_INF (need >= 1). Keys are settled BITS bits at a time
-// after the leading bits every item shares; exact key ties are settled on the
-// id the same way.
-template <int BITS, int NT, class Acc>
-__device__ SelRule block_rule(const Acc &acc, int count, int need, SelShared<BITS> &sh) {
-  constexpr int NB = 1 << BITS;
-  const int t = threadIdx.x, nt = NT;
-  if (t == 0) {
-    sh.kmin = 0xFFFFFFFFu;
-    sh.kmax = 0u;
-    sh.mcount = 0;
-  }
-  __syncthreads();
-  {
-    uint32_t lo = 0xFFFFFFFFu, hi = 0u, c = 0;
-    for (int i = t; i < count; i += nt) {
-      uint32_t k;
-      int32_t d;
-      acc.get(i, k, d);
-      if (k > KEY_NEG_INF) {
-        lo = min(lo, k);
-        hi = max(hi, k);
-        ++c;
-      }
-    }
-    if (c) {
-      atomicMin(&sh.kmin, lo);
-      atomicMax(&sh.kmax, hi);
-      atomicAdd(&sh.mcount, c);
-    }
-  }
-  __syncthreads();
-  const uint32_t diff = sh.kmin ^ sh.kmax;
-  int known = (sh.mcount == 0) ? 32 : (diff ? __clz(diff) : 32);
-  uint32_t kmask = known ? (0xFFFFFFFFu << (32 - known)) : 0u;
-  uint32_t kpref = sh.kmin & kmask;
-  int left = need;
-  int eqcnt = (int)sh.mcount;
-  bool take_all_eq = (left >= eqcnt);
-  __syncthreads();
-  while (!take_all_eq && known < 32) {
-    const int width = (32 - known) < BITS ? (32 - known) : BITS;
-    const int shift = 32 - known - width;
-    const uint32_t dmask = (1u << width) - 1u;
-    for (int i = t; i < NB; i += nt) sh.hist[i] = 0;
-    __syncthreads();
-    for (int i = t; i < count; i += nt) {
-      uint32_t k;
-      int32_t d;
-      acc.get(i, k, d);
-      if (k > KEY_NEG_INF && (k & kmask) == kpref) atomicAdd(&sh.hist[(k >> shift) & dmask], 1u);
-    }
-    __syncthreads();
-    hist_threshold_n<NB, NT, true>(sh.hist, (uint32_t)left, sh.scan, sh.out);
-    const int dsel = sh.out[0];
-    if (dsel < 0) {  // every item with this prefix is needed
-      take_all_eq = true;
-    } else {
-      left -= sh.out[1];
-      eqcnt = (int)sh.hist[dsel];
-      kpref |= (uint32_t)dsel << shift;
-      kmask |= dmask << shift;
-      known += width;
-      take_all_eq = (left >= eqcnt);
-    }
-    __syncthreads();
-  }
-  uint32_t idthr = 0xFFFFFFFFu;
-  if (!take_all_eq) {  // exact key ties at the boundary: keep the lowest ids
-    uint32_t ipref = 0, imask = 0;
-    int ib = 32;
-    while (ib > 0) {
-      const int width = ib < BITS ? ib : BITS;
-      const int shift = ib - width;
-      const uint32_t dmask = (1u << width) - 1u;
-      for (int i = t; i < NB; i += nt) sh.hist[i] = 0;
-      __syncthreads();
-      for (int i = t; i < count; i += nt) {
-        uint32_t k;
-        int32_t d;
-        acc.get(i, k, d);
-        if (k == kpref && ((uint32_t)d & imask) == ipref)
-          atomicAdd(&sh.hist[((uint32_t)d >> shift) & dmask], 1u);
-      }
-      __syncthreads();
-      hist_threshold_n<NB, NT, false>(sh.hist, (uint32_t)left, sh.scan, sh.out);
-      const int dsel = sh.out[0] < 0 ? (int)dmask : sh.out[0];
-      if (sh.out[0] >= 0) left -= sh.out[1];
-      ipref |= (uint32_t)dsel << shift;
-      imask |= dmask << shift;
-      ib -= width;
-      __syncthreads();
-    }
-    idthr = ipref;
-  }
-  return SelRule{kmask, kpref, idthr};
 }
 
 // ---- final pass: one workgroup per chunk ------------------------------------------
@@ -790,222 +658,6 @@ __global__ __launch_bounds__(FIN_NT) void k_select_direct(DirectArgs a) {
 
 hipError_t launch_select_direct(const DirectArgs &a, int rows, int ntarget, hipStream_t st) {
   hipLaunchKernelGGL(k_select_direct, dim3((unsigned)rows, (unsigned)ntarget), dim3(FIN_NT), 0, st, a);
-  return hipGetLastError();
-}
-
-// ---- one workgroup per row, every key in registers ----------------------------------
-// Rows of up to 1024 * PER columns (16 per thread: 32 would spill at 1024
-// threads). Thread t holds columns t * PER + [0, PER),
-// so (thread, item) is column order. The threshold key (the T-th largest) is
-// found exactly by radix levels over the row's own key range: level 1 bins
-// key - kmin by its top 12 significant bits, the next levels refine the
-// boundary bin 12 bits at a time. Every key above the threshold is taken, and
-// of the keys equal to it those with the lowest entry ids (by column, or by
-// radix levels over the mapped ids when a map is given). Ids are written in
-// column order, then -1.
-#define ROW_NT 1024
-
-// min and max over the workgroup (s: ROW_NT / 64 x 2 words)
-__device__ __forceinline__ void block_minmax(uint32_t lo, uint32_t hi, uint32_t *s, uint32_t &mn, uint32_t &mx) {
-  lo = wave_min(lo);
-  hi = wave_max(hi);
-  const int t = threadIdx.x, nw = blockDim.x >> 6;
-  if ((t & 63) == 0) {
-    s[2 * (t >> 6)] = lo;
-    s[2 * (t >> 6) + 1] = hi;
-  }
-  __syncthreads();
-  mn = 0xFFFFFFFFu;
-  mx = 0u;
-  for (int i = 0; i < nw; ++i) {
-    mn = min(mn, s[2 * i]);
-    mx = max(mx, s[2 * i + 1]);
-  }
-  __syncthreads();
-}
-
-template <int PER, bool VEC>
-__global__ __launch_bounds__(ROW_NT) void k_select_row(DirectArgs a) {
-  __shared__ uint32_t hist[DIG_BINS];
-  __shared__ uint32_t scan[ROW_NT / 64 * 2];
-  __shared__ int hout[4];
-  const int r = blockIdx.x, tg = blockIdx.y, t = threadIdx.x;
-  const float *row = a.scores + (int64_t)r * a.n_cols;
-  const int32_t lim = row_limit(a.n_entries, a.q_pos, a.nq, r, a.n_cols);
-  const int T = a.T[tg];
-  int32_t *gout = a.out[tg] + (int64_t)r * a.out_stride[tg];
-  const int32_t c0 = t * PER;
-
-  // ---- keys: columns past the row's limit count as absent (key 0) ----
-  uint32_t key[PER];
-  if constexpr (VEC) {
-#pragma unroll
-    for (int j = 0; j < PER / 4; ++j) {
-      const int32_t c = min(c0 + 4 * j, a.n_cols - 4);  // in the row even past its end
-      const v4f v = *(const v4f *)(row + c);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) key[4 * j + e] = score_key(v[e]);
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < PER; ++j) key[j] = score_key(row[min(c0 + j, a.n_cols - 1)]);
-  }
-  uint32_t nv = 0, lo = 0xFFFFFFFFu, hi = 0u;
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const bool ok = c0 + j < lim && key[j] > KEY_NEG_INF;
-    key[j] = ok ? key[j] : 0u;
-    nv += ok ? 1u : 0u;
-    lo = ok ? min(lo, key[j]) : lo;
-    hi = max(hi, key[j]);
-  }
-  const uint32_t n_valid = block_sum(nv, scan);
-  const int n_sel = min((uint32_t)T, n_valid);
-
-  // ---- threshold key and how many keys equal to it are taken ----
-  uint32_t thr = KEY_NEG_INF + 1u;  // every valid key passes
-  int take_eq = 1 << 30;
-  if ((uint32_t)T < n_valid) {
-    uint32_t kmin, kmax;
-    block_minmax(lo, hi, scan, kmin, kmax);
-    // level shifts: the range's significant bits, 12 per level
-    const uint32_t range = kmax - kmin;
-    const int bits = range ? 32 - __builtin_clz(range) : 0;
-    int shift = bits > 12 ? bits - 12 : 0;
-    uint32_t prefix = 0;  // bits [pshift, 32) of key - kmin in the boundary bin so far
-    int need = T;         // keys still to take at or below the current prefix
-    int pshift = 32;      // bits above the current level are fixed to `prefix`
-    bool all_in_set = false;
-    for (int level = 0; level < 3; ++level) {
-      for (int i = t; i < DIG_BINS; i += ROW_NT) hist[i] = 0;
-      __syncthreads();
-      // this level's digit: bits [shift, pshift) of key - kmin (at most 12)
-      const uint32_t mask = pshift >= 32 ? (uint32_t)(DIG_BINS - 1) : ((1u << (pshift - shift)) - 1u);
-#pragma unroll
-      for (int j = 0; j < PER; ++j) {
-        const uint32_t d = key[j] - kmin;
-        const bool in = key[j] != 0u && (pshift >= 32 || (d >> pshift) == prefix);
-        if (in) atomicAdd(&hist[(d >> shift) & mask], 1u);
-      }
-      __syncthreads();
-      hist_threshold_n<DIG_BINS, ROW_NT, true>(hist, (uint32_t)need, scan, hout);
-      const int bin = hout[0];
-      const int before = hout[1];
-      __syncthreads();  // hout is read before the next level rewrites it
-      if (bin < 0) {
-        // the set holds exactly `need` keys: all of them are taken, and the
-        // threshold is the set's smallest key
-        uint32_t lo2 = 0xFFFFFFFFu;
-#pragma unroll
-        for (int j = 0; j < PER; ++j) {
-          const uint32_t d = key[j] - kmin;
-          const bool in = key[j] != 0u && (pshift >= 32 || (d >> pshift) == prefix);
-          lo2 = in ? min(lo2, key[j]) : lo2;
-        }
-        uint32_t mn, mx;
-        block_minmax(lo2, 0u, scan, mn, mx);
-        thr = mn;
-        all_in_set = true;
-        break;
-      }
-      need -= before;  // keys in higher bins are all taken
-      prefix = (pshift >= 32 ? 0u : (prefix << (pshift - shift))) | (uint32_t)bin;
-      pshift = shift;
-      if (shift == 0) break;
-      shift = shift > 12 ? shift - 12 : 0;
-    }
-    if (!all_in_set) {
-      thr = kmin + (prefix << pshift);
-      take_eq = need;
-    }
-  }
-
-  // ---- ties at the threshold ----
-  // Of the keys equal to thr, the take_eq with the lowest ids are taken.
-  // Without a map the id is the column, so these are the first ones in column
-  // order. With a map, column order is not id order: when only some of them
-  // are taken, radix levels over their ids (bits 31..20, 19..8, 7..0 of an
-  // order key in which a lower id is larger) find the boundary id exactly.
-  // Afterwards an equal key is taken when its id key's bits from ishift up
-  // exceed iprefix, or equal it and it is among the first ineed such.
-  const int32_t *map = a.cand_map ? a.cand_map + (int64_t)r * a.n_cols : nullptr;
-  auto id_key = [&](int j) { return ~((uint32_t)map[min(c0 + j, a.n_cols - 1)] ^ 0x80000000u); };
-  uint32_t ne = 0;
-#pragma unroll
-  for (int j = 0; j < PER; ++j) ne += key[j] == thr ? 1u : 0u;
-  uint32_t tot_eq;
-  block_exclusive_scan(ne, scan, &tot_eq);
-  int ishift = 32;  // 32: ids play no part
-  uint32_t iprefix = 0;
-  int ineed = take_eq;
-  if (map && take_eq < (int)tot_eq) {  // uniform over the workgroup
-    constexpr int kShift[3] = {20, 8, 0};
-    for (int level = 0; level < 3; ++level) {
-      const int shift = kShift[level];
-      for (int i = t; i < DIG_BINS; i += ROW_NT) hist[i] = 0;
-      __syncthreads();
-      const uint32_t mask = ishift >= 32 ? (uint32_t)(DIG_BINS - 1) : ((1u << (ishift - shift)) - 1u);
-#pragma unroll
-      for (int j = 0; j < PER; ++j) {
-        if (key[j] != thr) continue;
-        const uint32_t ik = id_key(j);
-        if (ishift >= 32 || (ik >> ishift) == iprefix) atomicAdd(&hist[(ik >> shift) & mask], 1u);
-      }
-      __syncthreads();
-      hist_threshold_n<DIG_BINS, ROW_NT, true>(hist, (uint32_t)ineed, scan, hout);
-      const int bin = hout[0];
-      const int before = hout[1];
-      __syncthreads();
-      if (bin < 0) break;  // the current set holds exactly ineed keys: all are taken
-      ineed -= before;
-      iprefix = (ishift >= 32 ? 0u : (iprefix << (ishift - shift))) | (uint32_t)bin;
-      ishift = shift;
-    }
-  }
-  // bit j of take_m: key j taken outright; of eq_m: key j equal to thr with
-  // an id matching the boundary prefix (the first ineed of those are taken)
-  uint32_t take_m = 0, eq_m = 0;
-  if (ishift >= 32) {
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      take_m |= (key[j] > thr ? 1u : 0u) << j;
-      eq_m |= (key[j] == thr ? 1u : 0u) << j;
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const uint32_t ik = key[j] == thr ? id_key(j) >> ishift : 0u;
-      take_m |= (key[j] > thr || (key[j] == thr && ik > iprefix) ? 1u : 0u) << j;
-      eq_m |= (key[j] == thr && ik == iprefix ? 1u : 0u) << j;
-    }
-  }
-
-  // ---- emission in column order ----
-  uint32_t tot;
-  const uint32_t eb = block_exclusive_scan((uint32_t)__builtin_popcount(eq_m), scan, &tot);
-  const int eq_take = max(0, min(__builtin_popcount(eq_m), ineed - (int)eb));
-  const uint32_t off = block_exclusive_scan((uint32_t)(__builtin_popcount(take_m) + eq_take), scan, &tot);
-  int o = (int)off, e = 0;
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const bool eq = (eq_m >> j) & 1u;
-    const bool take = ((take_m >> j) & 1u) || (eq && e < eq_take);
-    e += eq ? 1 : 0;
-    if (take) {
-      gout[o++] = map ? map[c0 + j] : c0 + j;
-    }
-  }
-  for (int i = n_sel + t; i < T; i += ROW_NT) gout[i] = -1;
-}
-
-hipError_t launch_select_row(const DirectArgs &a, int rows, int ntarget, hipStream_t st) {
-  const bool vec = (a.n_cols & 3) == 0 && (((uintptr_t)a.scores) & 15) == 0;
-  const dim3 grid((unsigned)rows, (unsigned)ntarget);
-  if (a.n_cols > kSelectRowMax) return hipErrorInvalidValue;
-  if (vec)
-    hipLaunchKernelGGL((k_select_row<kSelectRowMax / ROW_NT, true>), grid, dim3(ROW_NT), 0, st, a);
-  else
-    hipLaunchKernelGGL((k_select_row<kSelectRowMax / ROW_NT, false>), grid, dim3(ROW_NT), 0, st, a);
   return hipGetLastError();
 }
 

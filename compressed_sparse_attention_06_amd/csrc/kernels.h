@@ -162,9 +162,9 @@ hipError_t launch_index_score_mq(const ScoreArgs &a, int batch, hipStream_t st);
 hipError_t launch_compact(const CompactArgs &a, int rows, hipStream_t st);
 hipError_t launch_final(const FinalArgs &a, int rows, int ntarget, hipStream_t st);
 hipError_t launch_select_direct(const DirectArgs &a, int rows, int ntarget, hipStream_t st);
-// one workgroup per row of up to kSelectRowMax columns; ids in column order
+// one workgroup per row of up to kSelectRowMax columns, histogram in LDS; ids in column order
 constexpr int kSelectRowMax = 16384;
-hipError_t launch_select_row(const DirectArgs &a, int rows, int ntarget, hipStream_t st);
+hipError_t launch_sel_rowwise(const DirectArgs &a, int rows, int ntarget, hipStream_t st);
 hipError_t launch_sort_rows(int32_t *ids, int32_t stride, int32_t T, int rows, hipStream_t st);
 // max_slots: most workgroups sharing one row (2 or more: rows cut between
 // workgroups are combined by a merge pass)
