@@ -34,19 +34,24 @@ namespace csa2 {
 // CAND: columns are a candidate list of entry ids; PCACHE: contiguous columns
 // whose page ids are cached in LDS (pages of at least 32 entries). Both are
 // template parameters so no branch sits between a load and its use.
+// One chunk of columns [col0, col0 + chunk) of score row r. Candidate
+// columns are all scored (pads and ids past the visible entries give -inf);
+// entry columns are scored up to the row's visible entries, and past them
+// either left alone or, with write_masked, set to -inf by plain stores.
 template <bool CAND, bool PCACHE>
-__global__ __launch_bounds__(256) void k_index_score(ScoreArgs a) {
-  __shared__ uint32_t lhist[HIST_BINS];
-  __shared__ int32_t spage[SC_MAX_PAGES];
-  const int r = blockIdx.y;
+__device__ __forceinline__ void score_chunk(const ScoreArgs &a, int r, int64_t col0, uint32_t *lhist,
+                                            int32_t *spage) {
   const int b = r / a.nq, t = r % a.nq;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int32_t nent = a.c.n_entries[b];
   const int32_t V = visible_entries(a.c, a.q_pos, b, a.nq, t);
-  const int64_t col0 = (int64_t)blockIdx.x * a.chunk;
   const int64_t col_end = min(col0 + (int64_t)a.chunk, (int64_t)a.n_cols);
-  const int64_t work_end = (a.cand || a.write_masked) ? col_end : min(col_end, (int64_t)V);
+  const int64_t work_end = CAND ? col_end : min(col_end, (int64_t)V);
   const bool do_hist = a.hist != nullptr;
+  if (!CAND && a.write_masked) {  // masked tail: -inf, no key loads
+    float *sr = a.scores + (int64_t)r * a.n_cols;
+    for (int64_t c = max(col0, work_end) + threadIdx.x; c < col_end; c += 256) sr[c] = -INFINITY;
+  }
   if (col0 < work_end) {  // uniform across the block
   for (int i = threadIdx.x; i < HIST_BINS; i += 256) lhist[i] = 0;
   // Full rows with pages of >= 32 entries: cache this chunk's page ids in LDS
@@ -183,6 +188,13 @@ __global__ __launch_bounds__(256) void k_index_score(ScoreArgs a) {
     }
   }
   }  // active workgroup
+}
+
+template <bool CAND, bool PCACHE>
+__global__ __launch_bounds__(256) void k_index_score(ScoreArgs a) {
+  __shared__ uint32_t lhist[HIST_BINS];
+  __shared__ int32_t spage[SC_MAX_PAGES];
+  score_chunk<CAND, PCACHE>(a, blockIdx.y, (int64_t)blockIdx.x * a.chunk, lhist, spage);
 }
 
 hipError_t launch_index_score(const ScoreArgs &a, int rows, hipStream_t st) {
