@@ -563,11 +563,17 @@ csa2_status run_layer_select(const csa2_layer_args *p, const WsLayout &L, int32_
   return s;
 }
 
-csa2_status csa2_layer_step(const csa2_layer_args *p, void *stream) {
-  if (!p) return fail(CSA2_EINVAL, "args is NULL");
+csa2_status csa2_layer_step(const csa2_layer_args *args, void *stream) {
+  if (!args) return fail(CSA2_EINVAL, "args is NULL");
+  // the mode's bytes are read as an int first: a C caller may pass any value,
+  // and a C++ load of an out-of-range enumerator is undefined
+  int32_t mode_raw;
+  static_assert(sizeof(csa2_mode) == sizeof(int32_t), "csa2_mode is an int");
+  memcpy(&mode_raw, &args->mode, sizeof mode_raw);
+  if (mode_raw != CSA2_FULL && mode_raw != CSA2_REINDEX && mode_raw != CSA2_REUSE)
+    return fail(CSA2_EINVAL, "unknown mode %d", (int)mode_raw);
+  const csa2_layer_args *p = args;
   const bool selecting = p->mode == CSA2_FULL || p->mode == CSA2_REINDEX;
-  if (p->mode != CSA2_FULL && p->mode != CSA2_REINDEX && p->mode != CSA2_REUSE)
-    return fail(CSA2_EINVAL, "unknown mode %d", (int)p->mode);
   csa2_status s = check_cache(p->cache, true, selecting);
   if (s) return s;
   if ((s = check_window(p->win))) return s;
