@@ -21,7 +21,8 @@ of the tiny workload, two measured ceilings beside the 8 TB/s datasheet
 figure -- a 1 GiB device copy (read + write) and a 2 GiB read-only stream --,
 and rooflines measured live with HIP events around back-to-back calls replayed
 from one HIP graph on the stream they run on: `roofline` for the kernel that
-takes the most step time, the attention call (k_attend_seg and its merge),
+takes the most step time, the attention call (k_attend_seg, or k_attend_wave
+where every workgroup takes a long range of units, and their merge),
 and `roofline_scoring` for the indexer scoring kernel (HBM-bound in decode;
 in the prefill chunk the kernel that scores and selects without a score
 matrix, against the fp16 matrix-core peak)).
@@ -48,7 +49,9 @@ WORKLOAD_128K = "b32_128k_full_reuse5"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_index_score_b8_1m.json")
 SCORE_SRC = os.path.join(ROOT, "compressed_sparse_attention_06_amd", "csrc", "k_score.hip")
 ATT_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attend_b8_1m.json")
-ATT_SRC = os.path.join(ROOT, "compressed_sparse_attention_06_amd", "csrc", "k_attend.hip")
+# the sources an attention traffic record was taken from (kernel + shared helpers)
+ATT_SRC = [os.path.join(ROOT, "compressed_sparse_attention_06_amd", "csrc", f)
+           for f in ("k_attend.hip", "attend_common.h", "csa2_dev.h")]
 
 
 def log(*a):
@@ -311,6 +314,14 @@ def time_steps(chains, steps, warmup, use_graph):
     return eager_s, graph_s
 
 
+def src_sha256(src):
+    """sha256 of a source file, or of the concatenation of a list of them."""
+    h = hashlib.sha256()
+    for f in ([src] if isinstance(src, str) else src):
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
 def traffic_of(path, src, name):
     """Calibrated counter bytes per launch from a profiles/ record, while the
     kernel source it was taken from is unchanged and the workload matches."""
@@ -318,7 +329,7 @@ def traffic_of(path, src, name):
         return None
     try:
         rec = json.load(open(path))
-        src_hash = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        src_hash = src_sha256(src)
         if rec.get("kernel_source_sha256") == src_hash and rec.get("workload") == name:
             return rec.get("bytes_per_launch")
     except Exception:
@@ -383,7 +394,7 @@ def measure_workload(wl, name, n_copies, steps, warmup, kernel_iters, use_graph,
               "traffic": traffic_of(TRAFFIC_FILE, SCORE_SRC, name),
               "bytes_per_launch": kb, "us_per_launch": round(k_ms * 1e3, 3)}
 
-    # the dominant kernel by step time: attention (k_attend_seg + its merge) of the
+    # the dominant kernel by step time: attention (k_attend_seg or k_attend_wave + the merge) of the
     # first layer, called with that layer's selection
     li0 = 0
     att_args = []
@@ -413,7 +424,7 @@ def measure_workload(wl, name, n_copies, steps, warmup, kernel_iters, use_graph,
     # 4096 queries gather from a 9.4 MB cache that stays in the on-chip caches,
     # so there the matrix cores are the roofline
     if prefill:
-        ra = {"kernel": "csa2_sparse_attend: k_attend_seg (first layer's selection; no merge: "
+        ra = {"kernel": "csa2_sparse_attend: k_attend_wave (paired waves; first layer's selection; no merge: "
                         "every row falls whole to one workgroup)",
               "bound": "mfma", "achieved": round(att_tflops, 1), "peak": MFMA_F16_PEAK_TFLOPS,
               "unit": "TFLOP/s", "frac": round(att_tflops / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
@@ -658,7 +669,7 @@ def main():
                 csa2.sparse_attend(caches[0], vidx, L["q"], vwin, sm_scale=wl.sm_scale, out=out, lse=lse, ws=wsv)
         torch.cuda.synchronize()
         log("attention variants: 5 calls each of (a) the selection, (b) runs of 4 consecutive entries, "
-            "(c) the selection without the window (the last 15 k_attend_seg dispatches)")
+            "(c) the selection without the window (the last 15 attention dispatches)")
 
     # ---- the other workloads beside the main one (two input copies each, fewer steps) ----
     extras = {}

@@ -71,7 +71,7 @@ def lib():
         for name in ("csa2_index_score", "csa2_topk", "csa2_sparse_attend", "csa2_sparse_attend_noalloc",
                      "csa2_layer_step",
                      "csa2_index_topk", "csa2_dequant_fp4", "csa2_dequant_e4m3", "csa2_quantize_fp4", "csa2_kv_append",
-                     "csa2_window_append", "csa2_stream_read"):
+                     "csa2_window_append", "csa2_stream_read", "csa2_set_attend_kernel"):
             getattr(L, name).restype = C.c_int
         _lib = L
     return _lib
@@ -80,6 +80,7 @@ def lib():
 EXPORTS = ["csa2_index_score", "csa2_topk", "csa2_sparse_attend", "csa2_sparse_attend_noalloc", "csa2_layer_step",
            "csa2_index_topk", "csa2_workspace_bytes", "csa2_dequant_fp4", "csa2_dequant_e4m3",
            "csa2_quantize_fp4", "csa2_kv_append", "csa2_window_append", "csa2_stream_read",
+           "csa2_set_attend_kernel",
            "csa2_status_string", "csa2_last_error", "csa2_version"]
 
 
@@ -287,6 +288,17 @@ def sparse_attend(cache: Cache, idx, q, win: Optional[Window], q_pos=None, sm_sc
                                     C.c_float(sm_scale), C.c_int32(B), C.c_int32(nq), _ptr(out),
                                     _ptr(lse), _ptr(ws), C.c_size_t(ws.numel()), _stream()))
     return out, lse
+
+
+ATTEND_KERNELS = {"auto": 0, "seg": 1, "pair": 2}
+
+
+def set_attend_kernel(name: str):
+    """csa2_set_attend_kernel: the attention kernel of the calls that follow
+    ("auto", "seg": eight waves per unit, "pair": paired waves); process-wide."""
+    if name not in ATTEND_KERNELS:
+        raise CSA2Error(1, f"attend kernel {name!r} is not one of {sorted(ATTEND_KERNELS)}")
+    _check(lib().csa2_set_attend_kernel(C.c_int32(ATTEND_KERNELS[name])))
 
 
 def stream_read(x: torch.Tensor, sink: torch.Tensor, blocks: int = 2048):

@@ -31,8 +31,15 @@ def _run(cmd):
 
 # per-file additions: the attention kernels and the fused prefill selection
 # carry no NaN (logits, weights and index scores are finite or -inf), which
-# lets max reductions and ReLUs skip NaN quieting
-FILE_FLAGS = {"k_attend.hip": ["-fno-honor-nans"], "k_prefill_topk.hip": ["-fno-honor-nans"]}
+# lets max reductions and ReLUs skip NaN quieting. The wave-split attention
+# keeps its 128 fp32 output accumulators in VGPRs (MFMA results written to
+# VGPRs rather than AGPRs): its rescale multiplies them in place, and the
+# AGPR form made the register allocator shuttle them between the two files
+FILE_FLAGS = {
+    "k_attend.hip": ["-fno-honor-nans"],
+    "k_attend_wave.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "k_prefill_topk.hip": ["-fno-honor-nans"],
+}
 
 
 def build(verbose: bool = False) -> str:

@@ -4,9 +4,11 @@
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <mutex>
 
 #include "../../include/csa2_probe.h"
@@ -306,6 +308,26 @@ csa2_status run_select(const WsLayout &L, char *ws, int rows, int32_t n_cols, co
   return hip_check(csa2::launch_final(f, rows, ntarget, st), "select");
 }
 
+// Attention kernel choice (csa2_set_attend_kernel): auto, the eight-wave
+// kernel, or the paired-wave kernel; the initial value from the environment.
+int initial_attend_kernel() {
+  const char *v = getenv("CSA2_ATTEND_KERNEL");
+  if (v && strcmp(v, "seg") == 0) return CSA2_ATTEND_SEG;
+  if (v && strcmp(v, "pair") == 0) return CSA2_ATTEND_PAIR;
+  return CSA2_ATTEND_AUTO;
+}
+std::atomic<int> g_attend_kernel{initial_attend_kernel()};
+
+// auto: the paired-wave kernel pays more per row (Q staging, the combine of
+// four pairs) and less per unit, so it is taken where every workgroup has a
+// long range of units (the prefill chunk: 272 per workgroup; decode batches:
+// one to five)
+bool use_pair_kernel(const WsLayout &L) {
+  const int k = g_attend_kernel.load(std::memory_order_relaxed);
+  if (k != CSA2_ATTEND_AUTO) return k == CSA2_ATTEND_PAIR;
+  return (L.att_T + L.att_G - 1) / L.att_G >= 16;
+}
+
 csa2_status run_attend(const WsLayout &L, char *ws, const csa2_cache *cache, const int32_t *idx,
                        int32_t k, const float *q, const csa2_window *win, const int32_t *q_pos,
                        float sm_scale, int rows, int32_t nq, float *out, float *lse, hipStream_t st) {
@@ -334,6 +356,7 @@ csa2_status run_attend(const WsLayout &L, char *ws, const csa2_cache *cache, con
   sg.xcd = 1;
   sg.out = out;
   sg.lse = lse;
+  if (use_pair_kernel(L)) return hip_check(csa2::launch_attend_wave(a, sg, L.att_slots, st), "attend");
   return hip_check(csa2::launch_attend_seg(a, sg, L.att_slots, st), "attend");
 }
 
@@ -717,6 +740,13 @@ csa2_status csa2_stream_read(const void *p, size_t n_bytes, uint32_t *sink, int3
   if (n_bytes < 16 || n_bytes % 16 || ((uintptr_t)p & 15)) return fail(CSA2_EINVAL, "n_bytes must be a positive multiple of 16, p 16-byte aligned");
   if (blocks < 1) return fail(CSA2_EINVAL, "blocks must be positive");
   return hip_check(csa2::launch_stream_read(p, (int64_t)n_bytes, sink, blocks, (hipStream_t)stream), "stream_read");
+}
+
+csa2_status csa2_set_attend_kernel(int32_t kernel) {
+  if (kernel != CSA2_ATTEND_AUTO && kernel != CSA2_ATTEND_SEG && kernel != CSA2_ATTEND_PAIR)
+    return fail(CSA2_EINVAL, "attend kernel %d is not one of 0 (auto), 1 (seg), 2 (pair)", kernel);
+  g_attend_kernel.store(kernel, std::memory_order_relaxed);
+  return CSA2_OK;
 }
 
 csa2_status csa2_dequant_e4m3(const uint8_t *bytes, int64_t n, float *out, void *stream) {

@@ -24,52 +24,13 @@
 //    per unit.
 #include "csa2_dev.h"
 #include "kernels.h"
+#include "attend_common.h"
 
 namespace csa2 {
 
 #define AT_PITCH 520   // halfs per LDS row of the staged Q (512 + 8)
 
-typedef __attribute__((address_space(3))) v4s *lds_v4s_ptr;
-
 enum { SPLIT_ENTRIES = 0, SPLIT_WINDOW = 1 };
-
-// DPP move within rows of 16 lanes (quad_perm / mirror controls only)
-template <int CTRL>
-__device__ __forceinline__ float dpp_f32(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-
-// Q of query row r: this thread's 32 fp32 values (head tid / 16, channels
-// 32 (tid % 16) + [0, 32)).
-__device__ __forceinline__ void load_q(const AttendArgs &a, int r, float *qv) {
-  const int tid = threadIdx.x;
-  const float *src = a.q + ((int64_t)r * CSA2_H + (tid >> 4)) * CSA2_D + (tid & 15) * 32;
-#pragma unroll
-  for (int i = 0; i < 32; i += 4) {
-    const v4f x = *(const v4f *)(src + i);
-    qv[i] = x[0];
-    qv[i + 1] = x[1];
-    qv[i + 2] = x[2];
-    qv[i + 3] = x[3];
-  }
-}
-
-// Window geometry of query row r: rows w_first..w_last of its request's window.
-__device__ __forceinline__ void window_range(const AttendArgs &a, int r, int b, int32_t &w_first,
-                                             int32_t &w_last) {
-  w_first = 0;
-  w_last = -1;
-  if (!a.win_codes) return;
-  const int32_t len = a.win_len[b];
-  if (a.win_pos0) {
-    const int32_t pq = a.q_pos ? a.q_pos[r] : 0x7FFFFFFF;
-    const int64_t rel = (int64_t)pq - a.win_pos0[b];
-    w_first = (int32_t)max((int64_t)0, rel - a.win_window + 1);
-    w_last = (int32_t)min(min((int64_t)len, (int64_t)a.win_rows) - 1, rel);
-  } else {
-    w_last = min(len, a.win_rows) - 1;
-  }
-}
 
 // ---- segmented attention: eight waves, 128 positions per step -----------------------
 // The attention set of every query row (k selected entries, then from k
@@ -83,16 +44,7 @@ __device__ __forceinline__ void window_range(const AttendArgs &a, int r, int b, 
 // whose units all fall to one workgroup is normalised and written there; a row
 // cut between workgroups leaves one partial per workgroup (slot 0 for the
 // workgroup's first row, slot 1 for its last), which k_merge_seg combines.
-#define AS_UNIT 128   // positions per unit (8 waves x 16)
 #define AS_PPITCH 136 // halfs per LDS row of P (128 + 8)
-#define AS_RPITCH 512 // halfs per LDS row of the R tile (unpadded; 16-byte chunks are swizzled)
-
-// R tile swizzle: in row r, the 16-byte chunk c of each 256-byte block is
-// stored at chunk c ^ seg_rswz(r). Sixteen consecutive rows then fill every
-// bank for the QK stores (same chunk, 16 rows) and eight rows x two chunks do
-// the same for the PV transposed loads, with 32 or 64 banks.
-__device__ __forceinline__ int seg_rswz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1) | (r & 8); }
-
 struct SegShared {
   union {
     _Float16 q[CSA2_H * AT_PITCH];  // hi halves of Q, staged once per row
@@ -123,24 +75,6 @@ struct SegSlice {
 struct SegFetch {
   int32_t id, page;
 };
-
-// max of two non-NaN floats in one instruction: median of (a, b, +inf)
-__device__ __forceinline__ float fmax_nc(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, INFINITY); }
-
-// maximum over each row of 16 lanes: swap neighbours, swap pairs, mirror
-// within 8 lanes, mirror within 16
-__device__ __forceinline__ float row16_max(float v) {
-  v = fmax_nc(v, dpp_f32<0xB1>(v));
-  v = fmax_nc(v, dpp_f32<0x4E>(v));
-  v = fmax_nc(v, dpp_f32<0x141>(v));
-  v = fmax_nc(v, dpp_f32<0x140>(v));
-  return v;
-}
-
-// Positions of a row's attention set: entries at [0, k), window rows from
-// kw = k rounded up to 16, so that each wave's 16 positions are all entries
-// (those at k and beyond hold nothing) or all window rows.
-__device__ __forceinline__ int32_t seg_kw(int32_t k) { return (k + 15) & ~15; }
 
 // id of the lane's position in unit y (0 past the range or for window waves)
 __device__ __forceinline__ int32_t seg_fetch_id(const AttendArgs &a, int64_t y, int64_t u_end, int32_t U,
@@ -651,11 +585,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     s.lse[(int64_t)r * CSA2_H + h] = (L > 0.f) ? (M + log2f(L)) * 0.6931471805599453f : -INFINITY;
 }
 
-hipError_t launch_attend_seg(const AttendArgs &a, const SegArgs &s, int max_slots, hipStream_t st) {
-  if (s.G < 1 || s.G > kSegMaxWg || s.T < s.G || s.U < 1) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_attend_seg, dim3((unsigned)s.G), dim3(512), 0, st, a, s);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || max_slots < 2) return e;
+hipError_t launch_merge_seg(const AttendArgs &a, const SegArgs &s, int max_slots, hipStream_t st) {
+  if (max_slots < 2) return hipSuccess;
   MergeArgs m{};
   m.part = a.part;
   const dim3 grid((unsigned)(CSA2_H * (s.T / s.U)));
@@ -667,6 +598,14 @@ hipError_t launch_attend_seg(const AttendArgs &a, const SegArgs &s, int max_slot
   else
     hipLaunchKernelGGL(k_merge_seg<24>, grid, dim3(128), 0, st, m, s);
   return hipGetLastError();
+}
+
+hipError_t launch_attend_seg(const AttendArgs &a, const SegArgs &s, int max_slots, hipStream_t st) {
+  if (s.G < 1 || s.G > kSegMaxWg || s.T < s.G || s.U < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_attend_seg, dim3((unsigned)s.G), dim3(512), 0, st, a, s);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_merge_seg(a, s, max_slots, st);
 }
 
 // ---- bit-exact dequantisation probes (same device helpers as above) ----

@@ -169,6 +169,10 @@ hipError_t launch_sort_rows(int32_t *ids, int32_t stride, int32_t T, int rows, h
 // max_slots: most workgroups sharing one row (2 or more: rows cut between
 // workgroups are combined by a merge pass)
 hipError_t launch_attend_seg(const AttendArgs &a, const SegArgs &s, int max_slots, hipStream_t st);
+// the same work split with each of four waves taking 32 positions of every unit on its own
+hipError_t launch_attend_wave(const AttendArgs &a, const SegArgs &s, int max_slots, hipStream_t st);
+// the pass that combines the partials of rows cut between workgroups (max_slots >= 2)
+hipError_t launch_merge_seg(const AttendArgs &a, const SegArgs &s, int max_slots, hipStream_t st);
 hipError_t launch_dequant_fp4(const uint8_t *codes, const uint8_t *scales, int64_t n_rows,
                               int32_t channels, uint16_t *out, hipStream_t st);
 hipError_t launch_dequant_e4m3(const uint8_t *bytes, int64_t n, float *out, hipStream_t st);

@@ -142,6 +142,11 @@ def test_other_entry_points_validation():
     assert L.csa2_index_topk(C.byref(cs), p, p, p, None, 1, 1, 8, 16, p, None, p, big, None) == EINVAL
     assert L.csa2_index_topk(C.byref(cs), p, p, p, None, 1, 1, 8, 0, p, None, None, C.c_size_t(0),
                              None) == EWORKSPACE
+    # the attention-kernel choice: 0 (auto), 1 (eight waves), 2 (paired waves); nothing else
+    for k in (3, -1):
+        assert L.csa2_set_attend_kernel(k) == EINVAL
+    for k in (1, 2, 0):
+        assert L.csa2_set_attend_kernel(k) == 0
 
 
 @pytest.mark.parametrize("mode,n_cols,k,pool,win", [

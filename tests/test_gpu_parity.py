@@ -35,6 +35,15 @@ def setup_module(module):
     csa2.lib()
 
 
+@pytest.fixture(params=["seg", "pair"])
+def attend_kernel(request):
+    """The attention tests run once per attention kernel (the eight-wave and
+    the paired-wave form; by default the library picks one by work size)."""
+    csa2.set_attend_kernel(request.param)
+    yield request.param
+    csa2.set_attend_kernel("auto")
+
+
 def _log(msg):
     print(msg, flush=True)
 
@@ -289,7 +298,7 @@ ATT_CASES = [
 
 
 @pytest.mark.parametrize("case", ATT_CASES, ids=["tiny", "ragged_rowscale", "short"])
-def test_sparse_attend_given_oracle_indices(case):
+def test_sparse_attend_given_oracle_indices(case, attend_kernel):
     _log(f"sparse_attend {case}")
     wl = make_small_decode(layers="F", **case)
     L, c = wl.layers[0], wl.caches[0]
@@ -299,7 +308,7 @@ def test_sparse_attend_given_oracle_indices(case):
     assert_attention_close(g_out.cpu().numpy(), g_lse.cpu().numpy(), r["out"], r["lse"], "attend")
 
 
-def test_sparse_attend_edge_cases():
+def test_sparse_attend_edge_cases(attend_kernel):
     _log("sparse_attend edges")
     wl = make_small_decode([4 * 64, 4 * 64], layers="F", k=8)
     c, L = wl.caches[0], wl.layers[0]
@@ -316,7 +325,7 @@ def test_sparse_attend_edge_cases():
     assert_attention_close(g_out.cpu().numpy(), g_lse.cpu().numpy(), o_out, o_lse, "no window")
 
 
-def test_sparse_attend_poisoned_unused_bytes():
+def test_sparse_attend_poisoned_unused_bytes(attend_kernel):
     """Bytes that no position of the attention set may use are NaN patterns
     (0xFF: an E4M3 NaN as a scale or window byte): a physical page no request
     maps (page 0, which a position without an entry addresses), the slots past
@@ -383,7 +392,7 @@ UNIT_CASES = [
 @pytest.mark.parametrize("case", UNIT_CASES, ids=["k1", "k13_nowin", "k300", "nq3_prefill", "b30_k2048",
                                                  "nq50_k2048", "k4096_b1", "k4096_b3", "b16_k2048",
                                                  "b40_k2048"])
-def test_sparse_attend_unit_geometry(case):
+def test_sparse_attend_unit_geometry(case, attend_kernel):
     _log(f"sparse_attend geometry {case}")
     wl = make_small_decode(contexts=case["contexts"], layers="F", k=case["k"], nq=case["nq"],
                            prefill=case.get("prefill", False), page_size=32, shuffle=True, row_scale=True)
@@ -408,7 +417,7 @@ def test_sparse_attend_unit_geometry(case):
     assert_attention_close(g_out.cpu().numpy(), g_lse.cpu().numpy(), o_out, o_lse, f"geometry {case}")
 
 
-def test_sparse_attend_large_logits():
+def test_sparse_attend_large_logits(attend_kernel):
     """Rows of 2688 and a large query: the running max keeps the softmax finite."""
     wl = make_small_decode([4 * 64], layers="F", k=4)
     c = wl.caches[0]
@@ -425,7 +434,7 @@ def test_sparse_attend_large_logits():
     assert np.abs(g_lse - o_lse).max() / abs(o_lse).max() < 1e-6
 
 
-def test_sparse_attend_prefill_windows():
+def test_sparse_attend_prefill_windows(attend_kernel):
     _log("sparse_attend prefill windows")
     wl = make_small_decode([4 * 900], layers="F", k=64, nq=7, prefill=True, page_size=32)
     L, c = wl.layers[0], wl.caches[0]
@@ -461,7 +470,7 @@ LAYER_CASES = [
 @pytest.mark.parametrize("case", LAYER_CASES, ids=["tiny_full", "full_reuse", "full_reindex_reuse",
                                                    "rowscale", "short_ctx", "long_pool", "prefill_rows",
                                                    "max_k_pool", "page_1", "page_4096", "empty_request"])
-def test_layer_step_chain(case):
+def test_layer_step_chain(case, attend_kernel):
     _log(f"layer chain {case}")
     wl = make_small_decode(**case)
     res_g = run_gpu(wl)
@@ -469,7 +478,7 @@ def test_layer_step_chain(case):
     compare_workload(wl, res_g, res_o, "chain")
 
 
-def test_reuse_equals_full_given_same_indices():
+def test_reuse_equals_full_given_same_indices(attend_kernel):
     wl = make_small_decode([4 * 5000], layers="FU", k=256, page_size=64)
     dw = DevWorkload(wl)
     calls = dw.calls()
@@ -492,7 +501,7 @@ def test_layer_step_repeatable():
         assert (x["out"] == y["out"]).all() and (x["lse"] == y["lse"]).all()
 
 
-def test_graph_capture_replays_match_eager():
+def test_graph_capture_replays_match_eager(attend_kernel):
     """A captured Full/Reindex/Reuse chain replays to the eager result every time."""
     _log("graph capture")
     wl = make_small_decode([4 * 30000, 4 * 7000], layers="FRUU", k=512, pool=2048, shuffle=True)
