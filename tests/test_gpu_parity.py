@@ -278,6 +278,32 @@ def test_reindex_shuffled_pool_many_rows():
     assert_attention_close(call.out.cpu().numpy(), call.lse.cpu().numpy(), o_out, o_lse, "reindex attend")
 
 
+def test_index_topk_many_ragged_rows():
+    """Rows of very different lengths in grids sized by the longest: 128 rows
+    of 1,000..40,960 entries (capacity 40,960), so most of the scoring,
+    compaction and final workgroups hold no column of their row, and some
+    rows are shorter than k. Every row's top-2048 and pool of 4096 against
+    the oracle's scores: sets equal outside the near-tie band, ascending, -1
+    past the visible entries."""
+    rng = np.random.default_rng(11)
+    ent = np.concatenate([[40960], rng.integers(1000, 40960, size=127)])
+    _log(f"many ragged rows: {len(ent)} rows, {int(ent.sum())} entries")
+    wl = make_small_decode(contexts=list(4 * ent), layers="F", k=2048, pool=4096, page_size=64, shuffle=True)
+    c, L = wl.caches[0], wl.layers[0]
+    g_idx, g_pool = csa2.index_topk(dev_cache(c), t(L.qix_codes), t(L.qix_scales), t(L.w), 2048, pool=4096)
+    g_idx, g_pool = g_idx.cpu().numpy(), g_pool.cpu().numpy()
+    o_sc = oracle.index_score(c, L.qix_codes, L.qix_scales, L.w)
+    o_idx, o_pool = oracle.topk(o_sc, 2048), oracle.topk(o_sc, 4096)
+    n_exact = 0
+    for b in range(len(ent)):
+        for g, o, tag in ((g_idx, o_idx, "top-k"), (g_pool, o_pool, "pool")):
+            row = g[b, 0]
+            v = row[row >= 0]
+            assert (np.diff(v) > 0).all() and (row[len(v):] == -1).all(), f"row {b} {tag}: order or pads"
+            n_exact += assert_selection_matches(o_sc[b, 0], o[b, 0], row, what=f"row {b} {tag}")
+    _log(f"{n_exact}/{2 * len(ent)} selections identical")
+
+
 def test_topk_candidate_map():
     rng = np.random.default_rng(9)
     n, k = 20000, 300
