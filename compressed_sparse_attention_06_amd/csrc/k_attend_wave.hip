@@ -33,8 +33,10 @@
 //    ds_read_b64_tr_b16 returns the B operand of the product (R with positions
 //    along K) for each block of 16 of its output channels;
 //  * O and the sum are rescaled only in chunks that raise some head's maximum.
-// Two workgroup barriers per unit (the exchange of the partial S), none
-// inside the logits or the product.
+// No workgroup barrier per unit: the two waves of a pair exchange their
+// partial S through LDS with a handshake of their own (a posted and an
+// acknowledged unit count per wave), so the four pairs run independently
+// between the row's start and its end.
 #include "csa2_dev.h"
 #include "kernels.h"
 #include "attend_common.h"
@@ -56,6 +58,7 @@ struct PairShared {
     float stage[4][CSA2_H][CSA2_D];     // row-end combine: each pair's scaled O
   };
   v4f sx[8][2][64];                     // each wave's partial S of its two tiles
+  int sflag[8], sack[8];                // per wave: last unit whose partial S is posted / was read by the partner
   float wm[4][CSA2_H], wl[4][CSA2_H];   // each pair's running max and sum
 };
 
@@ -336,6 +339,19 @@ __device__ __forceinline__ void pw_finish(const AttendArgs &a, const SegArgs &s,
   __syncthreads();  // the staging area and the pair states are read before the next row
 }
 
+// Pair-level handshake through LDS (the two waves of a pair run on
+// different SIMDs of the same compute unit, so the awaited wave always gets
+// there); the wait gives up after ~2^22 polls, so no wave can hang on it.
+__device__ __forceinline__ void pw_post(int *f, int v) {
+  if ((threadIdx.x & 63) == 0) __hip_atomic_store(f, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void pw_wait(int *f, int v) {
+  for (int it = 0; it < (1 << 22); ++it) {
+    if (__hip_atomic_load(f, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= v) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
 __global__ __launch_bounds__(PW_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attend_wave(AttendArgs a,
                                                                                                   SegArgs s) {
   __shared__ __attribute__((aligned(16))) PairShared sh;
@@ -354,6 +370,12 @@ __global__ __launch_bounds__(PW_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   // transposed-load row 4 g + c and channel 4 rq
   const uint32_t wr_base = (uint32_t)(n * PW_RP + 64 * g);
   const uint32_t tr_base = (uint32_t)((4 * g + (n >> 2)) * PW_RP + 4 * (n & 3));
+  if (lane == 0) {
+    sh.sflag[wave] = 0;
+    sh.sack[wave] = 0;
+  }
+  __syncthreads();
+  int useq = 0;  // units this wave has exchanged partial S for
 
   for (int64_t x = u_begin; x < u_end;) {
     const int32_t row = (int32_t)(x / U);
@@ -491,12 +513,18 @@ __global__ __launch_bounds__(PW_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
         for (int i = 0; i < 4; ++i) rs[0][i] = rs[1][i] = 1.f;
       }
       // the pair adds its two partial S (half 0 + half 1)
-      __syncthreads();  // the partner has read the previous unit's partial S
+      // (only the two waves of the pair wait for each other: the other pairs
+      // run on, which two workgroup barriers per unit did not allow)
+      ++useq;
+      pw_wait(&sh.sack[wave], useq - 1);  // the partner has read the previous unit's partial S
       sh.sx[wave][0][lane] = s0;
       sh.sx[wave][1][lane] = s1;
-      __syncthreads();
+      pw_post(&sh.sflag[wave], useq);
+      pw_wait(&sh.sflag[wave ^ 1], useq);
+      const v4f p0r = sh.sx[wave ^ 1][0][lane], p1r = sh.sx[wave ^ 1][1][lane];
+      pw_post(&sh.sack[wave ^ 1], useq);  // its slot may be written again
       if (live) {
-        const v4f p0v = sh.sx[wave ^ 1][0][lane], p1v = sh.sx[wave ^ 1][1][lane];
+        const v4f p0v = p0r, p1v = p1r;
         v4f Sf[2];
         Sf[0] = half ? p0v + s0 : s0 + p0v;
         Sf[1] = half ? p1v + s1 : s1 + p1v;
