@@ -224,13 +224,16 @@ __device__ __forceinline__ void pt_sweep(const PrefillTopkArgs &a, PtShared &sh,
     shf[mt] = sh.shift[r];
     coll[mt] = sh.mode[r] == PT_COLLECT;
   }
-  // lane g < 4 writes the bitmap halves of row 4 mt + g when that row collects
+  // refinement sweeps: lane g < 4 writes the bitmap halves of row 4 mt + g
+  // when that row collects
   bool wbits[PT_MT];
 #pragma unroll
   for (int mt = 0; mt < PT_MT; ++mt) {
     const int rr = 4 * mt + (lane & 3);
     wbits[mt] = lane < 4 && KIND != SW_HIST0 && pt_open(sh, KIND, rr) && sh.mode[rr] == PT_COLLECT;
   }
+  // collect sweeps: lane L < 16 writes the bitmap half of row L for each tile
+  const bool wrow = lane < PT_R && KIND == SW_COLLECT_F && pt_open(sh, KIND, lane) && sh.mode[lane] == PT_COLLECT;
   const int shift = a.c.page_shift;
   const int32_t pmask = (1 << shift) - 1;
   const int64_t bt_row = (int64_t)b * a.c.max_pages;
@@ -288,6 +291,45 @@ __device__ __forceinline__ void pt_sweep(const PrefillTopkArgs &a, PtShared &sh,
       const v8h b0 = fp4x8_dequant((uint32_t)__float_as_int(cur.code[u][0]), s);
       const v8h b1 = fp4x8_dequant((uint32_t)__float_as_int(cur.code[u][1]), s);
       const int32_t e = et + m;
+      if constexpr (KIND == SW_COLLECT_F) {
+        float scv[PT_MT];
+        bool inrv[PT_MT];
+        uint64_t bmv[PT_MT];
+#pragma unroll
+        for (int mt = 0; mt < PT_MT; ++mt) {
+          v4f acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[mt][0], b0, (v4f){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[mt][1], b1, acc, 0, 0, 0);
+          float sc = 0.f;
+#pragma unroll
+          for (int h = 0; h < CSA2_HI; ++h) sc = fmaf(W[mt][h], fmaxf(acc[h], 0.f), sc);
+          const bool v = cur.eok[u] && e < vlim[mt];
+          const bool sel = v && sc > fhi[mt];
+          inrv[mt] = v && !sel && sc >= flo[mt];
+          bmv[mt] = __ballot(sel);
+          scv[mt] = sc;
+        }
+        if (et < vmax) {  // uniform
+          const int gl = lane & 3, ml = (lane >> 2) & 3;
+          uint64_t bsel = bmv[0];
+          bsel = ml == 1 ? bmv[1] : bsel;
+          bsel = ml == 2 ? bmv[2] : bsel;
+          bsel = ml == 3 ? bmv[3] : bsel;
+          if (wrow) ((uint16_t *)&sh.bits[lane][0])[et >> 4] = (uint16_t)(bsel >> (16 * gl));
+        }
+        if (__ballot(inrv[0] || inrv[1] || inrv[2] || inrv[3])) {  // uniform, and rare
+#pragma unroll
+          for (int mt = 0; mt < PT_MT; ++mt) {
+            if (inrv[mt]) {
+              const int r = 4 * mt + gq;
+              const uint64_t comp = ((uint64_t)score_key(scv[mt]) << 32) | (uint64_t)(~(uint32_t)e);
+              const uint32_t slot = atomicAdd((uint32_t *)&sh.cnt[r], 1u);
+              if (slot < PT_CAND) pt_cand(sh, r)[slot] = comp;
+            }
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        continue;
+      }
 #pragma unroll
       for (int mt = 0; mt < PT_MT; ++mt) {
         v4f acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[mt][0], b0, (v4f){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
