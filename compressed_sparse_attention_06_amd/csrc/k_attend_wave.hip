@@ -32,7 +32,10 @@
 //    groups and every address is a lane base plus a constant), and
 //    ds_read_b64_tr_b16 returns the B operand of the product (R with positions
 //    along K) for each block of 16 of its output channels;
-//  * O and the sum are rescaled only in chunks that raise some head's maximum.
+//  * O and the sum are rescaled only in chunks that raise some head's logit
+//    more than 2^4 above its reference maximum (the weights are then at most
+//    16, which fp16 holds exactly enough; the final normalisation divides by
+//    the sum taken against the same reference).
 // No workgroup barrier per unit: the two waves of a pair exchange their
 // partial S through LDS with a handshake of their own (a posted and an
 // acknowledged unit count per wave), so the four pairs run independently
@@ -46,6 +49,7 @@ namespace csa2 {
 #define PW_NT 512   // eight waves: four pairs
 #define PW_RP 264   // halfs per LDS row of a wave's R tile (256 + 8)
 #define PW_QP 520   // halfs per LDS row of the staged Q (512 + 8)
+#define PW_SLACK 4.0f  // log2 of the largest weight before the reference maximum moves
 
 struct PairShared {
   union {
@@ -124,15 +128,18 @@ __device__ __forceinline__ int32_t pw_window_row(int32_t p, int32_t kw, int32_t 
 
 // Rows of position p, channels cb .. cb + 63, of a tile of kind ty (uniform;
 // PW_NONE past the row's units): an entry, a window row, or nothing; three
-// loads in every case. wcodes / wscale: the request's window rows and row
-// scales (uniform). The masking of a position that is not a row (kind 0)
-// happens where the bytes are used: its entry scale word is taken as 0 (E2M1
-// has no NaN or infinity, so its codes dequantise to 0), its window bytes as
-// 0 and its row scale as 1.
-__device__ __forceinline__ void pw_fetch_rows(const AttendArgs &a, int ty, int32_t p, int cb, int32_t nent,
+// loads in every case. cbase / sbase: the cache's code and scale arrays at the
+// lane's channels; elim: the ids below it are visible entries with a page
+// slot in the block table (the row's entry count, capped by the table);
+// wcodes / wscale: the request's window rows and row scales (uniform). A
+// position that is not a row (kind 0) loads physical row 0 (or window row 0)
+// and is masked where the bytes are used: its entry scale word is taken as 0
+// (E2M1 has no NaN or infinity, so its codes dequantise to 0), its window
+// bytes as 0 and its row scale as 1.
+__device__ __forceinline__ void pw_fetch_rows(const AttendArgs &a, int ty, int32_t p, int cb, int32_t elim,
                                               int32_t id, int32_t page, int32_t kw, int32_t span,
-                                              const uint8_t *wcodes, const float *wscale, int32_t wf, int32_t wl,
-                                              const uint8_t *qrow, PwSlice &s) {
+                                              const uint8_t *cbase, const uint8_t *sbase, const uint8_t *wcodes,
+                                              const float *wscale, int32_t wf, int32_t wl, PwSlice &s) {
   if (ty == PW_WINDOW) {
     bool ok;
     const int32_t wr = pw_window_row(p, kw, span, wf, wl, ok);
@@ -143,17 +150,16 @@ __device__ __forceinline__ void pw_fetch_rows(const AttendArgs &a, int ty, int32
     s.w = *sp;
     s.kind = ok ? 2 : 0;
   } else {
-    // a position with nothing to load reads the row's query instead (32 KB,
-    // just read by this workgroup, so it is in the caches)
+    // cache rows number fewer than 2^31, so the row index fits 32 bits
     const int sh = a.c.page_shift;
-    const bool addr_ok = id >= 0 && (id >> sh) < a.c.max_pages && page >= 0 && page < a.c.num_pages;
-    const bool load = ty == PW_ENTRY && addr_ok;
-    const int64_t crow = load ? ((int64_t)page << sh) + (id & ((1 << sh) - 1)) : 0;
-    const uint8_t *cp = load ? a.c.kv_codes + crow * 256 + cb / 2 : qrow + cb / 2;
+    const bool ok = ty == PW_ENTRY && p < a.k && (uint32_t)id < (uint32_t)elim &&
+                    (uint32_t)page < (uint32_t)a.c.num_pages;
+    const uint32_t crow = ok ? ((uint32_t)page << sh) | ((uint32_t)id & ((1u << sh) - 1u)) : 0u;
+    const uint8_t *cp = cbase + (uint64_t)crow * 256u;
     s.c[0] = *(const v4i *)cp;
     s.c[1] = *(const v4i *)(cp + 16);
-    s.w = *(const uint32_t *)(load ? a.c.kv_scales + crow * 32 + cb / 16 : qrow + 256 + cb / 16);
-    s.kind = (ty == PW_ENTRY && addr_ok && p < a.k && id < nent) ? 1 : 0;
+    s.w = *(const uint32_t *)(sbase + (uint64_t)crow * 32u);
+    s.kind = ok ? 1 : 0;
   }
 }
 
@@ -227,10 +233,14 @@ __device__ __forceinline__ void pw_softmax_pv(const _Float16 *rt, const v4f *S, 
   float cm = fmax_nc(fmax_nc(fmax_nc(z[0][0], z[0][1]), fmax_nc(z[0][2], z[0][3])),
                      fmax_nc(fmax_nc(z[1][0], z[1][1]), fmax_nc(z[1][2], z[1][3])));
   cm = max_rows4(cm);
+  // m_run is the reference of the weights, not always the maximum: it moves
+  // (every head to its own maximum, with O and the sum rescaled) only when
+  // some head's logit exceeds it by more than PW_SLACK, so the weights stay
+  // below 2^PW_SLACK and most chunks skip the rescale
   const float m_new = fmax_nc(m_run, cm);
-  const float mref = (m_new == -INFINITY) ? 0.f : m_new;
-  if (__ballot(m_new > m_run) != 0) {  // uniform: some head's maximum rose
-    const float alpha = __builtin_amdgcn_exp2f(m_run - mref);  // 0 while m_run is -inf
+  if (__ballot(m_new > m_run + PW_SLACK) != 0) {  // uniform
+    const float mr = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - mr);  // 0 while m_run is -inf
     l_run *= alpha;
     float ah[4];
 #pragma unroll
@@ -242,6 +252,7 @@ __device__ __forceinline__ void pw_softmax_pv(const _Float16 *rt, const v4f *S, 
     }
     m_run = m_new;
   }
+  const float mref = (m_run == -INFINITY) ? 0.f : m_run;
   v8h pa;
   float ps = 0.f;
 #pragma unroll
@@ -256,14 +267,30 @@ __device__ __forceinline__ void pw_softmax_pv(const _Float16 *rt, const v4f *S, 
   l_run += ps;
   // block q (channels 16 q .. 16 q + 15 of the wave): lane (c, rq) of row group
   // g reads channels 16 q + 4 rq .. + 3 of rows 4 g + c and 16 + 4 g + c
+  // the reads run four blocks ahead of the products
+  v4s t0[4], t1[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    t0[q] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(rt + tr_base + 16 * q));
+    t1[q] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(rt + tr_base + 16 * PW_RP + 16 * q));
+  }
 #pragma unroll
   for (int q = 0; q < 16; ++q) {
-    const v4s t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(rt + tr_base + 16 * q));
-    const v4s t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(rt + tr_base + 16 * PW_RP + 16 * q));
-    const v4h h0 = __builtin_bit_cast(v4h, t0), h1 = __builtin_bit_cast(v4h, t1);
+    const v4h h0 = __builtin_bit_cast(v4h, t0[q & 3]), h1 = __builtin_bit_cast(v4h, t1[q & 3]);
     const v8h rb = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
     o[q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, rb, o[q], 0, 0, 0);
+    if (q + 4 < 16) {
+      t0[q & 3] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(rt + tr_base + 16 * (q + 4)));
+      t1[q & 3] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(rt + tr_base + 16 * PW_RP + 16 * (q + 4)));
+    }
   }
+  __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // the first four blocks' reads
+#pragma unroll
+  for (int q = 0; q < 12; ++q) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one product
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // the reads of block q + 4
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 }
 
 // The row ends in this workgroup: combine the four pairs' states (common
@@ -362,6 +389,7 @@ __global__ __launch_bounds__(PW_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   const int wave = tid >> 6, pair = wave >> 1, half = wave & 1;
   const int n = lane & 15, g = lane >> 4;
   const int cb = 256 * half + 64 * g;  // the lane's first channel
+  const uint8_t *cbase = a.c.kv_codes + cb / 2, *sbase = a.c.kv_scales + cb / 16;
   const int32_t first_row = (int32_t)(u_begin / U);
   const int32_t kw = seg_kw(a.k);
   const int32_t span = kw + (a.win_codes ? a.win_cap : 0);
@@ -398,13 +426,13 @@ __global__ __launch_bounds__(PW_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     auto fpage = [&](int32_t j, int t, int32_t id) {
       return pw_fetch_page(a, btab, j < j_end && tile0(j, t) < kw, id);
     };
-    auto fid = [&](int32_t j, int t) {
-      const bool use = j < j_end && tile0(j, t) < kw;
-      return pw_fetch_id(a, use ? irow : a.c.n_entries, use, tile0(j, t) + n);
-    };
+    // (a tile with no entries reads the row's first id)
+    auto fid = [&](int32_t j, int t) { return pw_fetch_id(a, irow, j < j_end && tile0(j, t) < kw, tile0(j, t) + n); };
     const uint8_t *qrow = (const uint8_t *)(a.q + (int64_t)row * CSA2_H * CSA2_D);
+    const int32_t elim = min(nent, a.c.max_pages << a.c.page_shift);
     auto frows = [&](int32_t j, int t, int32_t id, int32_t page, PwSlice &sl) {
-      pw_fetch_rows(a, tkind(j, t), tile0(j, t) + n, cb, nent, id, page, kw, span, wcodes, wscale, wf, wl, qrow, sl);
+      pw_fetch_rows(a, tkind(j, t), tile0(j, t) + n, cb, elim, id, page, kw, span, cbase, sbase, wcodes, wscale, wf,
+                    wl, sl);
     };
     // A = the set of unit j0; B.id = the ids of unit j0 + 1 (the set of unit
     // j0 - 1 would have carried them)
