@@ -5,7 +5,10 @@
 // scores) and "FP4 量化 + Bounded Replay" (FP4 indexer keys and queries);
 // block-causal visibility as for the other scoring kernels).
 //
-// A workgroup owns 16 query rows of one request and every entry they see.
+// A workgroup owns 16 query rows of one request and every entry they see;
+// its sixteen waves (four per SIMD, so at most 128 registers each) split the
+// entries, and the queries' operands and head weights wait in LDS between
+// sweeps rather than in registers.
 // Scores are recomputed on the matrix cores in each pass instead of being
 // stored; what a pass keeps is small and lives in LDS:
 //   pass 0   a 2048-bin histogram per row over a fixed monotone map of the
@@ -42,14 +45,14 @@ namespace csa2 {
 #define PT_R 16                        // query rows per workgroup
 #define PT_MT (PT_R / 4)               // M tiles: 4 rows x 4 heads each
 #define PT_WG_PER_CU 1                 // minimum waves per SIMD for the register budget
-#define PT_NT 512                      // threads (8 waves)
+#define PT_NT 1024                     // threads (16 waves: four per SIMD)
 #define PT_WAVES (PT_NT / 64)
 #define PT_BINS 2048
 #define PT_BIN_BITS 11
 #define PT_CAND 512                    // candidates per row in a collect pass
 #define PT_BITW (kPrefillTopkMaxCols / 32)
 #define PT_PAGES 2048
-#define PT_B 4                         // 16-entry tiles per wave batch (two in flight)
+#define PT_B 2                         // 16-entry tiles per wave batch (two batches in flight)
 #define PT_MAX_PASSES 12               // 1 histogram pass + at most 6 refinements + collect
 
 // fixed monotone map of pass 0: IEEE bits of 2^-12, 64 bins per octave
@@ -71,10 +74,21 @@ struct PtShared {
   uint64_t rlo[PT_R], rhi[PT_R];     // composite range still open
   float flo[PT_R], fhi[PT_R];        // the same range as score bounds (when fb)
   int32_t mode[PT_R], shift[PT_R], need[PT_R], vis[PT_R], cnt[PT_R], fb[PT_R];
+  v8h qa[PT_MT][2][64];              // each lane's A operands (dequantised queries)
+  float qw[PT_R][CSA2_HI];           // head weights of each row
 };
 
 __device__ __forceinline__ uint64_t *pt_cand(PtShared &sh, int r) {
   return (uint64_t *)&sh.hist[r >> 1][(r & 1) * (PT_BINS / 2)];
+}
+
+// the thread id through an opaque copy: indices and LDS addresses derived
+// from it are computed where they are used, not once for the whole kernel
+// and held (or spilled) across the passes
+__device__ __forceinline__ int pt_tid() {
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  return tid;
 }
 
 __device__ __forceinline__ int pt_bin0(float s) {
@@ -115,7 +129,7 @@ __device__ __forceinline__ uint32_t pt_wave_incl_scan(uint32_t v) { return wave_
 // 256 i + 4 j + c (i < 8, c < 4), read as conflict-free 16-byte loads.
 __device__ void pt_find_bin(const uint32_t *h, int half, uint32_t need, int *T, uint32_t *above,
                             uint32_t *cnt) {
-  const int lane = threadIdx.x & 63;
+  const int lane = pt_tid() & 63;
   uint32_t x[8][4];
   uint32_t seg[8];
 #pragma unroll
@@ -196,11 +210,22 @@ __device__ __forceinline__ bool pt_open(const PtShared &sh, int kind, int r) {
 // the histogram of its range. TILEPAGE: pages of >= 16 entries, so a
 // 16-entry tile lies in one page and its addresses are wave-uniform.
 template <int KIND, bool TILEPAGE>
-__device__ __forceinline__ void pt_sweep(const PrefillTopkArgs &a, PtShared &sh, int b,
-                                         const v8h (&A)[PT_MT][2], const float (&W)[PT_MT][4]) {
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+__device__ __forceinline__ void pt_sweep(const PrefillTopkArgs &a, PtShared &sh, int b) {
+  const int tid = pt_tid();
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int m = lane & 15, gq = lane >> 4;
+  // the queries' A operands and the head weights of the lane's result rows
+  // 4 mt + gq, from LDS for the sweep only (not held across the passes)
+  v8h A[PT_MT][2];
+  float W[PT_MT][CSA2_HI];
+#pragma unroll
+  for (int mt = 0; mt < PT_MT; ++mt) {
+    A[mt][0] = sh.qa[mt][0][lane];
+    A[mt][1] = sh.qa[mt][1][lane];
+#pragma unroll
+    for (int h = 0; h < CSA2_HI; ++h) W[mt][h] = sh.qw[4 * mt + gq][h];
+  }
   // per M tile: the lane's result row (4 mt + gq) and its pass parameters
   int32_t vlim[PT_MT];
   uint32_t inc[PT_MT];
@@ -377,7 +402,7 @@ __device__ __forceinline__ void pt_sweep(const PrefillTopkArgs &a, PtShared &sh,
 
 // After a histogram pass: the next state of row r (one wave).
 __device__ void pt_resolve_hist(PtShared &sh, int r) {
-  const int lane = threadIdx.x & 63;
+  const int lane = pt_tid() & 63;
   const int md = sh.mode[r];
   const uint32_t need = (uint32_t)sh.need[r];
   int T;
@@ -438,7 +463,7 @@ __device__ void pt_resolve_hist(PtShared &sh, int r) {
 // After a collect pass: rank the candidates by composite (descending) and
 // select the first `need`.
 __device__ void pt_resolve_collect(PtShared &sh, int r) {
-  const int lane = threadIdx.x & 63;
+  const int lane = pt_tid() & 63;
   const int n = min(sh.cnt[r], PT_CAND);
   const int need = sh.need[r];
   const uint64_t *cand = pt_cand(sh, r);
@@ -505,29 +530,28 @@ __global__ __launch_bounds__(PT_NT, PT_WG_PER_CU) void k_prefill_topk(PrefillTop
       sh.page[i] = i < a.c.max_pages ? a.c.block_table[(int64_t)b * a.c.max_pages + i] : -1;
   }
 
-  // A operands (rows 4 mt + m/4, head m%4) and the head weights of the
-  // lane's result rows 4 mt + gq
-  const int m = lane & 15, gq = lane >> 4;
-  v8h A[PT_MT][2];
-  float W[PT_MT][4];
+  // A operands (rows 4 mt + m/4, head m%4) of every lane, by wave 0, and
+  // the head weights of every row, into LDS
+  if (wave == 0) {
+    const int m = lane & 15, gq = lane >> 4;
 #pragma unroll
-  for (int mt = 0; mt < PT_MT; ++mt) {
-    const int ta = qb * PT_R + 4 * mt + (m >> 2), h = m & 3;
-    const int64_t row_a = (int64_t)b * a.nq + min(ta, a.nq - 1);
-    const v2f c = *(const v2f *)(a.qix_codes + (row_a * CSA2_HI + h) * 32 + 8 * gq);
-    const uint32_t sb = a.qix_scales[(row_a * CSA2_HI + h) * 4 + gq];
-    const _Float16 s = ta < a.nq ? (_Float16)e4m3_to_f32(sb) : (_Float16)0.f;
-    A[mt][0] = fp4x8_dequant((uint32_t)__float_as_int(c[0]), s);
-    A[mt][1] = fp4x8_dequant((uint32_t)__float_as_int(c[1]), s);
-    const int te = qb * PT_R + 4 * mt + gq;
+    for (int mt = 0; mt < PT_MT; ++mt) {
+      const int ta = qb * PT_R + 4 * mt + (m >> 2), h = m & 3;
+      const int64_t row_a = (int64_t)b * a.nq + min(ta, a.nq - 1);
+      const v2f c = *(const v2f *)(a.qix_codes + (row_a * CSA2_HI + h) * 32 + 8 * gq);
+      const uint32_t sb = a.qix_scales[(row_a * CSA2_HI + h) * 4 + gq];
+      const _Float16 s = ta < a.nq ? (_Float16)e4m3_to_f32(sb) : (_Float16)0.f;
+      sh.qa[mt][0][lane] = fp4x8_dequant((uint32_t)__float_as_int(c[0]), s);
+      sh.qa[mt][1][lane] = fp4x8_dequant((uint32_t)__float_as_int(c[1]), s);
+    }
+    const int te = qb * PT_R + (lane >> 2);
     const int64_t row_e = (int64_t)b * a.nq + min(te, a.nq - 1);
-#pragma unroll
-    for (int h2 = 0; h2 < CSA2_HI; ++h2) W[mt][h2] = a.w[row_e * CSA2_HI + h2];
+    sh.qw[lane >> 2][lane & 3] = a.w[row_e * CSA2_HI + (lane & 3)];
   }
   __syncthreads();
 
   if (any) {
-    pt_sweep<SW_HIST0, TILEPAGE>(a, sh, b, A, W);
+    pt_sweep<SW_HIST0, TILEPAGE>(a, sh, b);
     __syncthreads();
     for (int half = 0; half < 2 && 2 * wave < PT_R; ++half) {
       const int r = 2 * wave + half;
@@ -544,22 +568,23 @@ __global__ __launch_bounds__(PT_NT, PT_WG_PER_CU) void k_prefill_topk(PrefillTop
       general |= md == PT_HIST || (md == PT_COLLECT && !sh.fb[i]);
     }
     if (!open) break;  // uniform
+    const int ptid = pt_tid(), pwave = __builtin_amdgcn_readfirstlane(ptid >> 6);
     // refining pairs start from an empty histogram; collect rows from no candidates
-    for (int i = tid; i < (PT_R / 2) * PT_BINS / 4; i += PT_NT) {
+    for (int i = ptid; i < (PT_R / 2) * PT_BINS / 4; i += PT_NT) {
       const int p = i / (PT_BINS / 4);
       if (sh.mode[2 * p] == PT_HIST || sh.mode[2 * p + 1] == PT_HIST)
         ((v4i *)&sh.hist[0][0])[i] = (v4i){0, 0, 0, 0};
     }
-    if (tid < PT_R) sh.cnt[tid] = 0;
+    if (ptid < PT_R) sh.cnt[ptid] = 0;
     __syncthreads();
-    if (general) pt_sweep<SW_GENERAL, TILEPAGE>(a, sh, b, A, W);
-    else pt_sweep<SW_COLLECT_F, TILEPAGE>(a, sh, b, A, W);
+    if (general) pt_sweep<SW_GENERAL, TILEPAGE>(a, sh, b);
+    else pt_sweep<SW_COLLECT_F, TILEPAGE>(a, sh, b);
     __syncthreads();
-    if (2 * wave < PT_R) {
+    if (2 * pwave < PT_R) {
       // modes as the sweep saw them (resolving one row of the pair changes its mode)
-      const int md2[2] = {sh.mode[2 * wave], sh.mode[2 * wave + 1]};
+      const int md2[2] = {sh.mode[2 * pwave], sh.mode[2 * pwave + 1]};
       for (int half = 0; half < 2; ++half) {
-        const int r = 2 * wave + half;
+        const int r = 2 * pwave + half;
         if (md2[half] == PT_HIST) pt_resolve_hist(sh, r);
         else if (md2[half] == PT_COLLECT && md2[half ^ 1] != PT_HIST) pt_resolve_collect(sh, r);
       }
