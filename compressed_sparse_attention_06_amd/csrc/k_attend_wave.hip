@@ -59,7 +59,8 @@ struct PairShared {
       _Float16 lo[CSA2_H * PW_QP];
       float qexp[CSA2_H];
     } q;                                // Q of the row, staged once per row
-    float stage[4][CSA2_H][CSA2_D];     // row-end combine: each pair's scaled O
+    float stage[4][CSA2_H][kPartStride];  // row-end combine: each pair's scaled O (rows padded so that
+                                          // the four row groups of a store fall in different banks)
   };
   v4f sx[8][2][64];                     // each wave's partial S of its two tiles
   int sflag[8], sack[8];                // per wave: last unit whose partial S is posted / was read by the partner
@@ -405,55 +406,99 @@ __global__ __launch_bounds__(PW_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   __syncthreads();
   int useq = 0;  // units this wave has exchanged partial S for
 
-  for (int64_t x = u_begin; x < u_end;) {
-    const int32_t row = (int32_t)(x / U);
-    const int64_t xe = min(u_end, (int64_t)(row + 1) * U);
-    // units j0 .. j_end - 1 of the row fall to this workgroup
-    const int32_t j0 = (int32_t)(x - (int64_t)row * U), j_end = (int32_t)(xe - (int64_t)row * U);
-    x = xe;
-    const int b = row / a.nq;
-    const int32_t nent = a.c.n_entries[b];
-    const int32_t *irow = a.idx + (int64_t)row * a.k;
-    const int32_t *btab = a.c.block_table + (int64_t)b * a.c.max_pages;
-    const uint8_t *wcodes = a.win_codes ? a.win_codes + (int64_t)b * a.win_rows * CSA2_D : nullptr;
-    const float *wscale = a.win_row_scale ? a.win_row_scale + (int64_t)b * a.win_rows : nullptr;
-    int32_t wf, wl;
-    window_range(a, row, b, wf, wl);
-    // first position of tile t of unit j in the row's set (uniform), its kind,
-    // and the loads of the lane's position in it
-    auto tile0 = [&](int32_t j, int t) { return j * AS_UNIT + 32 * pair + 16 * t; };
-    auto tkind = [&](int32_t j, int t) { return j < j_end ? pw_tile_type(tile0(j, t), kw, span) : (int)PW_NONE; };
-    auto fpage = [&](int32_t j, int t, int32_t id) {
-      return pw_fetch_page(a, btab, j < j_end && tile0(j, t) < kw, id);
-    };
-    // (a tile with no entries reads the row's first id)
-    auto fid = [&](int32_t j, int t) { return pw_fetch_id(a, irow, j < j_end && tile0(j, t) < kw, tile0(j, t) + n); };
-    const uint8_t *qrow = (const uint8_t *)(a.q + (int64_t)row * CSA2_H * CSA2_D);
-    const int32_t elim = min(nent, a.c.max_pages << a.c.page_shift);
-    auto frows = [&](int32_t j, int t, int32_t id, int32_t page, PwSlice &sl) {
-      pw_fetch_rows(a, tkind(j, t), tile0(j, t) + n, cb, elim, id, page, kw, span, cbase, sbase, wcodes, wscale, wf,
-                    wl, sl);
-    };
-    // A = the set of unit j0; B.id = the ids of unit j0 + 1 (the set of unit
-    // j0 - 1 would have carried them)
-    PwSet A, B;
-    float qv[32];
-    if (tid < 256) load_q(a, row, qv);  // uniform per wave
-    {
-      int32_t id0[2], pg0[2];
-      id0[0] = fid(j0, 0);
-      id0[1] = fid(j0, 1);
-      B.id[0] = fid(j0 + 1, 0);
-      B.id[1] = fid(j0 + 1, 1);
-      A.id[0] = fid(j0 + 2, 0);
-      A.id[1] = fid(j0 + 2, 1);
-      pg0[0] = fpage(j0, 0, id0[0]);
-      pg0[1] = fpage(j0, 1, id0[1]);
-      A.pg[0] = fpage(j0 + 1, 0, B.id[0]);
-      A.pg[1] = fpage(j0 + 1, 1, B.id[1]);
-      frows(j0, 0, id0[0], pg0[0], A.t[0]);
-      frows(j0, 1, id0[1], pg0[1], A.t[1]);
+  // The fetch context of a row: its ids, block-table row, window rows and
+  // row scales, visible window range and entry bound; j_end: the end of its
+  // units in this workgroup's range.
+  struct PwRow {
+    const int32_t *irow, *btab;
+    const uint8_t *wcodes, *qrow;
+    const float *wscale;
+    int32_t wf, wl, elim, j_end;
+  };
+  auto row_ctx = [&](int32_t r) {
+    PwRow c;
+    const int bb = r / a.nq;
+    c.j_end = (int32_t)(min(u_end, (int64_t)(r + 1) * U) - (int64_t)r * U);
+    c.irow = a.idx + (int64_t)r * a.k;
+    c.btab = a.c.block_table + (int64_t)bb * a.c.max_pages;
+    c.wcodes = a.win_codes ? a.win_codes + (int64_t)bb * a.win_rows * CSA2_D : nullptr;
+    c.wscale = a.win_row_scale ? a.win_row_scale + (int64_t)bb * a.win_rows : nullptr;
+    window_range(a, r, bb, c.wf, c.wl);
+    c.qrow = (const uint8_t *)(a.q + (int64_t)r * CSA2_H * CSA2_D);
+    c.elim = min(a.c.n_entries[bb], a.c.max_pages << a.c.page_shift);
+    return c;
+  };
+  int32_t row = first_row;
+  int32_t j0 = (int32_t)(u_begin - (int64_t)row * U);
+  PwRow cur = row_ctx(row);
+  // The loads of the units of a row: unit j of the current row, or, for j
+  // at or past its end, unit j - j_end of the next row when `cross` (the
+  // next row's first units are fetched during this row's last ones, so that
+  // its prologue does not wait for the id -> page -> row chain).
+  PwRow nxt = cur;
+  bool has_next = false, cross = false;
+  // the next row in this workgroup's range, if any; its first three units
+  // are entry tiles when kw >= 3 units (else they are fetched after the row)
+  auto plan_next = [&]() {
+    has_next = (int64_t)(row + 1) * U < u_end;
+    cross = has_next && kw >= 3 * AS_UNIT;
+    if (has_next) {
+      const int bn = (row + 1) / a.nq, bc = row / a.nq;
+      nxt.j_end = (int32_t)(min(u_end, (int64_t)(row + 2) * U) - (int64_t)(row + 1) * U);
+      nxt.irow = a.idx + (int64_t)(row + 1) * a.k;
+      nxt.btab = a.c.block_table + (int64_t)bn * a.c.max_pages;
+      nxt.elim = bn == bc ? cur.elim : min(a.c.n_entries[bn], a.c.max_pages << a.c.page_shift);
     }
+  };
+  auto tinfo = [&](int32_t j, int t, bool &nx, int32_t &p) {
+    nx = j >= cur.j_end;
+    const int32_t jj = nx ? j - cur.j_end : j;
+    p = jj * AS_UNIT + 32 * pair + 16 * t;  // first position of the tile in its row's set (uniform)
+    const bool in = nx ? (cross && jj < nxt.j_end) : true;
+    return in ? pw_tile_type(p, kw, span) : (int)PW_NONE;
+  };
+  auto fid = [&](int32_t j, int t) {
+    bool nx;
+    int32_t p;
+    const int ty = tinfo(j, t, nx, p);
+    return pw_fetch_id(a, nx ? nxt.irow : cur.irow, ty == PW_ENTRY, p + n);  // no entry: the row's first id
+  };
+  auto fpage = [&](int32_t j, int t, int32_t id) {
+    bool nx;
+    int32_t p;
+    const int ty = tinfo(j, t, nx, p);
+    return pw_fetch_page(a, nx ? nxt.btab : cur.btab, ty == PW_ENTRY, id);
+  };
+  // (the next row's tiles fetched here are all entries, so its window fields are not needed)
+  auto frows = [&](int32_t j, int t, int32_t id, int32_t page, PwSlice &sl) {
+    bool nx;
+    int32_t p;
+    const int ty = tinfo(j, t, nx, p);
+    pw_fetch_rows(a, ty, p + n, cb, nx ? nxt.elim : cur.elim, id, page, kw, span, cbase, sbase, cur.wcodes,
+                  cur.wscale, cur.wf, cur.wl, sl);
+  };
+  // the id, page and row loads of unit j0 into A, the ids of j0 + 1 into B
+  auto prologue = [&](PwSet &A, PwSet &B) {
+    int32_t id0[2], pg0[2];
+    id0[0] = fid(j0, 0);
+    id0[1] = fid(j0, 1);
+    B.id[0] = fid(j0 + 1, 0);
+    B.id[1] = fid(j0 + 1, 1);
+    A.id[0] = fid(j0 + 2, 0);
+    A.id[1] = fid(j0 + 2, 1);
+    pg0[0] = fpage(j0, 0, id0[0]);
+    pg0[1] = fpage(j0, 1, id0[1]);
+    A.pg[0] = fpage(j0 + 1, 0, B.id[0]);
+    A.pg[1] = fpage(j0 + 1, 1, B.id[1]);
+    frows(j0, 0, id0[0], pg0[0], A.t[0]);
+    frows(j0, 1, id0[1], pg0[1], A.t[1]);
+  };
+  PwSet A, B;
+  float qv[32];
+  if (tid < 256) load_q(a, row, qv);  // uniform per wave
+  plan_next();
+  prologue(A, B);
+  for (;;) {
     // Q of the row (waves 0-3 convert): per-head power-of-two normalisation,
     // fp16 hi + lo halves
     if (tid < 256) {
@@ -502,6 +547,14 @@ __global__ __launch_bounds__(PW_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     // computes.
     auto unit = [&](int32_t j, PwSet &X, PwSet &Y) {
       const int32_t p0 = j * AS_UNIT + 32 * pair;  // first position of the pair's chunk
+      // issue priority to the wave that lags the other wave on its SIMD (wave
+      // ^ 4): by default the older wave wins every tie, so pairs 2 and 3 would
+      // fall behind and pairs 0 and 1 wait for them at the row's end
+      {
+        const int sib = __hip_atomic_load(&sh.sflag[wave ^ 4], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (__builtin_amdgcn_readfirstlane(useq < sib ? 1 : 0)) __builtin_amdgcn_s_setprio(1);
+        else __builtin_amdgcn_s_setprio(0);
+      }
       const int ty0 = pw_tile_type(p0, kw, span), ty1 = pw_tile_type(p0 + 16, kw, span);
       const bool live = p0 < span;  // uniform per pair: the chunk holds some position of the row's set
       // page words and ids first: the rows of j + 1, issued at the start of
@@ -520,8 +573,10 @@ __global__ __launch_bounds__(PW_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
       v4i tail0[2], tail1[2];
       {
         bool ok;
-        pw_window_tail(ty0 == PW_WINDOW, wcodes, qrow, pw_window_row(p0 + n, kw, span, wf, wl, ok), cb, tail0);
-        pw_window_tail(ty1 == PW_WINDOW, wcodes, qrow, pw_window_row(p0 + 16 + n, kw, span, wf, wl, ok), cb, tail1);
+        pw_window_tail(ty0 == PW_WINDOW, cur.wcodes, cur.qrow, pw_window_row(p0 + n, kw, span, cur.wf, cur.wl, ok), cb,
+                       tail0);
+        pw_window_tail(ty1 == PW_WINDOW, cur.wcodes, cur.qrow, pw_window_row(p0 + 16 + n, kw, span, cur.wf, cur.wl, ok),
+                       cb, tail1);
       }
       v4f s0, s1;  // partial S of each tile over the wave's channels (hi and lo products)
       float rs[2][4];
@@ -565,11 +620,29 @@ __global__ __launch_bounds__(PW_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     // the loads of unit j0 complete before the loop, so that the wait counts at
     // the loop head are those of the loop's own issue order on both entries
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    for (int32_t j = j0; j < j_end; j += 2) {
+    for (int32_t j = j0; j < cur.j_end; j += 2) {
       unit(j, A, B);
-      if (j + 1 < j_end) unit(j + 1, B, A);
+      if (j + 1 < cur.j_end) unit(j + 1, B, A);
     }
+    if (has_next && tid < 256) load_q(a, row + 1, qv);  // in flight during the row's finish
     pw_finish(a, s, sh, wg, row, first_row, u_begin, u_end, m_run, l_run, o);
+    if (!has_next) break;
+    // the set of the next row's first unit is the one the last unit filled:
+    // A after an even number of units, else B
+    const bool odd = ((cur.j_end - j0) & 1) != 0, fetched = cross;
+    ++row;
+    j0 = 0;
+    cur = row_ctx(row);
+    plan_next();
+    if (fetched) {
+      if (odd) {
+        const PwSet t = A;
+        A = B;
+        B = t;
+      }
+    } else {
+      prologue(A, B);
+    }
   }
 }
 

@@ -398,9 +398,10 @@ def test_sparse_attend_poisoned_unused_bytes(attend_kernel):
 # k rounded up to 16) in units of 128 positions, shared over at most 256
 # workgroups. These cases cover k below, at and off a multiple of 16, sets of
 # one unit, rows cut between workgroups at many offsets (T > 256 units, with
-# 2..20 units per workgroup), several query rows per request with their own
-# causal windows, no window, and rows cut into more partials (33) than the
-# merge loads in one batch.
+# 2..20 units per workgroup), workgroups that run through several rows with
+# odd and even unit counts per row, several query rows per request with their
+# own causal windows, no window, and rows cut into more partials (33) than
+# the merge loads in one batch.
 UNIT_CASES = [
     dict(contexts=[4 * 300, 4 * 40], k=1, nq=1, win=True),                       # U = 2
     dict(contexts=[4 * 300], k=13, nq=1, win=False),                              # one unit, tail lanes empty
@@ -412,12 +413,14 @@ UNIT_CASES = [
     dict(contexts=[4 * 5000, 4 * 4500, 4 * 6000], k=4096, nq=1, win=True),        # the merge takes two batches
     dict(contexts=[4 * 2200] * 16, k=2048, nq=1, win=True),                       # 9 workgroups per row
     dict(contexts=[4 * 2200] * 40, k=2048, nq=1, win=True),                       # 6 per row, 240 in all
+    dict(contexts=[4 * 1500] * 6, k=512, nq=60, win=False, prefill=True),         # 360 rows x 4 units
+    dict(contexts=[4 * 1500] * 4, k=640, nq=40, win=True, prefill=True),          # 160 rows x 6 units
 ]
 
 
 @pytest.mark.parametrize("case", UNIT_CASES, ids=["k1", "k13_nowin", "k300", "nq3_prefill", "b30_k2048",
                                                  "nq50_k2048", "k4096_b1", "k4096_b3", "b16_k2048",
-                                                 "b40_k2048"])
+                                                 "b40_k2048", "nq60_k512_nowin", "nq40_k640"])
 def test_sparse_attend_unit_geometry(case, attend_kernel):
     _log(f"sparse_attend geometry {case}")
     wl = make_small_decode(contexts=case["contexts"], layers="F", k=case["k"], nq=case["nq"],
