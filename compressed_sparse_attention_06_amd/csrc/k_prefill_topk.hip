@@ -74,6 +74,7 @@ struct PtShared {
   uint64_t rlo[PT_R], rhi[PT_R];     // composite range still open
   float flo[PT_R], fhi[PT_R];        // the same range as score bounds (when fb)
   int32_t mode[PT_R], shift[PT_R], need[PT_R], vis[PT_R], cnt[PT_R], fb[PT_R];
+  int32_t next;                      // the next batch of a sweep (entries), taken by the waves in turn
   v8h qa[PT_MT][2][64];              // each lane's A operands (dequantised queries)
   float qw[PT_R][CSA2_HI];           // head weights of each row
 };
@@ -297,15 +298,22 @@ __device__ __forceinline__ void pt_sweep(const PrefillTopkArgs &a, PtShared &sh,
       }
     }
   };
-  constexpr int32_t kStride = PT_WAVES * 16 * PT_B;  // entries per workgroup step
+  // batches of 16 PT_B entries go to the waves as they ask (a wave that gets
+  // fewer issue slots takes fewer), each wave holding two taken ahead
+  auto take = [&]() {
+    int32_t v = 0;
+    if (lane == 0) v = atomicAdd(&sh.next, 16 * PT_B);
+    return __builtin_amdgcn_readfirstlane(v);
+  };
   Batch cur, nxt;
-  int32_t base = wave * (16 * PT_B);
+  int32_t base = take(), nb = take();
   load(base, cur);
-  for (; base < vmax; base += kStride) {
+  while (base < vmax) {
     // the next batch's loads are in flight while this one is scored; past
     // the end they read row 0 and are dropped (unconditional, so the waits
     // for this batch count the next batch's loads as still outstanding)
-    load(base + kStride, nxt);
+    load(nb, nxt);
+    const int32_t nnb = take();
     __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of this batch's work
     // branch-free over the batch: tiles past the row ends or on missing pages
     // are masked per lane (their loads read row 0)
@@ -397,6 +405,8 @@ __device__ __forceinline__ void pt_sweep(const PrefillTopkArgs &a, PtShared &sh,
       __builtin_amdgcn_sched_barrier(0);  // one tile at a time: bounded register use
     }
     cur = nxt;
+    base = nb;
+    nb = nnb;
   }
 }
 
@@ -511,6 +521,7 @@ __global__ __launch_bounds__(PT_NT, PT_WG_PER_CU) void k_prefill_topk(PrefillTop
     sh.shift[tid] = 0;
     sh.cnt[tid] = 0;
   }
+  if (tid == 0) sh.next = 0;
   {
     v4i z = {0, 0, 0, 0};
     for (int i = tid; i < PT_R * PT_BITW / 4; i += PT_NT) ((v4i *)&sh.bits[0][0])[i] = z;
@@ -576,6 +587,7 @@ __global__ __launch_bounds__(PT_NT, PT_WG_PER_CU) void k_prefill_topk(PrefillTop
         ((v4i *)&sh.hist[0][0])[i] = (v4i){0, 0, 0, 0};
     }
     if (ptid < PT_R) sh.cnt[ptid] = 0;
+    if (ptid == 0) sh.next = 0;
     __syncthreads();
     if (general) pt_sweep<SW_GENERAL, TILEPAGE>(a, sh, b);
     else pt_sweep<SW_COLLECT_F, TILEPAGE>(a, sh, b);
