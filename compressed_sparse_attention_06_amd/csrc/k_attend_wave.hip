@@ -49,6 +49,7 @@ namespace csa2 {
 #define PW_NT 512   // eight waves: four pairs
 #define PW_RP 264   // halfs per LDS row of a wave's R tile (256 + 8)
 #define PW_QP 520   // halfs per LDS row of the staged Q (512 + 8)
+#define PW_SP 260   // floats per row of a wave's staged O at the row's end (256 + 4)
 #define PW_SLACK 4.0f  // log2 of the largest weight before the reference maximum moves
 
 struct PairShared {
@@ -59,8 +60,7 @@ struct PairShared {
       _Float16 lo[CSA2_H * PW_QP];
       float qexp[CSA2_H];
     } q;                                // Q of the row, staged once per row
-    float stage[4][CSA2_H][kPartStride];  // row-end combine: each pair's scaled O (rows padded so that
-                                          // the four row groups of a store fall in different banks)
+    float stg[8][32 * PW_RP / 2];       // row end: each wave's O [16 heads][PW_SP], in its own R tile's storage
   };
   v4f sx[8][2][64];                     // each wave's partial S of its two tiles
   int sflag[8], sack[8];                // per wave: last unit whose partial S is posted / was read by the partner
@@ -297,6 +297,9 @@ __device__ __forceinline__ void pw_softmax_pv(const _Float16 *rt, const v4f *S, 
 // The row ends in this workgroup: combine the four pairs' states (common
 // reference: the largest of their maxima), then write the row whole
 // (normalised, with its lse) or leave its partial in the workgroup's slot.
+// Each wave stages its O in its own R tile's storage, which no other wave
+// touches, so one barrier precedes the combine and one follows it (before
+// the next row's rows overwrite the tiles).
 __device__ __forceinline__ void pw_finish(const AttendArgs &a, const SegArgs &s, PairShared &sh, int wg,
                                           int32_t row, int32_t first_row, int64_t u_begin, int64_t u_end,
                                           float m_run, float l_run, const v4f *o) {
@@ -311,19 +314,12 @@ __device__ __forceinline__ void pw_finish(const AttendArgs &a, const SegArgs &s,
     sh.wm[pair][n] = m_run;
     sh.wl[pair][n] = l_tot;
   }
-  __syncthreads();  // every wave is past its last unit: the R tiles are free
-  float fo[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int h = 4 * g + i;
-    const float M = fmax_nc(fmax_nc(sh.wm[0][h], sh.wm[1][h]), fmax_nc(sh.wm[2][h], sh.wm[3][h]));
-    const float mr = (M == -INFINITY) ? 0.f : M;
-    fo[i] = __builtin_amdgcn_exp2f(sh.wm[pair][h] - mr);  // 0 for a pair with no row
-  }
+  asm volatile("" ::: "memory");  // after the wave's last reads of its R tile
+  float *st = sh.stg[wave];
 #pragma unroll
   for (int q = 0; q < 16; ++q) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sh.stage[pair][4 * g + i][256 * half + 16 * q + n] = o[q][i] * fo[i];
+    for (int i = 0; i < 4; ++i) st[(4 * g + i) * PW_SP + 16 * q + n] = o[q][i];
   }
   __syncthreads();
   const int64_t r0 = (int64_t)row * s.U;
@@ -331,18 +327,20 @@ __device__ __forceinline__ void pw_finish(const AttendArgs &a, const SegArgs &s,
   const int slot = (row == first_row) ? 0 : 1;
   float *part = a.part + ((int64_t)wg * 2 + slot) * CSA2_H * kPartStride;
   // 16 x 512 outputs as 2048 float4, four per thread, summed over the pairs
+  // (pair p's channel c is in wave 2 p + c / 256)
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) {
-    const int v = tid + PW_NT * jj, h = v >> 7, c = (v & 127) * 4;
-    const v4f x = (*(const v4f *)&sh.stage[0][h][c] + *(const v4f *)&sh.stage[1][h][c]) +
-                  (*(const v4f *)&sh.stage[2][h][c] + *(const v4f *)&sh.stage[3][h][c]);
+    const int v = tid + PW_NT * jj, h = v >> 7, c = (v & 127) * 4, hf = c >> 8, cc = c & 255;
+    const float M = fmax_nc(fmax_nc(sh.wm[0][h], sh.wm[1][h]), fmax_nc(sh.wm[2][h], sh.wm[3][h]));
+    const float mr = (M == -INFINITY) ? 0.f : M;
+    float f[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) f[p] = __builtin_amdgcn_exp2f(sh.wm[p][h] - mr);  // 0 for a pair with no row
+    const v4f o0 = *(const v4f *)&sh.stg[hf][h * PW_SP + cc], o1 = *(const v4f *)&sh.stg[2 + hf][h * PW_SP + cc];
+    const v4f o2 = *(const v4f *)&sh.stg[4 + hf][h * PW_SP + cc], o3 = *(const v4f *)&sh.stg[6 + hf][h * PW_SP + cc];
+    const v4f x = (o0 * f[0] + o1 * f[1]) + (o2 * f[2] + o3 * f[3]);
     if (whole) {
-      const float M = fmax_nc(fmax_nc(sh.wm[0][h], sh.wm[1][h]), fmax_nc(sh.wm[2][h], sh.wm[3][h]));
-      const float mr = (M == -INFINITY) ? 0.f : M;
-      const float L = (sh.wl[0][h] * __builtin_amdgcn_exp2f(sh.wm[0][h] - mr) +
-                       sh.wl[1][h] * __builtin_amdgcn_exp2f(sh.wm[1][h] - mr)) +
-                      (sh.wl[2][h] * __builtin_amdgcn_exp2f(sh.wm[2][h] - mr) +
-                       sh.wl[3][h] * __builtin_amdgcn_exp2f(sh.wm[3][h] - mr));
+      const float L = (sh.wl[0][h] * f[0] + sh.wl[1][h] * f[1]) + (sh.wl[2][h] * f[2] + sh.wl[3][h] * f[3]);
       const float inv = (L > 0.f) ? 1.f / L : 0.f;
       *(v4f *)&s.out[((int64_t)row * CSA2_H + h) * CSA2_D + c] = x * inv;
     } else {
@@ -364,7 +362,7 @@ __device__ __forceinline__ void pw_finish(const AttendArgs &a, const SegArgs &s,
       part[(int64_t)h * kPartStride + CSA2_D + 1] = L;
     }
   }
-  __syncthreads();  // the staging area and the pair states are read before the next row
+  __syncthreads();  // the staged O and the pair states are read before the next row
 }
 
 // Pair-level handshake through LDS (the two waves of a pair run on
