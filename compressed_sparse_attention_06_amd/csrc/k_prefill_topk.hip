@@ -47,6 +47,7 @@ namespace csa2 {
 #define PT_WG_PER_CU 1                 // minimum waves per SIMD for the register budget
 #define PT_NT 1024                     // threads (16 waves: four per SIMD)
 #define PT_WAVES (PT_NT / 64)
+static_assert(PT_WAVES >= PT_R, "one wave per row in the resolves");
 #define PT_BINS 2048
 #define PT_BIN_BITS 11
 #define PT_CAND 512                    // candidates per row in a collect pass
@@ -470,28 +471,39 @@ __device__ void pt_resolve_hist(PtShared &sh, int r) {
   }
 }
 
-// After a collect pass: rank the candidates by composite (descending) and
-// select the first `need`.
+// After a collect pass: select the `need` largest candidates (composites are
+// unique, so exactly those at or above the need-th largest). The need-th
+// largest is found bit by bit from the top (radix selection): every
+// candidate lies in the row's range [rlo, rhi], so the bits above the
+// highest bit where rlo and rhi differ are common; at each lower bit the
+// count of candidates in the upper half of what is left decides that bit.
 __device__ void pt_resolve_collect(PtShared &sh, int r) {
   const int lane = pt_tid() & 63;
   const int n = min(sh.cnt[r], PT_CAND);
-  const int need = sh.need[r];
+  const uint32_t need = (uint32_t)sh.need[r];
   const uint64_t *cand = pt_cand(sh, r);
+  const int kn = (n + 63) >> 6;  // candidate slots in use per lane (uniform)
   uint64_t mine[PT_CAND / 64];
-  int rank[PT_CAND / 64];
+#pragma unroll
+  for (int k = 0; k < PT_CAND / 64; ++k) mine[k] = lane + 64 * k < n ? cand[lane + 64 * k] : 0ull;
+  const uint64_t rlo = sh.rlo[r], rhi = sh.rhi[r];
+  const uint64_t d = rlo ^ rhi;
+  const int top = d ? 63 - __clzll((long long)d) : -1;
+  uint64_t P = top >= 0 ? rlo & ~((2ull << top) - 1ull) : rlo;  // the common bits (none when top = 63)
+  uint32_t above = 0;  // candidates above what is left
+  for (int bt = top; bt >= 0; --bt) {
+    const uint64_t hi = (P >> bt) | 1ull;
+    uint32_t c = 0;
+#pragma unroll
+    for (int k = 0; k < PT_CAND / 64; ++k) {
+      if (k < kn) c += (uint32_t)__popcll(__ballot(lane + 64 * k < n && (mine[k] >> bt) == hi));
+    }
+    if (above + c >= need) P |= 1ull << bt;
+    else above += c;
+  }
 #pragma unroll
   for (int k = 0; k < PT_CAND / 64; ++k) {
-    mine[k] = lane + 64 * k < n ? cand[lane + 64 * k] : ~0ull;
-    rank[k] = 0;
-  }
-  for (int j = 0; j < n; ++j) {
-    const uint64_t cj = cand[j];
-#pragma unroll
-    for (int k = 0; k < PT_CAND / 64; ++k) rank[k] += cj > mine[k] ? 1 : 0;
-  }
-#pragma unroll
-  for (int k = 0; k < PT_CAND / 64; ++k) {
-    if (lane + 64 * k < n && rank[k] < need) {
+    if (lane + 64 * k < n && need > 0 && mine[k] >= P) {
       const uint32_t e = ~(uint32_t)mine[k];
       atomicOr(&sh.bits[r][e >> 5], 1u << (e & 31));
     }
@@ -564,10 +576,7 @@ __global__ __launch_bounds__(PT_NT, PT_WG_PER_CU) void k_prefill_topk(PrefillTop
   if (any) {
     pt_sweep<SW_HIST0, TILEPAGE>(a, sh, b);
     __syncthreads();
-    for (int half = 0; half < 2 && 2 * wave < PT_R; ++half) {
-      const int r = 2 * wave + half;
-      if (sh.mode[r] == PT_HIST0) pt_resolve_hist(sh, r);
-    }
+    if (wave < PT_R && sh.mode[wave] == PT_HIST0) pt_resolve_hist(sh, wave);  // one row per wave
     __syncthreads();
   }
   for (int pass = 1; pass < PT_MAX_PASSES; ++pass) {
@@ -592,21 +601,17 @@ __global__ __launch_bounds__(PT_NT, PT_WG_PER_CU) void k_prefill_topk(PrefillTop
     if (general) pt_sweep<SW_GENERAL, TILEPAGE>(a, sh, b);
     else pt_sweep<SW_COLLECT_F, TILEPAGE>(a, sh, b);
     __syncthreads();
-    if (2 * pwave < PT_R) {
-      // modes as the sweep saw them (resolving one row of the pair changes its mode)
-      const int md2[2] = {sh.mode[2 * pwave], sh.mode[2 * pwave + 1]};
-      for (int half = 0; half < 2; ++half) {
-        const int r = 2 * pwave + half;
-        if (md2[half] == PT_HIST) pt_resolve_hist(sh, r);
-        else if (md2[half] == PT_COLLECT && md2[half ^ 1] != PT_HIST) pt_resolve_collect(sh, r);
-      }
-    }
+    // one row per wave; the modes as the sweep saw them are read before any
+    // row's resolve changes its own
+    const int md = pwave < PT_R ? sh.mode[pwave] : PT_DONE, mdo = pwave < PT_R ? sh.mode[pwave ^ 1] : PT_DONE;
+    __syncthreads();
+    if (md == PT_HIST) pt_resolve_hist(sh, pwave);
+    else if (md == PT_COLLECT && mdo != PT_HIST) pt_resolve_collect(sh, pwave);
     __syncthreads();
   }
 
-  // ascending ids of each row, then -1 pads (one wave per row pair)
-  for (int half = 0; half < 2 && 2 * wave < PT_R; ++half) {
-    const int r = 2 * wave + half;
+  // ascending ids of each row, then -1 pads (one wave per row)
+  for (int r = wave; r < PT_R; r += PT_WAVES) {
     const int t = qb * PT_R + r;
     if (t >= a.nq) continue;
     int32_t *out = a.idx_out + ((int64_t)b * a.nq + t) * K;
