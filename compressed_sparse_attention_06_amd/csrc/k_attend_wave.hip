@@ -294,6 +294,21 @@ __device__ __forceinline__ void pw_softmax_pv(const _Float16 *rt, const v4f *S, 
   __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 }
 
+// Q of query row r: this thread's 16 fp32 values (head tid / 32, channels
+// 16 (tid % 32) + [0, 16)).
+__device__ __forceinline__ void pw_load_q16(const AttendArgs &a, int32_t r, float *qv) {
+  const int tid = threadIdx.x;
+  const float *src = a.q + ((int64_t)r * CSA2_H + (tid >> 5)) * CSA2_D + (tid & 31) * 16;
+#pragma unroll
+  for (int i = 0; i < 16; i += 4) {
+    const v4f x = *(const v4f *)(src + i);
+    qv[i] = x[0];
+    qv[i + 1] = x[1];
+    qv[i + 2] = x[2];
+    qv[i + 3] = x[3];
+  }
+}
+
 // The row ends in this workgroup: combine the four pairs' states (common
 // reference: the largest of their maxima), then write the row whole
 // (normalised, with its lse) or leave its partial in the workgroup's slot.
@@ -492,24 +507,26 @@ __global__ __launch_bounds__(PW_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     frows(j0, 1, id0[1], pg0[1], A.t[1]);
   };
   PwSet A, B;
-  float qv[32];
-  if (tid < 256) load_q(a, row, qv);  // uniform per wave
+  float qv[16];
+  pw_load_q16(a, row, qv);
   plan_next();
   prologue(A, B);
   for (;;) {
-    // Q of the row (waves 0-3 convert): per-head power-of-two normalisation,
-    // fp16 hi + lo halves
-    if (tid < 256) {
-      const int h = tid >> 4;
+    // Q of the row (all eight waves convert, 32 threads per head): per-head
+    // power-of-two normalisation, fp16 hi + lo halves
+    {
+      const int h = tid >> 5, part = tid & 31;
       float mx = 0.f;
 #pragma unroll
-      for (int i = 0; i < 32; ++i) mx = fmaxf(mx, fabsf(qv[i]));
-      mx = row16_max(mx);
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fabsf(qv[i]));
+      mx = row16_max(mx);  // then across the two rows of 16 lanes that hold the head
+      const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmax_nc(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
       int e = 0;
       if (mx > 0.f) frexpf(mx, &e);
       const float sc = ldexpf(1.f, -e);
 #pragma unroll
-      for (int i = 0; i < 32; i += 8) {
+      for (int i = 0; i < 16; i += 8) {
         v8h hv, lv;
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) {
@@ -518,10 +535,10 @@ __global__ __launch_bounds__(PW_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
           hv[jj] = hi;
           lv[jj] = (_Float16)(xq - (float)hi);
         }
-        *(v8h *)&sh.q.hi[h * PW_QP + (tid & 15) * 32 + i] = hv;
-        *(v8h *)&sh.q.lo[h * PW_QP + (tid & 15) * 32 + i] = lv;
+        *(v8h *)&sh.q.hi[h * PW_QP + part * 16 + i] = hv;
+        *(v8h *)&sh.q.lo[h * PW_QP + part * 16 + i] = lv;
       }
-      if ((tid & 15) == 0) sh.q.qexp[h] = (float)e;
+      if (part == 0) sh.q.qexp[h] = (float)e;
     }
     __syncthreads();
     const float qs = ldexpf(a.sm_scale * 1.4426950408889634f, (int)sh.q.qexp[n]);
@@ -622,7 +639,7 @@ __global__ __launch_bounds__(PW_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
       unit(j, A, B);
       if (j + 1 < cur.j_end) unit(j + 1, B, A);
     }
-    if (has_next && tid < 256) load_q(a, row + 1, qv);  // in flight during the row's finish
+    if (has_next) pw_load_q16(a, row + 1, qv);  // in flight during the row's finish
     pw_finish(a, s, sh, wg, row, first_row, u_begin, u_end, m_run, l_run, o);
     if (!has_next) break;
     // the set of the next row's first unit is the one the last unit filled:
