@@ -53,7 +53,7 @@ static_assert(PT_WAVES >= PT_R, "one wave per row in the resolves");
 #define PT_CAND 512                    // candidates per row in a collect pass
 #define PT_BITW (kPrefillTopkMaxCols / 32)
 #define PT_PAGES 2048
-#define PT_B 2                         // 16-entry tiles per wave batch (two batches in flight)
+#define PT_B 4                         // 16-entry tiles per batch (two batches in flight per wave)
 #define PT_MAX_PASSES 12               // 1 histogram pass + at most 6 refinements + collect
 
 // fixed monotone map of pass 0: IEEE bits of 2^-12, 64 bins per octave
