@@ -319,13 +319,14 @@ int initial_attend_kernel() {
 std::atomic<int> g_attend_kernel{initial_attend_kernel()};
 
 // auto: the paired-wave kernel pays more per row (Q staging, the combine of
-// four pairs) and less per unit, so it is taken where every workgroup has a
-// long range of units (the prefill chunk: 272 per workgroup; decode batches:
-// one to five)
+// four pairs) and less per unit, so it is taken where a workgroup takes at
+// least three units (measured: the prefill chunk, 272 per workgroup; the
+// ragged stack and the speculative step, 4-5; even at the 128K decode step's
+// 3; the eight-wave kernel is faster with one unit per workgroup, as at 1M)
 bool use_pair_kernel(const WsLayout &L) {
   const int k = g_attend_kernel.load(std::memory_order_relaxed);
   if (k != CSA2_ATTEND_AUTO) return k == CSA2_ATTEND_PAIR;
-  return (L.att_T + L.att_G - 1) / L.att_G >= 16;
+  return (L.att_T + L.att_G - 1) / L.att_G >= 3;
 }
 
 csa2_status run_attend(const WsLayout &L, char *ws, const csa2_cache *cache, const int32_t *idx,

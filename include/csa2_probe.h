@@ -27,8 +27,8 @@ csa2_status csa2_stream_read(const void *p, size_t n_bytes, uint32_t *sink, int3
  * csa2_layer_step, for the calls that follow (process-wide; both kernels give
  * the same results to rounding and use the same workspace):
  *   CSA2_ATTEND_AUTO (0)  by the work per workgroup: the paired-wave kernel
- *                         when each workgroup takes at least 16 units of 128
- *                         positions, the eight-wave kernel otherwise;
+ *                         when the busiest workgroup takes at least 3 units of
+ *                         128 positions, the eight-wave kernel otherwise;
  *   CSA2_ATTEND_SEG  (1)  the eight-wave kernel (each unit's rows shared by
  *                         eight waves through LDS);
  *   CSA2_ATTEND_PAIR (2)  the paired-wave kernel (each pair of waves its own
