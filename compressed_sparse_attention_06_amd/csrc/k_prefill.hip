@@ -73,7 +73,7 @@ __global__ __launch_bounds__(256) void k_prefill_score(ScoreArgs a, int32_t qblo
   for (int h = 0; h < CSA2_HI; ++h) {
     const v2f c = *(const v2f *)(a.qix_codes + (row_a * CSA2_HI + h) * 32 + 8 * gq);
     const uint32_t sb = a.qix_scales[(row_a * CSA2_HI + h) * 4 + gq];
-    const _Float16 s = qok_a ? (_Float16)e4m3_to_f32(sb) : (_Float16)0.f;
+    const _Float16 s = qok_a ? e4m3_to_f16(sb) : (_Float16)0.f;
     qa[h][0] = fp4x8_dequant((uint32_t)__float_as_int(c[0]), s);
     qa[h][1] = fp4x8_dequant((uint32_t)__float_as_int(c[1]), s);
   }
@@ -105,7 +105,7 @@ __global__ __launch_bounds__(256) void k_prefill_score(ScoreArgs a, int32_t qblo
     for (int u = 0; u < PF_BATCH; ++u) {
       const int64_t et = tb + 16 * u;  // first entry of the tile
       if (et >= work_end) break;       // uniform
-      const _Float16 s = (_Float16)e4m3_to_f32(scb[u]);
+      const _Float16 s = e4m3_to_f16(scb[u]);
       const v8h b0 = fp4x8_dequant((uint32_t)__float_as_int(code[u][0]), s);
       const v8h b1 = fp4x8_dequant((uint32_t)__float_as_int(code[u][1]), s);
       v4f acc[CSA2_HI];

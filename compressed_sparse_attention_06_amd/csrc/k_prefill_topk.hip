@@ -321,7 +321,7 @@ __device__ __forceinline__ void pt_sweep(const PrefillTopkArgs &a, PtShared &sh,
 #pragma unroll
     for (int u = 0; u < PT_B; ++u) {
       const int32_t et = base + 16 * u;
-      const _Float16 s = (_Float16)e4m3_to_f32(cur.scb[u]);
+      const _Float16 s = e4m3_to_f16(cur.scb[u]);
       const v8h b0 = fp4x8_dequant((uint32_t)__float_as_int(cur.code[u][0]), s);
       const v8h b1 = fp4x8_dequant((uint32_t)__float_as_int(cur.code[u][1]), s);
       const int32_t e = et + m;
@@ -563,7 +563,7 @@ __global__ __launch_bounds__(PT_NT, PT_WG_PER_CU) void k_prefill_topk(PrefillTop
       const int64_t row_a = (int64_t)b * a.nq + min(ta, a.nq - 1);
       const v2f c = *(const v2f *)(a.qix_codes + (row_a * CSA2_HI + h) * 32 + 8 * gq);
       const uint32_t sb = a.qix_scales[(row_a * CSA2_HI + h) * 4 + gq];
-      const _Float16 s = ta < a.nq ? (_Float16)e4m3_to_f32(sb) : (_Float16)0.f;
+      const _Float16 s = ta < a.nq ? e4m3_to_f16(sb) : (_Float16)0.f;
       sh.qa[mt][0][lane] = fp4x8_dequant((uint32_t)__float_as_int(c[0]), s);
       sh.qa[mt][1][lane] = fp4x8_dequant((uint32_t)__float_as_int(c[1]), s);
     }
