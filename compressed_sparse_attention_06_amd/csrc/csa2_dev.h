@@ -73,12 +73,6 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t byte) {
   return e4m3x2_lo_to_f32(byte & 0xFFu)[0];
 }
 
-// The E4M3 byte in bits 0..7 of `word` as fp16 (exact), in one conversion;
-// the other bits of the word do not affect it.
-__device__ __forceinline__ _Float16 e4m3_to_f16(uint32_t word) {
-  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(word, 1.0f, false)[0];
-}
-
 // E2M1 codes of one byte of `word` (low nibble first) -> two fp16 values. The
 // hardware scale operand applies only its power-of-two part, so the conversion
 // runs at scale 1.0 and the E4M3 block scale is applied by an fp16 multiply:

@@ -19,6 +19,7 @@
 // (or -inf past the limit when write_masked is set).
 #include "csa2_dev.h"
 #include "kernels.h"
+#include "prefill_ops.h"
 
 namespace csa2 {
 

@@ -38,6 +38,7 @@
 // M tiles cover the 16 rows and share each dequantised key tile.
 #include "csa2_dev.h"
 #include "kernels.h"
+#include "prefill_ops.h"
 #include "block_ops.h"
 
 namespace csa2 {
